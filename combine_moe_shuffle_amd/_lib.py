@@ -1,0 +1,77 @@
+"""Loads libmoe_shuffle.so (built in-tree by combine_moe_shuffle_amd.build)
+and declares the C ABI of include/moe_shuffle.h for ctypes.
+
+There is no fallback: if the library is missing, every op raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_shuffle.so")
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+_status = ctypes.c_int
+
+# name -> (restype, argtypes), in the header's order
+SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [_status]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_shuffle_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_shuffle": (_status, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
+                              _sz, _p]),
+    "moe_gather_scale": (_status, [_p, _i32, _i32, _p, _p, _i32, _p, _i64, _i64, _i32, _p,
+                                   _p, _p]),
+    "moe_gather_scale_by_token": (_status, [_p, _i32, _i32, _p, _i32, _p, _i32, _p, _i64,
+                                            _i64, _i32, _p, _p, _p]),
+    "moe_gather_scale_quant": (_status, [_p, _i32, _i32, _p, _p, _i32, _p, _i64, _i64, _i32,
+                                         _p, _p, _p, _p, _p]),
+    "moe_scatter_add_workspace_bytes": (_sz, [_i32, _i32]),
+    "moe_scatter_add": (_status, [_p, _i32, _p, _p, _i32, _i32, _p, _p, _sz, _p]),
+    "moe_scatter_add_by_token": (_status, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _p]),
+    "moe_finalize_rmsnorm": (_status, [_p, _i64, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _u32,
+                                       _p, _p, _p, _p]),
+    "moe_convert_check": (_status, [_p, _i64, _p, _p, _p]),
+}
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m combine_moe_shuffle_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        msg = load().moe_last_error().decode(errors="replace")
+        raise MoeError(status, msg)

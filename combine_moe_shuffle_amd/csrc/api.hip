@@ -1,0 +1,281 @@
+// C ABI of libmoe_shuffle.so: host-side argument checks, then the launchers.
+// Every check runs before any HIP call, so a rejected call enqueues nothing
+// (and these error paths run on a machine with no GPU).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moe_shuffle.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr int kMaxQuantD = 65536;     // 16 waves * 64 lanes * 8 chunks * 8
+constexpr int kMaxFinalizeD = 65536;  // same bound for the finalize workgroup
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+moe_status_t check_scores(const float* scores, int64_t st, int64_t se, int T, int E) {
+  REQUIRE(E >= 1, MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+  REQUIRE(st >= 0 && se >= 0, MOE_ERR_INVALID_ARG, "score strides must be >= 0");
+  if (T > 0) {
+    REQUIRE(scores != nullptr, MOE_ERR_INVALID_ARG, "scores is NULL");
+    REQUIRE(aligned(scores, 4), MOE_ERR_INVALID_ARG, "scores must be 4-byte aligned");
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_rows(int D, int mult) {
+  REQUIRE(D >= 0, MOE_ERR_INVALID_ARG, "D must be >= 0 (got %d)", D);
+  REQUIRE(D % mult == 0, MOE_ERR_INVALID_ARG, "D must be a multiple of %d (got %d)", mult, D);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_shuffle_workspace_bytes(int32_t T, int32_t E, int32_t K) {
+  if (T < 0 || E < 1 || K < 1) return 0;
+  return moe::shuffle_workspace_bytes(T, E, K);
+}
+
+moe_status_t moe_shuffle(const float* scores, int64_t stride_t, int64_t stride_e, int32_t T,
+                         int32_t E, int32_t K, const int32_t* valid_token_count,
+                         int32_t* counts, int32_t* expert_indices, int32_t* token_indices,
+                         int32_t* row_of_pair, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
+  moe_status_t s = check_scores(scores, stride_t, stride_e, T, E);
+  if (s != MOE_OK) return s;
+  REQUIRE(K >= 1 && K <= E, MOE_ERR_INVALID_ARG, "K must be in [1, E] (K=%d, E=%d)", K, E);
+  REQUIRE(E <= kMaxE, MOE_ERR_UNSUPPORTED, "E > %d is not supported (got %d)", kMaxE, E);
+  REQUIRE(K <= kMaxK, MOE_ERR_UNSUPPORTED, "K > %d is not supported (got %d)", kMaxK, K);
+  REQUIRE(static_cast<int64_t>(T) * K < (int64_t{1} << 31), MOE_ERR_INVALID_ARG,
+          "T*K must be < 2^31");
+  REQUIRE(counts != nullptr, MOE_ERR_INVALID_ARG, "counts is NULL");
+  if (T > 0) {
+    REQUIRE(expert_indices && token_indices, MOE_ERR_INVALID_ARG, "index outputs are NULL");
+    const size_t need = moe::shuffle_workspace_bytes(T, E, K);
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+            "shuffle workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    REQUIRE(aligned(workspace, 256), MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  // T == 0 still writes counts (all zero)
+  return hip_status(moe::launch_shuffle(scores, stride_t, stride_e, T, E, K, valid_token_count,
+                                        counts, expert_indices, token_indices, row_of_pair,
+                                        workspace, static_cast<hipStream_t>(stream)),
+                    "moe_shuffle");
+}
+
+static moe_status_t check_gather(const moe_bf16_t* x, int32_t T, int32_t D, int32_t a,
+                                 const float* scores, int64_t st, int64_t se, int32_t E,
+                                 const void* out, int out_align) {
+  REQUIRE(T >= 0 && a >= 0, MOE_ERR_INVALID_ARG, "T and a must be >= 0");
+  moe_status_t s = check_rows(D, 8);
+  if (s != MOE_OK) return s;
+  if (a == 0 || D == 0) return MOE_OK;
+  s = check_scores(scores, st, se, 1, E);
+  if (s != MOE_OK) return s;
+  REQUIRE(x != nullptr || T == 0, MOE_ERR_INVALID_ARG, "x is NULL");
+  REQUIRE(out != nullptr, MOE_ERR_INVALID_ARG, "out is NULL");
+  REQUIRE(aligned(x, 16), MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
+  REQUIRE(aligned(out, out_align), MOE_ERR_INVALID_ARG, "out must be %d-byte aligned",
+          out_align);
+  return MOE_OK;
+}
+
+moe_status_t moe_gather_scale(const moe_bf16_t* x, int32_t T, int32_t D,
+                              const int32_t* token_indices, const int32_t* expert_indices,
+                              int32_t a, const float* scores, int64_t stride_t,
+                              int64_t stride_e, int32_t E, const int32_t* valid_rows,
+                              moe_bf16_t* out, void* stream) {
+  moe_status_t s = check_gather(x, T, D, a, scores, stride_t, stride_e, E, out, 16);
+  if (s != MOE_OK) return s;
+  if (a == 0 || D == 0) return ok();
+  REQUIRE(token_indices && expert_indices, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  return hip_status(moe::launch_gather_scale(x, T, D, token_indices, expert_indices, a, scores,
+                                             stride_t, stride_e, E, valid_rows, out,
+                                             static_cast<hipStream_t>(stream)),
+                    "moe_gather_scale");
+}
+
+moe_status_t moe_gather_scale_by_token(const moe_bf16_t* x, int32_t T, int32_t D,
+                                       const int32_t* row_of_pair, int32_t K,
+                                       const int32_t* expert_indices, int32_t a,
+                                       const float* scores, int64_t stride_t,
+                                       int64_t stride_e, int32_t E,
+                                       const int32_t* valid_rows, moe_bf16_t* out,
+                                       void* stream) {
+  moe_status_t s = check_gather(x, T, D, a, scores, stride_t, stride_e, E, out, 16);
+  if (s != MOE_OK) return s;
+  REQUIRE(K >= 1 && K <= kMaxK, MOE_ERR_INVALID_ARG, "K must be in [1, %d] (got %d)", kMaxK, K);
+  if (a == 0 || D == 0 || T == 0) return ok();
+  REQUIRE(row_of_pair && expert_indices, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  return hip_status(moe::launch_gather_scale_by_token(x, T, D, row_of_pair, K, expert_indices,
+                                                      a, scores, stride_t, stride_e, E,
+                                                      valid_rows, out,
+                                                      static_cast<hipStream_t>(stream)),
+                    "moe_gather_scale_by_token");
+}
+
+moe_status_t moe_gather_scale_quant(const moe_bf16_t* x, int32_t T, int32_t D,
+                                    const int32_t* token_indices,
+                                    const int32_t* expert_indices, int32_t a,
+                                    const float* scores, int64_t stride_t, int64_t stride_e,
+                                    int32_t E, const float* scale_ub,
+                                    const int32_t* valid_rows, uint8_t* out_fp8,
+                                    float* out_scale, void* stream) {
+  moe_status_t s = check_gather(x, T, D, a, scores, stride_t, stride_e, E, out_fp8, 16);
+  if (s != MOE_OK) return s;
+  if (a == 0 || D == 0) return ok();
+  REQUIRE(D <= kMaxQuantD, MOE_ERR_UNSUPPORTED, "D > %d is not supported (got %d)", kMaxQuantD,
+          D);
+  REQUIRE(token_indices && expert_indices, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  REQUIRE(out_scale != nullptr && aligned(out_scale, 4), MOE_ERR_INVALID_ARG,
+          "out_scale is NULL or misaligned");
+  REQUIRE(scale_ub == nullptr || aligned(scale_ub, 4), MOE_ERR_INVALID_ARG,
+          "scale_ub misaligned");
+  return hip_status(moe::launch_gather_scale_quant(x, T, D, token_indices, expert_indices, a,
+                                                   scores, stride_t, stride_e, E, scale_ub,
+                                                   valid_rows, out_fp8, out_scale,
+                                                   static_cast<hipStream_t>(stream)),
+                    "moe_gather_scale_quant");
+}
+
+size_t moe_scatter_add_workspace_bytes(int32_t T, int32_t a) {
+  if (T < 0 || a < 0) return 0;
+  return moe::scatter_add_workspace_bytes(T, a);
+}
+
+static moe_status_t check_scatter(const moe_bf16_t* out, int32_t T, const moe_bf16_t* in,
+                                  int32_t a, int32_t D) {
+  REQUIRE(T >= 0 && a >= 0, MOE_ERR_INVALID_ARG, "T and a must be >= 0");
+  moe_status_t s = check_rows(D, 8);
+  if (s != MOE_OK) return s;
+  if (a == 0 || D == 0 || T == 0) return MOE_OK;
+  REQUIRE(out && in, MOE_ERR_INVALID_ARG, "out_tokens or in_tokens is NULL");
+  REQUIRE(aligned(out, 16) && aligned(in, 16), MOE_ERR_INVALID_ARG,
+          "row buffers must be 16-byte aligned");
+  return MOE_OK;
+}
+
+moe_status_t moe_scatter_add(moe_bf16_t* out_tokens, int32_t T, const moe_bf16_t* in_tokens,
+                             const int32_t* token_indices, int32_t a, int32_t D,
+                             const int32_t* valid_rows, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_scatter(out_tokens, T, in_tokens, a, D);
+  if (s != MOE_OK) return s;
+  if (a == 0 || D == 0 || T == 0) return ok();
+  REQUIRE(token_indices != nullptr, MOE_ERR_INVALID_ARG, "token_indices is NULL");
+  const size_t need = moe::scatter_add_workspace_bytes(T, a);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "scatter_add workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(moe::launch_scatter_add(out_tokens, T, in_tokens, token_indices, a, D,
+                                            valid_rows, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                    "moe_scatter_add");
+}
+
+moe_status_t moe_scatter_add_by_token(moe_bf16_t* out_tokens, int32_t T,
+                                      const moe_bf16_t* in_tokens, const int32_t* row_of_pair,
+                                      int32_t K, int32_t a, int32_t D,
+                                      const int32_t* valid_rows, void* stream) {
+  moe_status_t s = check_scatter(out_tokens, T, in_tokens, a, D);
+  if (s != MOE_OK) return s;
+  REQUIRE(K >= 1 && K <= kMaxK, MOE_ERR_INVALID_ARG, "K must be in [1, %d] (got %d)", kMaxK, K);
+  if (a == 0 || D == 0 || T == 0) return ok();
+  REQUIRE(row_of_pair != nullptr, MOE_ERR_INVALID_ARG, "row_of_pair is NULL");
+  return hip_status(moe::launch_scatter_add_by_token(out_tokens, T, in_tokens, row_of_pair, K,
+                                                     a, D, valid_rows,
+                                                     static_cast<hipStream_t>(stream)),
+                    "moe_scatter_add_by_token");
+}
+
+moe_status_t moe_finalize_rmsnorm(const moe_bf16_t* y_permuted, int64_t rows,
+                                  const float* expert_weights, const int32_t* row_of_pair,
+                                  const moe_bf16_t* shared, const moe_bf16_t* gamma, float eps,
+                                  int32_t T, int32_t K, int32_t D, uint32_t flags,
+                                  moe_bf16_t* out, uint8_t* mx_codes, uint8_t* mx_scales,
+                                  void* stream) {
+  REQUIRE(T >= 0 && rows >= 0, MOE_ERR_INVALID_ARG, "T and rows must be >= 0");
+  REQUIRE(K >= 1, MOE_ERR_INVALID_ARG, "K must be >= 1 (got %d)", K);
+  REQUIRE(K <= kMaxK, MOE_ERR_UNSUPPORTED, "K > %d is not supported (got %d)", kMaxK, K);
+  REQUIRE((flags & ~MOE_FINALIZE_BF16_SQUARES) == 0, MOE_ERR_INVALID_ARG,
+          "unknown flags 0x%x", flags);
+  REQUIRE((mx_codes == nullptr) == (mx_scales == nullptr), MOE_ERR_INVALID_ARG,
+          "mx_codes and mx_scales must both be NULL or both be set");
+  moe_status_t s = check_rows(D, mx_codes ? 32 : 8);
+  if (s != MOE_OK) return s;
+  REQUIRE(D <= kMaxFinalizeD, MOE_ERR_UNSUPPORTED, "D > %d is not supported (got %d)",
+          kMaxFinalizeD, D);
+  if (T == 0 || D == 0) return ok();
+  REQUIRE(expert_weights && row_of_pair && gamma && out, MOE_ERR_INVALID_ARG,
+          "a required pointer is NULL");
+  REQUIRE(y_permuted != nullptr || rows == 0, MOE_ERR_INVALID_ARG, "y_permuted is NULL");
+  REQUIRE(aligned(y_permuted, 16) && aligned(gamma, 16) && aligned(out, 16) &&
+              aligned(shared, 16) && aligned(mx_codes, 16),
+          MOE_ERR_INVALID_ARG, "row buffers must be 16-byte aligned");
+  REQUIRE(aligned(expert_weights, 4) && aligned(row_of_pair, 4), MOE_ERR_INVALID_ARG,
+          "expert_weights / row_of_pair must be 4-byte aligned");
+  return hip_status(moe::launch_finalize_rmsnorm(y_permuted, rows, expert_weights, row_of_pair,
+                                                 shared, gamma, eps, T, K, D, flags, out,
+                                                 mx_codes, mx_scales,
+                                                 static_cast<hipStream_t>(stream)),
+                    "moe_finalize_rmsnorm");
+}
+
+moe_status_t moe_convert_check(const float* in, int64_t n, moe_bf16_t* bf16_out,
+                               uint8_t* e4m3_out, void* stream) {
+  REQUIRE(n >= 0, MOE_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  REQUIRE(in != nullptr && aligned(in, 4), MOE_ERR_INVALID_ARG, "in is NULL or misaligned");
+  REQUIRE(n < (int64_t{1} << 31) * 256, MOE_ERR_INVALID_ARG, "n too large");
+  return hip_status(moe::launch_convert_check(in, n, bf16_out, e4m3_out,
+                                              static_cast<hipStream_t>(stream)),
+                    "moe_convert_check");
+}
+
+}  // extern "C"

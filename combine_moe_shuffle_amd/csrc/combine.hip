@@ -1,0 +1,325 @@
+// Combine: add expert output rows back into token order, deterministically.
+//
+// [GS] "mslk/moe/gather_scatter.py", scatter_add_dense_tokens: each valid
+// input row is added into out[token_indices[row]] (the pages use relaxed
+// atomics, so their order of additions is not fixed). [LY] "mslk/moe/
+// layers.py", _combine_outputs: out starts as the shared-expert output.
+//
+// Here each token is owned by one wave per row slice, which reads the token's
+// initial row and its expert rows and writes the row once:
+//   acc = f32(out[t]); acc += f32(in[r]) for its rows r in ascending order;
+//   out[t] = bf16(acc).
+// No atomics, one write per output element, and the same fp32 addition
+// sequence on every run.
+//
+// Where a token's rows come from:
+//  by_token  the inverse map row_of_pair[t, 0..K) written by the shuffle;
+//            invalid slots dropped and the rest sorted in-wave.
+//  general   only token_indices is known: a CSR of rows per token is built
+//            first (count with atomics on per-token counters, exclusive scan,
+//            fill); the order inside a token's list then depends on the
+//            atomics, so the reduce kernel sorts each list before adding.
+#include <limits.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kRowWaves = 4;
+constexpr int kGroup = 4;  // expert rows whose loads are in flight together
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ int clamp_count(const int* p, int hi) {
+  if (!p) return hi;
+  int v = *p;
+  return v < 0 ? 0 : (v > hi ? hi : v);
+}
+
+// Ascending bitonic sort of one int per lane across the wave.
+__device__ __forceinline__ int wave_sort_asc(int v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = __shfl_xor(v, j, kWave);
+      const bool up = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      v = (lower == up) ? min(v, o) : max(v, o);
+    }
+  }
+  return v;
+}
+
+// acc[j] (this lane's CPL chunks of the slice) += the n rows listed in
+// ascending order in lanes 0..n-1 of `sorted_rows`.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void add_rows(float (&acc)[CPL][8], const uint16_t* __restrict__ in,
+                                         int D, int nch, int base, int sorted_rows, int n) {
+  for (int i0 = 0; i0 < n; i0 += kGroup) {
+    u32x4 buf[kGroup][CPL];
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      if (i0 + q < n) {
+        const int r = __builtin_amdgcn_readlane(sorted_rows, i0 + q);
+        const uint16_t* src = in + static_cast<int64_t>(r) * D;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = base + j * kWave;
+          if (FULL || c < nch) buf[q][j] = ld16_stream(src + c * kChunk);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      if (i0 + q < n) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = base + j * kWave;
+          if (FULL || c < nch) {
+            float f[8];
+            unpack8(buf[q][j], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int CPL, bool FULL>
+__device__ __forceinline__ void load_acc(float (&acc)[CPL][8], const uint16_t* __restrict__ row,
+                                         int nch, int base) {
+  u32x4 v[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    v[j] = (FULL || c < nch) ? ld16(row + c * kChunk) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) unpack8(v[j], acc[j]);
+}
+
+// Packs every chunk before the first store, so that no store's data
+// registers are reused while it is in flight.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void store_acc(const float (&acc)[CPL][8], uint16_t* __restrict__ row,
+                                          int nch, int base) {
+  u32x4 o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = pack8(acc[j]);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) st16_stream(row + c * kChunk, o[j]);
+  }
+}
+
+// The whole per-token reduction of one slice: initial row, n expert rows in
+// the ascending order held in lanes 0..n-1 of sorted_rows, one store.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
+                                             const uint16_t* __restrict__ in, int D, int nch,
+                                             int base, int sorted_rows, int n) {
+  float acc[CPL][8];
+  load_acc<CPL, FULL>(acc, orow, nch, base);
+  add_rows<CPL, FULL>(acc, in, D, nch, base, sorted_rows, n);
+  store_acc<CPL, FULL>(acc, orow, nch, base);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
+    const int* __restrict__ rop, int K, int a, int D, const int* __restrict__ vrows,
+    int nsl) {
+  const int lane = lane_id();
+  const int64_t unit =
+      static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int V = clamp_count(vrows, a);
+  int r = lane < K ? rop[static_cast<int64_t>(t) * K + lane] : -1;
+  const bool ok = r >= 0 && r < V;
+  const int n = __popcll(__ballot(ok));
+  if (n == 0) return;
+  const int sorted_rows = wave_sort_asc(ok ? r : INT_MAX, lane);
+
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  if (slice0 + kWave * CPL <= nch)
+    reduce_slice<CPL, true>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+  else
+    reduce_slice<CPL, false>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+}
+
+// ---------------------------------------------------------------- general
+__global__ void csr_zero_kernel(int* __restrict__ cnt, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) cnt[i] = 0;
+}
+
+// Rows whose token index is out of [0, T) are skipped (no fault).
+__global__ void csr_count_kernel(const int* __restrict__ ti, int T, int a,
+                                 const int* __restrict__ vrows, int* __restrict__ cnt,
+                                 int* __restrict__ slot) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  const int V = clamp_count(vrows, a);
+  if (r >= V) return;
+  const int t = ti[r];
+  if (static_cast<unsigned>(t) < static_cast<unsigned>(T)) slot[r] = atomicAdd(&cnt[t], 1);
+}
+
+// Exclusive scan of cnt[0..n) in place (one workgroup); cnt[n] = total.
+__global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(int* __restrict__ cnt, int n) {
+  __shared__ int part[kScanThreads];
+  const int tid = threadIdx.x;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int beg = min(tid * per, n);
+  const int end = min(beg + per, n);
+  int s = 0;
+  for (int i = beg; i < end; ++i) s += cnt[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int i = beg; i < end; ++i) {
+    const int c = cnt[i];
+    cnt[i] = run;
+    run += c;
+  }
+  if (tid == kScanThreads - 1) cnt[n] = part[tid];
+}
+
+__global__ void csr_fill_kernel(const int* __restrict__ ti, int T, int a,
+                                const int* __restrict__ vrows, const int* __restrict__ start,
+                                const int* __restrict__ slot, int* __restrict__ list) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  const int V = clamp_count(vrows, a);
+  if (r >= V) return;
+  const int t = ti[r];
+  if (static_cast<unsigned>(t) < static_cast<unsigned>(T)) list[start[t] + slot[r]] = r;
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
+    const int* __restrict__ start, const int* __restrict__ list, int D, int nsl) {
+  const int lane = lane_id();
+  const int64_t unit =
+      static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int beg = start[t];
+  const int n = start[t + 1] - beg;
+  if (n == 0) return;
+
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  const int base = slice0 + lane;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  if (n <= kWave) {
+    const int r = lane < n ? list[beg + lane] : INT_MAX;
+    const int sorted_rows = wave_sort_asc(r, lane);
+    if (slice0 + kWave * CPL <= nch)
+      reduce_slice<CPL, true>(orow, in, D, nch, base, sorted_rows, n);
+    else
+      reduce_slice<CPL, false>(orow, in, D, nch, base, sorted_rows, n);
+  } else {
+    float acc[CPL][8];
+    load_acc<CPL, false>(acc, orow, nch, base);
+    // long list: take the rows in ascending order one at a time (each step a
+    // wave-wide minimum over the rows above the previous one)
+    int prev = -1;
+    for (int i = 0; i < n; ++i) {
+      int m = INT_MAX;
+      for (int q = lane; q < n; q += kWave) {
+        const int r = list[beg + q];
+        if (r > prev && r < m) m = r;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off, kWave));
+      prev = m;
+      add_rows<CPL, false>(acc, in, D, nch, base, m, 1);
+    }
+    store_acc<CPL, false>(acc, orow, nch, base);
+  }
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+SliceShape combine_shape(int nch) {
+  // kGroup rows * cpl chunks of loads in flight per lane: keep cpl <= 4
+  static const int allowed[] = {4, 3, 2, 1};
+  return pick_slices(nch, allowed, 4, 1 << 20);
+}
+
+}  // namespace
+
+size_t scatter_add_workspace_bytes(int T, int a) {
+  return align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
+         2 * align256(static_cast<size_t>(a) * sizeof(int));
+}
+
+#define MOE_DISPATCH_CPL4(CPLV, LAUNCH) \
+  switch (CPLV) {                       \
+    case 1: LAUNCH(1); break;           \
+    case 2: LAUNCH(2); break;           \
+    case 3: LAUNCH(3); break;           \
+    default: LAUNCH(4); break;          \
+  }
+
+hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
+                                       const int* row_of_pair, int K, int a, int D,
+                                       const int* valid_rows, hipStream_t stream) {
+  const SliceShape sh = combine_shape(D / kChunk);
+  const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
+  const dim3 block(kRowWaves * kWave);
+#define L(C)                                                                            \
+  hipLaunchKernelGGL(scatter_tokens_kernel<C>, grid, block, 0, stream, out, T, in,        \
+                     row_of_pair, K, a, D, valid_rows, sh.nsl)
+  MOE_DISPATCH_CPL4(sh.cpl, L)
+#undef L
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
+                              int a, int D, const int* valid_rows, void* workspace,
+                              hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int* cnt = reinterpret_cast<int*>(ws);  // [T+1]: counts, then starts
+  int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
+  int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
+                                     align256(static_cast<size_t>(a) * sizeof(int)));
+  hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
+                     T + 1);
+  const dim3 rgrid((a + 255) / 256);
+  hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows, cnt,
+                     slot);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
+  hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows, cnt,
+                     slot, list);
+  const SliceShape sh = combine_shape(D / kChunk);
+  const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
+  const dim3 block(kRowWaves * kWave);
+#define L(C)                                                                            \
+  hipLaunchKernelGGL(scatter_csr_kernel<C>, grid, block, 0, stream, out, T, in, cnt, list, \
+                     D, sh.nsl)
+  MOE_DISPATCH_CPL4(sh.cpl, L)
+#undef L
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,65 @@
+// Internal launchers, one per kernel family. Arguments are validated by the C
+// ABI layer (api.hip) before any of these is called; each returns the HIP
+// status of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// shuffle.hip
+size_t shuffle_workspace_bytes(int T, int E, int K);
+hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, int E,
+                          int K, const int* vtc, int* counts, int* expert_indices,
+                          int* token_indices, int* row_of_pair, void* workspace,
+                          hipStream_t stream);
+
+// gather.hip
+hipError_t launch_gather_scale(const uint16_t* x, int T, int D, const int* ti,
+                               const int* ei, int a, const float* scores, int64_t st,
+                               int64_t se, int E, const int* valid_rows, uint16_t* out,
+                               hipStream_t stream);
+hipError_t launch_gather_scale_by_token(const uint16_t* x, int T, int D,
+                                        const int* row_of_pair, int K, const int* ei,
+                                        int a, const float* scores, int64_t st,
+                                        int64_t se, int E, const int* valid_rows,
+                                        uint16_t* out, hipStream_t stream);
+hipError_t launch_gather_scale_quant(const uint16_t* x, int T, int D, const int* ti,
+                                     const int* ei, int a, const float* scores,
+                                     int64_t st, int64_t se, int E, const float* scale_ub,
+                                     const int* valid_rows, uint8_t* out_fp8,
+                                     float* out_scale, hipStream_t stream);
+
+// combine.hip
+size_t scatter_add_workspace_bytes(int T, int a);
+hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
+                              int a, int D, const int* valid_rows, void* workspace,
+                              hipStream_t stream);
+hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
+                                       const int* row_of_pair, int K, int a, int D,
+                                       const int* valid_rows, hipStream_t stream);
+
+// finalize.hip
+hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float* w,
+                                   const int* row_of_pair, const uint16_t* shared,
+                                   const uint16_t* gamma, float eps, int T, int K, int D,
+                                   uint32_t flags, uint16_t* out, uint8_t* mx_codes,
+                                   uint8_t* mx_scales, hipStream_t stream);
+hipError_t launch_convert_check(const float* in, int64_t n, uint16_t* bf16_out,
+                                uint8_t* e4m3_out, hipStream_t stream);
+
+// Row-slice layout of the streaming kernels: a row of D bf16 values is
+// nch = D/8 chunks of 16 bytes; a wave covers one slice of 64*cpl chunks,
+// lane l taking chunks base + j*64 + l (j < cpl), so every load and store
+// instruction of the wave touches 1 KiB of contiguous memory.
+struct SliceShape {
+  int cpl;  // chunks per lane
+  int nsl;  // slices per row
+};
+// Smallest cpl in `allowed` (ascending) whose slice count is <= max_slices
+// and that wastes the fewest lanes.
+SliceShape pick_slices(int nch, const int* allowed, int n_allowed, int max_slices);
+
+}  // namespace moe

@@ -1,0 +1,279 @@
+"""torch-tensor bindings of the C ABI (include/moe_shuffle.h).
+
+Argument marshalling only: every function checks dtypes, shapes, devices and
+contiguity (ValueError), allocates outputs and workspaces with torch, and
+calls the library on torch's current HIP stream. All the work runs in the
+library's gfx950 kernels; there is no CPU path.
+
+bf16 tensors are torch.bfloat16; FP8 codes and UE8M0 scales are torch.uint8.
+Device-side counts (valid_token_count, valid_rows) are int32 tensors of one
+element on the same device, read by the kernels (no host sync).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _scalar_i32(t, name, device):
+    if t is None:
+        return None
+    _need(t, name, torch.int32, device=device)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold one element")
+    return t
+
+
+def _scores(scores, device):
+    _need(scores, "scores", torch.float32, 2, device)
+    return scores.stride(0), scores.stride(1)
+
+
+# ---------------------------------------------------------------- shuffle
+def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspace=None,
+                out=None):
+    """Top-k routing + stable counting sort of (token, expert) pairs by expert.
+
+    Returns (counts[E+1], expert_indices[T*K], token_indices[T*K],
+    row_of_pair[T, K] or None); counts[E] is the valid row count V. ``out``
+    may supply those four tensors (row_of_pair may be None)."""
+    device = scores.device
+    st, se = _scores(scores, device)
+    T, E = scores.shape
+    vtc = _scalar_i32(valid_token_count, "valid_token_count", device)
+    lib = _lib.load()
+    if out is not None:
+        counts, ei, ti, rop = out
+        for t, n, numel in ((counts, "counts", E + 1), (ei, "expert_indices", T * K),
+                            (ti, "token_indices", T * K)):
+            _need(t, n, torch.int32, device=device)
+            _contig(t, n)
+            if t.numel() != numel:
+                raise ValueError(f"{n} must have {numel} elements")
+        if rop is not None:
+            _need(rop, "row_of_pair", torch.int32, device=device)
+            _contig(rop, "row_of_pair")
+            if rop.numel() != T * K:
+                raise ValueError(f"row_of_pair must have {T * K} elements")
+    else:
+        counts = torch.empty(E + 1, dtype=torch.int32, device=device)
+        ei = torch.empty(T * K, dtype=torch.int32, device=device)
+        ti = torch.empty(T * K, dtype=torch.int32, device=device)
+        rop = torch.empty((T, K), dtype=torch.int32, device=device) if row_of_pair else None
+    need = lib.moe_shuffle_workspace_bytes(T, E, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _lib.check(lib.moe_shuffle(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
+                               _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace),
+                               workspace.numel(), _stream()))
+    return counts, ei, ti, rop
+
+
+# ---------------------------------------------------------------- dispatch
+def _gather_common(x, expert_indices, scores, valid_rows):
+    device = x.device
+    _need(x, "x", torch.bfloat16, 2, device)
+    _contig(x, "x")
+    _need(expert_indices, "expert_indices", torch.int32, 1, device)
+    _contig(expert_indices, "expert_indices")
+    st, se = _scores(scores, device)
+    if scores.shape[0] != x.shape[0]:
+        raise ValueError("scores must be (T, E) with T = x.shape[0]")
+    return device, st, se, _scalar_i32(valid_rows, "valid_rows", device)
+
+
+def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, out=None):
+    """out[i] = bf16(x[token_indices[i]] * scores[t, expert_indices[i]]) for
+    i < valid_rows; other rows of ``out`` are left as they are."""
+    device, st, se, vr = _gather_common(x, expert_indices, scores, valid_rows)
+    _need(token_indices, "token_indices", torch.int32, 1, device)
+    _contig(token_indices, "token_indices")
+    a = token_indices.numel()
+    if expert_indices.numel() != a:
+        raise ValueError("token_indices and expert_indices must have the same length")
+    T, D = x.shape
+    if out is None:
+        out = torch.empty((a, D), dtype=torch.bfloat16, device=device)
+    _need(out, "out", torch.bfloat16, 2, device)
+    _contig(out, "out")
+    if tuple(out.shape) != (a, D):
+        raise ValueError("out must be (a, D)")
+    _lib.check(_lib.load().moe_gather_scale(
+        _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
+        scores.shape[1], _ptr(vr), _ptr(out), _stream()))
+    return out
+
+
+def moe_gather_scale_by_token(x, row_of_pair, expert_indices, scores, valid_rows=None,
+                              out=None):
+    """moe_gather_scale's output, visiting tokens through the inverse map."""
+    device, st, se, vr = _gather_common(x, expert_indices, scores, valid_rows)
+    _need(row_of_pair, "row_of_pair", torch.int32, 2, device)
+    _contig(row_of_pair, "row_of_pair")
+    T, D = x.shape
+    if row_of_pair.shape[0] != T:
+        raise ValueError("row_of_pair must be (T, K)")
+    K = row_of_pair.shape[1]
+    a = expert_indices.numel()
+    if out is None:
+        out = torch.empty((a, D), dtype=torch.bfloat16, device=device)
+    _need(out, "out", torch.bfloat16, 2, device)
+    _contig(out, "out")
+    if tuple(out.shape) != (a, D):
+        raise ValueError("out must be (a, D)")
+    _lib.check(_lib.load().moe_gather_scale_by_token(
+        _ptr(x), T, D, _ptr(row_of_pair), K, _ptr(expert_indices), a, _ptr(scores), st, se,
+        scores.shape[1], _ptr(vr), _ptr(out), _stream()))
+    return out
+
+
+def moe_gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=None,
+                           valid_rows=None, out=None, out_scale=None):
+    """FP8 E4M3 rowwise dispatch. Returns (codes (a, D) uint8, scale (a,) fp32)."""
+    device, st, se, vr = _gather_common(x, expert_indices, scores, valid_rows)
+    _need(token_indices, "token_indices", torch.int32, 1, device)
+    _contig(token_indices, "token_indices")
+    a = token_indices.numel()
+    T, D = x.shape
+    if scale_ub is not None:
+        _need(scale_ub, "scale_ub", torch.float32, device=device)
+        if scale_ub.numel() != 1:
+            raise ValueError("scale_ub must hold one element")
+    if out is None:
+        out = torch.empty((a, D), dtype=torch.uint8, device=device)
+    if out_scale is None:
+        out_scale = torch.empty(a, dtype=torch.float32, device=device)
+    _need(out, "out", torch.uint8, 2, device)
+    _need(out_scale, "out_scale", torch.float32, 1, device)
+    _contig(out, "out")
+    _lib.check(_lib.load().moe_gather_scale_quant(
+        _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
+        scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream()))
+    return out, out_scale
+
+
+# ---------------------------------------------------------------- combine
+def _scatter_common(out_tokens, in_tokens, valid_rows):
+    device = out_tokens.device
+    _need(out_tokens, "out_tokens", torch.bfloat16, 2, device)
+    _need(in_tokens, "in_tokens", torch.bfloat16, 2, device)
+    _contig(out_tokens, "out_tokens")
+    _contig(in_tokens, "in_tokens")
+    if out_tokens.shape[1] != in_tokens.shape[1]:
+        raise ValueError("out_tokens and in_tokens must have the same D")
+    return device, _scalar_i32(valid_rows, "valid_rows", device)
+
+
+def moe_scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None, workspace=None):
+    """In place: out[t] = bf16(f32(out[t]) + sum of its valid rows, ascending)."""
+    device, vr = _scatter_common(out_tokens, in_tokens, valid_rows)
+    _need(token_indices, "token_indices", torch.int32, 1, device)
+    _contig(token_indices, "token_indices")
+    T, D = out_tokens.shape
+    a = in_tokens.shape[0]
+    if token_indices.numel() != a:
+        raise ValueError("token_indices must have in_tokens.shape[0] entries")
+    lib = _lib.load()
+    need = lib.moe_scatter_add_workspace_bytes(T, a)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _lib.check(lib.moe_scatter_add(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
+                                   a, D, _ptr(vr), _ptr(workspace), workspace.numel(),
+                                   _stream()))
+    return out_tokens
+
+
+def moe_scatter_add_by_token(out_tokens, in_tokens, row_of_pair, valid_rows=None):
+    """moe_scatter_add's result, reading each token's rows from the inverse map."""
+    device, vr = _scatter_common(out_tokens, in_tokens, valid_rows)
+    _need(row_of_pair, "row_of_pair", torch.int32, 2, device)
+    _contig(row_of_pair, "row_of_pair")
+    T, D = out_tokens.shape
+    if row_of_pair.shape[0] != T:
+        raise ValueError("row_of_pair must be (T, K)")
+    _lib.check(_lib.load().moe_scatter_add_by_token(
+        _ptr(out_tokens), T, _ptr(in_tokens), _ptr(row_of_pair), row_of_pair.shape[1],
+        in_tokens.shape[0], D, _ptr(vr), _stream()))
+    return out_tokens
+
+
+# ---------------------------------------------------------------- finalize
+def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma, eps,
+                         flags=0, out=None, mxfp8=False):
+    """Weighted top-k reduction + shared add + RMSNorm (+ MXFP8).
+
+    Returns out (T, D) bf16, or (out, codes (T, D) uint8, scales (T, D/32)
+    uint8) with ``mxfp8``."""
+    device = y_permuted.device
+    _need(y_permuted, "y_permuted", torch.bfloat16, 2, device)
+    _need(expert_weights, "expert_weights", torch.float32, 2, device)
+    _need(row_of_pair, "row_of_pair", torch.int32, 2, device)
+    _need(gamma, "gamma", torch.bfloat16, 1, device)
+    for t, n in ((y_permuted, "y_permuted"), (expert_weights, "expert_weights"),
+                 (row_of_pair, "row_of_pair"), (gamma, "gamma")):
+        _contig(t, n)
+    T, K = row_of_pair.shape
+    rows, D = y_permuted.shape
+    if tuple(expert_weights.shape) != (T, K):
+        raise ValueError("expert_weights must be (T, K) like row_of_pair")
+    if gamma.numel() != D:
+        raise ValueError("gamma must have D entries")
+    if shared is not None:
+        _need(shared, "shared", torch.bfloat16, 2, device)
+        _contig(shared, "shared")
+        if tuple(shared.shape) != (T, D):
+            raise ValueError("shared must be (T, D)")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
+    codes = torch.empty((T, D), dtype=torch.uint8, device=device) if mxfp8 else None
+    scales = torch.empty((T, D // 32), dtype=torch.uint8, device=device) if mxfp8 else None
+    _lib.check(_lib.load().moe_finalize_rmsnorm(
+        _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
+        _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
+        _stream()))
+    return (out, codes, scales) if mxfp8 else out
+
+
+def moe_convert_check(values):
+    """The kernels' device conversions of fp32 values: (bf16 bits as int16
+    tensor, E4M3 codes of the +-448-clamped values as uint8)."""
+    _need(values, "values", torch.float32, 1)
+    _contig(values, "values")
+    n = values.numel()
+    bf = torch.empty(n, dtype=torch.int16, device=values.device)
+    e4 = torch.empty(n, dtype=torch.uint8, device=values.device)
+    _lib.check(_lib.load().moe_convert_check(_ptr(values), n, _ptr(bf), _ptr(e4), _stream()))
+    return bf, e4
+
+
+# The pages' names for the same operations
+gather_scale_dense_tokens = moe_gather_scale
+gather_scale_quant_dense_tokens = moe_gather_scale_quant
+scatter_add_dense_tokens = moe_scatter_add

@@ -1,0 +1,282 @@
+/*
+ * moe_shuffle.h -- C ABI of the MI355X (gfx950) MoE token dispatch/combine
+ * library (libmoe_shuffle.so).
+ *
+ * The path: route and shuffle (moe_shuffle), dispatch (moe_gather_scale or its
+ * FP8 rowwise form), expert GEMMs (not here), combine (moe_scatter_add) or the
+ * fused MoE tail (moe_finalize_rmsnorm).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [GS] "mslk/moe/gather_scatter.py" (mslk-cuda-nightly wheel)
+ *   [LY] "mslk/moe/layers.py" (same wheel)
+ *   [K3] "vllm ... kimi_k3 ... allreduce_rmsnorm_reduce_scatter_early_exit"
+ *   [MH] "vllm ... deepseek_v41 ... all_reduce_mhc"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer except where marked "host".
+ *    bf16 tensors are uint16_t bit patterns; FP8 is OCP E4M3FN (uint8_t);
+ *    MXFP8 scales are UE8M0 exponent bytes (uint8_t). All tensors are
+ *    row-major and dense unless a stride argument says otherwise.
+ *  - `stream` is a hipStream_t passed as void* (NULL: the null stream). Work
+ *    is enqueued on it and the call returns; nothing synchronises the host and
+ *    the library never reads device memory from the host. Device-side counts
+ *    (valid_token_count, valid_rows) are read by the kernels.
+ *  - The caller owns all memory. The library allocates nothing, keeps no
+ *    pointer after a call returns and holds no state; calls are reentrant.
+ *    Calls that share output or workspace memory must be ordered by the
+ *    caller (same stream, or events).
+ *  - Errors: all argument checks run on the host before any launch. On a
+ *    failed check nothing is enqueued and the status says why
+ *    (moe_last_error() gives a message for the calling thread):
+ *      MOE_ERR_INVALID_ARG  NULL required pointer, negative or too large size,
+ *                           misaligned pointer, K outside [1, E], D not a
+ *                           multiple of the vector width (8 bf16 elements;
+ *                           32 for MXFP8 output)
+ *      MOE_ERR_UNSUPPORTED  a size beyond what the kernels are built for
+ *                           (E > 1024, K > 64)
+ *      MOE_ERR_WORKSPACE    workspace NULL or smaller than *_workspace_bytes
+ *      MOE_ERR_HIP          a HIP launch error (hipGetLastError after launch)
+ *    A call with nothing to do (T == 0, a == 0 or D == 0) returns MOE_OK and
+ *    enqueues nothing, except moe_shuffle, which still writes counts (zeros).
+ *  - Device-side values are preconditions (as on the pages): indices must be
+ *    in range. The kernels range-check every index they address memory with
+ *    and skip an out-of-range row rather than fault; what they write for it is
+ *    unspecified. Device-side counts are clamped to [0, T] / [0, a].
+ *  - Row buffers (x, out, in_tokens, y, shared, gamma, codes) must be 16-byte
+ *    aligned; index and score buffers 4-byte aligned.
+ */
+#ifndef MOE_SHUFFLE_H
+#define MOE_SHUFFLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from the shared library. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef uint16_t moe_bf16_t; /* bfloat16 bit pattern */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status_t;
+
+/* Version of this ABI (bumped on any signature change). */
+#define MOE_ABI_VERSION 1
+MOE_API int moe_abi_version(void);
+
+/* Static name of a status code. */
+MOE_API const char *moe_status_str(moe_status_t status);
+
+/* Message of the last failed call on the calling thread ("" if none). The
+ * returned string is thread-local and valid until the next call. */
+MOE_API const char *moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * moe_shuffle -- top-k routing and the stable counting sort of
+ * (token, expert) pairs by expert.
+ *
+ * [LY] MetaShufflingMoE._route hands the router scores to the shuffle, which
+ * returns per-expert token counts plus the expert and token index of every
+ * routed row, grouped by expert; the grouped GEMMs and [GS]
+ * gather_scale_dense_tokens then read rows in that order. [LY]
+ * BaselineMoE._forward defines the routing as the K largest scores per token.
+ *
+ * For each token t < vtc (vtc = *valid_token_count clamped to [0, T], or T
+ * when NULL) the K experts with the largest scores are selected; slot k is
+ * the k-th largest; equal scores go to the lower expert id (+0 and -0 are
+ * equal). Scores must not be NaN.
+ *   counts[e] (e < E)  number of selected pairs of expert e
+ *   counts[E]          V = vtc * K, the number of valid rows (the row bound
+ *                      that moe_gather_scale / moe_scatter_add take)
+ *   rows [0, V)        the valid pairs sorted by (expert, token): a stable
+ *                      sort, so within an expert tokens ascend
+ *   rows [V, T*K)      the pairs of tokens t >= vtc in (t, k) order, with
+ *                      token_indices = t and expert_indices = -1
+ *   row_of_pair[t*K+k] row of pair (t, k); -1 for t >= vtc. It is the inverse
+ *                      of token_indices on the valid rows, and is what the
+ *                      finalize takes as its permuted-row map.
+ * The result is deterministic (no order depends on timing).
+ *
+ * scores           [T, E] fp32, element (t, e) at scores[t*stride_t + e*stride_e]
+ *                  (strides in elements, >= 0)
+ * valid_token_count  nullable device int32 scalar
+ * counts           [E+1] int32 out
+ * expert_indices, token_indices  [T*K] int32 out
+ * row_of_pair      [T*K] int32 out, nullable
+ * workspace        >= moe_shuffle_workspace_bytes(T, E, K) bytes, 256-byte
+ *                  aligned, contents ignored on entry and undefined after
+ * Limits: 1 <= E <= 1024, 1 <= K <= min(E, 64), T*K < 2^31.
+ * ---------------------------------------------------------------------- */
+MOE_API size_t moe_shuffle_workspace_bytes(int32_t T, int32_t E, int32_t K);
+MOE_API moe_status_t moe_shuffle(const float *scores, int64_t stride_t, int64_t stride_e,
+                         int32_t T, int32_t E, int32_t K,
+                         const int32_t *valid_token_count, int32_t *counts,
+                         int32_t *expert_indices, int32_t *token_indices,
+                         int32_t *row_of_pair, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_gather_scale -- dispatch: gather token rows into expert order, scaled
+ * by their router score.
+ *
+ * [GS] gather_scale_dense_tokens: for every row i < V (V = *valid_rows
+ * clamped to [0, a], or a when NULL; the pages call it valid_token_count),
+ *   t = token_indices[i], e = expert_indices[i],
+ *   out[i, :] = bf16_rne( f32(x[t, :]) * scores[t*stride_t + e*stride_e] )
+ * (one fp32 multiply per element). Rows i >= V are not written.
+ *
+ * x     [T, D] bf16;  out [a, D] bf16;  token_indices, expert_indices [a] int32
+ * D % 8 == 0.
+ * ---------------------------------------------------------------------- */
+MOE_API moe_status_t moe_gather_scale(const moe_bf16_t *x, int32_t T, int32_t D,
+                              const int32_t *token_indices,
+                              const int32_t *expert_indices, int32_t a,
+                              const float *scores, int64_t stride_t,
+                              int64_t stride_e, int32_t E,
+                              const int32_t *valid_rows, moe_bf16_t *out,
+                              void *stream);
+
+/* moe_gather_scale_by_token -- the same output as moe_gather_scale, visiting
+ * the rows token by token through the inverse map row_of_pair ([T, K] int32,
+ * as moe_shuffle writes it), so each token row of x is read from memory once
+ * and written to its K rows. Pairs with row < 0 or row >= V are skipped.
+ * Precondition: row_of_pair is the inverse of token_indices on rows [0, V)
+ * (it is, when both come from one moe_shuffle call); then the output equals
+ * moe_gather_scale's bit for bit. */
+MOE_API moe_status_t moe_gather_scale_by_token(const moe_bf16_t *x, int32_t T, int32_t D,
+                                       const int32_t *row_of_pair, int32_t K,
+                                       const int32_t *expert_indices, int32_t a,
+                                       const float *scores, int64_t stride_t,
+                                       int64_t stride_e, int32_t E,
+                                       const int32_t *valid_rows,
+                                       moe_bf16_t *out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_gather_scale_quant -- dispatch with FP8 (E4M3FN) rowwise quantisation.
+ *
+ * [GS] gather_scale_quant_dense_tokens and its FP8 rowwise kernel. For every
+ * row i < V: v = f32(x[t, :]) * s (s as in moe_gather_scale);
+ *   m = max_d |v_d|; m = clamp(m, EPS, *scale_ub) if scale_ub is given,
+ *   else max(m, EPS), EPS = 1e-12;
+ *   mult = 448 / m (correctly rounded);  out_scale[i] = 1 / mult;
+ *   out_fp8[i, d] = e4m3_rne( clamp(v_d * mult, -448, 448) ).
+ * Rows i >= V are not written (codes nor scale).
+ *
+ * scale_ub   nullable device fp32 scalar (the pages' CLAMP_MAX)
+ * out_fp8    [a, D] uint8 E4M3FN codes, 16-byte aligned
+ * out_scale  [a] fp32 dequantisation scale (value = code * out_scale)
+ * D % 8 == 0.
+ * ---------------------------------------------------------------------- */
+MOE_API moe_status_t moe_gather_scale_quant(const moe_bf16_t *x, int32_t T, int32_t D,
+                                    const int32_t *token_indices,
+                                    const int32_t *expert_indices, int32_t a,
+                                    const float *scores, int64_t stride_t,
+                                    int64_t stride_e, int32_t E,
+                                    const float *scale_ub,
+                                    const int32_t *valid_rows, uint8_t *out_fp8,
+                                    float *out_scale, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_scatter_add -- combine: add expert output rows back into token order.
+ *
+ * [GS] scatter_add_dense_tokens adds every valid input row r < V into output
+ * token token_indices[r]; [LY] _combine_outputs passes the shared-expert
+ * output as the initial out. The pages add with atomics in no fixed order;
+ * here the order is fixed and the result deterministic: for each token t,
+ *   acc = f32(out[t, :]);  for each valid row r with token_indices[r] == t,
+ *   in ascending r: acc += f32(in[r, :]);  out[t, :] = bf16_rne(acc).
+ * Tokens with no valid row are not written.
+ *
+ * out_tokens [T, D] bf16 in/out;  in_tokens [a, D] bf16;  token_indices [a]
+ * valid_rows nullable device int32 scalar (V, clamped to [0, a])
+ * workspace  >= moe_scatter_add_workspace_bytes(T, a) bytes, 256-byte aligned
+ * D % 8 == 0. Tokens routed to more than 64 valid rows take a slower
+ * (quadratic in that count) ordering step; the result is the same.
+ * ---------------------------------------------------------------------- */
+MOE_API size_t moe_scatter_add_workspace_bytes(int32_t T, int32_t a);
+MOE_API moe_status_t moe_scatter_add(moe_bf16_t *out_tokens, int32_t T,
+                             const moe_bf16_t *in_tokens,
+                             const int32_t *token_indices, int32_t a, int32_t D,
+                             const int32_t *valid_rows, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* moe_scatter_add_by_token -- the same result as moe_scatter_add, reading each
+ * token's rows from the inverse map row_of_pair ([T, K] int32, as moe_shuffle
+ * writes it) instead of building it: no workspace, one launch. Rows < 0 or
+ * >= V are skipped; the remaining rows of a token are added in ascending row
+ * order. Precondition: row_of_pair is the inverse of token_indices on rows
+ * [0, V); then the output equals moe_scatter_add's bit for bit. K <= 64. */
+MOE_API moe_status_t moe_scatter_add_by_token(moe_bf16_t *out_tokens, int32_t T,
+                                      const moe_bf16_t *in_tokens,
+                                      const int32_t *row_of_pair, int32_t K,
+                                      int32_t a, int32_t D,
+                                      const int32_t *valid_rows, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_finalize_rmsnorm -- the MoE tail: weighted top-k reduction, shared
+ * expert add, RMSNorm, optional MXFP8 output.
+ *
+ * [K3] routed role, top-k finalize; [MH] AllReduceMHC.finalize (top-k
+ * reduction and shared-expert add folded into one pass, fp32 weights) and
+ * _LamportMHCDeviceKernel (RMSNorm and MXFP8 of the bf16 output). On one GPU
+ * the tensor-parallel all-reduce of the pages is the identity. Per token t:
+ *   acc = 0; for k = 0..K-1 with r = row_of_pair[t*K+k] >= 0:
+ *       acc = fma(expert_weights[t*K+k], f32(y[r, :]), acc)
+ *   if shared: acc = acc + f32(shared[t, :]);   h = bf16_rne(acc)
+ *   ss = sum_d f32(h_d)^2 in fp32 (flags bit 0: each square rounded to bf16
+ *        first, the bf16-square mode of [K3]); the summation order is the
+ *        kernel's (a tree), not sequential
+ *   inv = 1 / sqrt(ss / D + eps), correctly rounded from double
+ *   out[t, d] = bf16_rne( (f32(h_d) * inv) * f32(gamma_d) )
+ * MXFP8 (mx_codes and mx_scales both set; D % 32 == 0): for each 32-element
+ * block j of out[t, :]: amax = max |out|; p = amax * fp32(1/448);
+ *   byte = clamp(ceil(log2 p) + 127, 0, 254) (0 when p == 0);
+ *   mx_scales[t*(D/32) + j] = byte  (row-major, no padding);
+ *   mx_codes[t, 32j+i] = e4m3_rne(clamp(out * 2^(127-byte), -448, 448)).
+ *
+ * y_permuted    [rows, D] bf16 unweighted expert outputs in permuted order
+ * expert_weights [T, K] fp32;  row_of_pair [T, K] int32 (-1: slot not held;
+ *               values must be < rows)
+ * shared        [T, D] bf16, nullable;  gamma [D] bf16
+ * out           [T, D] bf16;  mx_codes [T, D] uint8 (16-byte aligned) and
+ *               mx_scales [T, D/32] uint8: both NULL or both set
+ * flags         bit 0: bf16-rounded squares; other bits must be 0
+ * D % 8 == 0, D <= 65536; K <= 64.
+ * ---------------------------------------------------------------------- */
+#define MOE_FINALIZE_BF16_SQUARES 1u
+MOE_API moe_status_t moe_finalize_rmsnorm(const moe_bf16_t *y_permuted, int64_t rows,
+                                  const float *expert_weights,
+                                  const int32_t *row_of_pair,
+                                  const moe_bf16_t *shared,
+                                  const moe_bf16_t *gamma, float eps, int32_t T,
+                                  int32_t K, int32_t D, uint32_t flags,
+                                  moe_bf16_t *out, uint8_t *mx_codes,
+                                  uint8_t *mx_scales, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_convert_check -- the device conversions the kernels use, exposed so that
+ * a caller (and the test suite) can compare them with a reference: for
+ * i < n, bf16_out[i] = bf16_rne(in[i]) and e4m3_out[i] =
+ * e4m3_rne(clamp(in[i], -448, 448)). Either output may be NULL.
+ * ---------------------------------------------------------------------- */
+MOE_API moe_status_t moe_convert_check(const float *in, int64_t n, moe_bf16_t *bf16_out,
+                               uint8_t *e4m3_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_SHUFFLE_H */

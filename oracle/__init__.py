@@ -65,20 +65,22 @@ def _load():
     lib.orc_f32_to_e4m3_array.argtypes = [_f32p, _u8p, _ll]
     lib.orc_ue8m0_array.argtypes = [_f32p, _u8p, _ll]
     lib.orc_topk.argtypes = [_f32p, _ll, _ll, _int, _int, _int, _i32p]
-    lib.orc_shuffle.argtypes = [_f32p, _ll, _ll, _int, _int, _int, _ll,
+    lib.orc_shuffle.argtypes = [_f32p, _ll, _ll, _int, _int, _int, _int, _ll,
                                 _i32p, _i32p, _i32p, _i32p]
     lib.orc_gather_scale.argtypes = [_u16p, _int, _int, _i32p, _i32p, _int,
-                                     _f32p, _ll, _ll, _int, _ll, _u16p]
+                                     _f32p, _ll, _ll, _int, _int, _ll, _u16p]
     lib.orc_gather_scale_quant.argtypes = [_u16p, _int, _int, _i32p, _i32p,
                                            _int, _f32p, _ll, _ll, _int, _f32p,
-                                           _ll, _u8p, _f32p]
-    lib.orc_scatter_add.argtypes = [_u16p, _int, _u16p, _i32p, _int, _int, _ll]
+                                           _int, _ll, _u8p, _f32p]
+    lib.orc_scatter_add.argtypes = [_u16p, _int, _u16p, _i32p, _int, _int, _int,
+                                    _ll]
     lib.orc_finalize_rmsnorm.argtypes = [_u16p, _ll, _f32p, _i32p, _u16p,
                                          _u16p, ctypes.c_float, _int, _int,
                                          _int, ctypes.c_uint, _u16p, _u8p, _u8p]
+    lib.orc_mxfp8_quantize.argtypes = [_u16p, _int, _int, _u8p, _u8p]
     for name in ("orc_topk", "orc_shuffle", "orc_gather_scale",
                  "orc_gather_scale_quant", "orc_scatter_add",
-                 "orc_finalize_rmsnorm"):
+                 "orc_finalize_rmsnorm", "orc_mxfp8_quantize"):
         getattr(lib, name).restype = _int
     _lib = lib
     return lib
@@ -94,6 +96,11 @@ def _p(arr, ctype):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
+
+
+def _opt(count):
+    """(given?, value) of an optional valid count."""
+    return (0, 0) if count is None else (1, int(count))
 
 
 def _scores_view(scores):
@@ -157,8 +164,8 @@ def shuffle(scores: np.ndarray, K: int, valid_token_count: int | None = None):
     ei = np.empty(a, dtype=np.int32)
     ti = np.empty(a, dtype=np.int32)
     rop = np.empty((T, K), dtype=np.int32)
-    vtc = -1 if valid_token_count is None else int(valid_token_count)
-    _check(_load().orc_shuffle(base, st, se, T, E, K, vtc,
+    has, vtc = _opt(valid_token_count)
+    _check(_load().orc_shuffle(base, st, se, T, E, K, has, vtc,
                                _p(counts, _i32p), _p(ei, _i32p), _p(ti, _i32p),
                                _p(rop, _i32p)), "shuffle")
     return counts, ei, ti, rop
@@ -172,10 +179,10 @@ def gather_scale(x, token_indices, expert_indices, scores, valid_rows=None,
     base, st, se = _scores_view(scores)
     if out is None:
         out = np.zeros((a, D), dtype=np.uint16)
-    vr = -1 if valid_rows is None else int(valid_rows)
+    has, vr = _opt(valid_rows)
     _check(_load().orc_gather_scale(
         _p(x, _u16p), T, D, _p(token_indices, _i32p), _p(expert_indices, _i32p),
-        a, base, st, se, scores.shape[1], vr,
+        a, base, st, se, scores.shape[1], has, vr,
         _p(out, _u16p)), "gather_scale")
     return out
 
@@ -190,11 +197,11 @@ def gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=None,
     if out_scale is None:
         out_scale = np.zeros(a, dtype=np.float32)
     ub = None if scale_ub is None else np.array([scale_ub], dtype=np.float32)
-    vr = -1 if valid_rows is None else int(valid_rows)
+    has, vr = _opt(valid_rows)
     _check(_load().orc_gather_scale_quant(
         _p(x, _u16p), T, D, _p(token_indices, _i32p), _p(expert_indices, _i32p),
         a, base, st, se, scores.shape[1], _p(ub, _f32p),
-        vr, _p(out, _u8p), _p(out_scale, _f32p)), "gather_scale_quant")
+        has, vr, _p(out, _u8p), _p(out_scale, _f32p)), "gather_scale_quant")
     return out, out_scale
 
 
@@ -202,9 +209,9 @@ def scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None):
     """In place on ``out_tokens`` (uint16 (T,D)); also returns it."""
     T, D = out_tokens.shape
     a = in_tokens.shape[0]
-    vr = -1 if valid_rows is None else int(valid_rows)
+    has, vr = _opt(valid_rows)
     _check(_load().orc_scatter_add(_p(out_tokens, _u16p), T, _p(in_tokens, _u16p),
-                                   _p(token_indices, _i32p), a, D, vr),
+                                   _p(token_indices, _i32p), a, D, has, vr),
            "scatter_add")
     return out_tokens
 
@@ -223,3 +230,14 @@ def finalize_rmsnorm(y, expert_weights, row_of_pair, shared, gamma, eps,
         _p(shared, _u16p), _p(gamma, _u16p), float(eps), T, K, D, int(flags),
         _p(out, _u16p), _p(codes, _u8p), _p(scales, _u8p)), "finalize_rmsnorm")
     return (out, codes, scales) if mxfp8 else out
+
+
+def mxfp8_quantize(o_bits: np.ndarray):
+    """MXFP8 of bf16 rows (uint16 (rows, D), D % 32 == 0): (codes, scales)."""
+    o_bits = np.ascontiguousarray(o_bits, dtype=np.uint16)
+    rows, D = o_bits.shape
+    codes = np.empty((rows, D), dtype=np.uint8)
+    scales = np.empty((rows, D // 32), dtype=np.uint8)
+    _check(_load().orc_mxfp8_quantize(_p(o_bits, _u16p), rows, D, _p(codes, _u8p),
+                                      _p(scales, _u8p)), "mxfp8_quantize")
+    return codes, scales

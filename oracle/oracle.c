@@ -193,13 +193,14 @@ int orc_topk(const float *scores, long long st, long long se, int T, int E,
  *   rows [V, T*K) hold the pairs of tokens t >= vtc in (t, k) order, with
  *              token_indices = t and expert_indices = -1.
  *   row_of_pair[t*K+k] is the row of pair (t, k), -1 for t >= vtc.
- * vtc < 0 means "all T tokens are valid"; otherwise it is clamped to [0, T]. */
+ * Without a valid count (has_vtc == 0) all T tokens are valid; a given count
+ * is clamped to [0, T]. */
 int orc_shuffle(const float *scores, long long st, long long se, int T, int E,
-                int K, long long vtc_in, int *counts /* [E+1] */,
+                int K, int has_vtc, long long vtc_in, int *counts /* [E+1] */,
                 int *expert_indices, int *token_indices, int *row_of_pair)
 {
     if (T < 0 || E < 1 || K < 1 || K > E) return ORC_BAD;
-    int vtc = vtc_in < 0 ? T : clamp_count(vtc_in, T);
+    int vtc = has_vtc ? clamp_count(vtc_in, T) : T;
     long long a = (long long)T * K;
     int *sel = (int *)malloc(sizeof(int) * (size_t)(a > 0 ? a : 1));
     unsigned char *taken = (unsigned char *)malloc((size_t)E);
@@ -247,14 +248,15 @@ int orc_shuffle(const float *scores, long long st, long long se, int T, int E,
 /* [GS] gather_scale_dense_tokens and its kernel: output row i copies token
  * token_indices[i] scaled by its score scores[t, expert_indices[i]] (product
  * taken in fp32, stored in x's dtype), for rows below the valid bound only;
- * other rows are left as they were. valid_rows < 0 means all a rows. */
+ * other rows are left as they were. Without a bound (has_valid == 0) all a
+ * rows are valid; a given bound is clamped to [0, a] (as everywhere below). */
 int orc_gather_scale(const uint16_t *x, int T, int D, const int *token_indices,
                      const int *expert_indices, int a, const float *scores,
-                     long long st, long long se, int E, long long valid_rows,
-                     uint16_t *out /* [a*D] */)
+                     long long st, long long se, int E, int has_valid,
+                     long long valid_rows, uint16_t *out /* [a*D] */)
 {
     if (T < 0 || D < 0 || a < 0 || E < 1) return ORC_BAD;
-    int V = valid_rows < 0 ? a : clamp_count(valid_rows, a);
+    int V = has_valid ? clamp_count(valid_rows, a) : a;
     for (int i = 0; i < V; ++i) {
         int t = token_indices[i], e = expert_indices[i];
         if (t < 0 || t >= T || e < 0 || e >= E) return ORC_BAD;
@@ -276,11 +278,12 @@ int orc_gather_scale_quant(const uint16_t *x, int T, int D,
                            const int *token_indices, const int *expert_indices,
                            int a, const float *scores, long long st,
                            long long se, int E, const float *scale_ub,
-                           long long valid_rows, uint8_t *out_fp8 /* [a*D] */,
+                           int has_valid, long long valid_rows,
+                           uint8_t *out_fp8 /* [a*D] */,
                            float *out_scale /* [a] */)
 {
     if (T < 0 || D < 0 || a < 0 || E < 1) return ORC_BAD;
-    int V = valid_rows < 0 ? a : clamp_count(valid_rows, a);
+    int V = has_valid ? clamp_count(valid_rows, a) : a;
     for (int i = 0; i < V; ++i) {
         int t = token_indices[i], e = expert_indices[i];
         if (t < 0 || t >= T || e < 0 || e >= E) return ORC_BAD;
@@ -323,10 +326,10 @@ int orc_gather_scale_quant(const uint16_t *x, int T, int D,
  * no valid row is left untouched. */
 int orc_scatter_add(uint16_t *out /* [T*D] in/out */, int T,
                     const uint16_t *in /* [a*D] */, const int *token_indices,
-                    int a, int D, long long valid_rows)
+                    int a, int D, int has_valid, long long valid_rows)
 {
     if (T < 0 || D < 0 || a < 0) return ORC_BAD;
-    int V = valid_rows < 0 ? a : clamp_count(valid_rows, a);
+    int V = has_valid ? clamp_count(valid_rows, a) : a;
     /* bucket the valid rows by token, keeping ascending row order */
     int *cnt = (int *)calloc((size_t)T + 1, sizeof(int));
     for (int r = 0; r < V; ++r) {
@@ -354,6 +357,38 @@ int orc_scatter_add(uint16_t *out /* [T*D] in/out */, int T,
     free(rows);
     free(fill);
     free(cnt);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 of bf16 rows.                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* [MH] _LamportMHCDeviceKernel, MXFP8 output: per 32-element block of a bf16
+ * row, the UE8M0 byte of the block max (orc_ue8m0_from_amax), and codes
+ * E4M3(o * 2^(127 - byte)) with saturation. Scales row-major [rows, D/32]. */
+int orc_mxfp8_quantize(const uint16_t *o, int rows, int D, uint8_t *codes,
+                       uint8_t *scales)
+{
+    if (rows < 0 || D < 0 || D % 32 != 0) return ORC_BAD;
+    int nb = D / 32;
+    for (int t = 0; t < rows; ++t) {
+        const uint16_t *orow = o + (long long)t * D;
+        for (int j = 0; j < nb; ++j) {
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float av = fabsf(orc_bf16_to_f32(orow[j * 32 + i]));
+                if (av > amax) amax = av;
+            }
+            uint8_t byte = orc_ue8m0_from_amax(amax);
+            scales[(long long)t * nb + j] = byte;
+            float mult = ldexpf(1.0f, 127 - (int)byte);
+            for (int i = 0; i < 32; ++i) {
+                float v = orc_bf16_to_f32(orow[j * 32 + i]) * mult;
+                codes[(long long)t * D + j * 32 + i] = orc_f32_to_e4m3(v);
+            }
+        }
+    }
     return ORC_OK;
 }
 
@@ -420,23 +455,9 @@ int orc_finalize_rmsnorm(const uint16_t *y, long long rows, const float *w,
             v = v * orc_bf16_to_f32(gamma[d]);
             o[d] = orc_f32_to_bf16(v);
         }
-        if (mx_codes) {
-            int nb = D / 32;
-            for (int j = 0; j < nb; ++j) {
-                float amax = 0.0f;
-                for (int i = 0; i < 32; ++i) {
-                    float av = fabsf(orc_bf16_to_f32(o[j * 32 + i]));
-                    if (av > amax) amax = av;
-                }
-                uint8_t byte = orc_ue8m0_from_amax(amax);
-                mx_scales[(long long)t * nb + j] = byte;
-                float mult = ldexpf(1.0f, 127 - (int)byte);
-                for (int i = 0; i < 32; ++i) {
-                    float v = orc_bf16_to_f32(o[j * 32 + i]) * mult;
-                    mx_codes[(long long)t * D + j * 32 + i] = orc_f32_to_e4m3(v);
-                }
-            }
-        }
+        if (mx_codes)
+            orc_mxfp8_quantize(o, 1, D, mx_codes + (long long)t * D,
+                               mx_scales + (long long)t * (D / 32));
     }
     free(h);
     return ORC_OK;

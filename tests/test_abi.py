@@ -1,0 +1,186 @@
+"""The C ABI library on the CPU: it loads, exports every entry point the header
+declares (with the binding's signature table covering each), and rejects bad
+arguments on the host with the documented status before any HIP call (so
+these calls run without a GPU). No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_moe_shuffle_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_shuffle.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # a 256-byte aligned non-NULL address; never dereferenced here
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+# The rejection tests pass fake device addresses that the host checks must
+# refuse. Where a GPU is visible a wrong check would launch a kernel on them,
+# so there these tests are skipped (they are host logic; the CPU runs them).
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from combine_moe_shuffle_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_path(lib):
+    names = set(_declared())
+    for n in ("moe_shuffle", "moe_gather_scale", "moe_gather_scale_quant",
+              "moe_scatter_add", "moe_finalize_rmsnorm"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n                # exported by the .so
+        assert n in _lib.SIGNATURES, n           # declared to ctypes
+
+
+def test_signature_table_arity_matches_header(lib):
+    text = open(HEADER).read()
+    for name, (_, args) in _lib.SIGNATURES.items():
+        m = re.search(rf"\b{name}\s*\(([^)]*)\)", text, re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() not in ("", "void")]
+        assert len(params) == len(args), (name, len(params), len(args))
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_workspace_sizes(lib):
+    # shuffle: T*K pair words + E*ceil(T/64) histogram words, 256-aligned
+    assert lib.moe_shuffle_workspace_bytes(8192, 256, 8) == 8192 * 8 * 4 + 256 * 128 * 4
+    assert lib.moe_shuffle_workspace_bytes(65, 3, 2) == 768 + 256
+    assert lib.moe_shuffle_workspace_bytes(-1, 3, 2) == 0
+    # scatter: (T+1) counters + a slots + a list entries
+    assert lib.moe_scatter_add_workspace_bytes(8192, 65536) == 33024 + 2 * 262144
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+@host_only
+def test_shuffle_rejects(lib):
+    f = lib.moe_shuffle
+    # K > E
+    assert f(FAKE, 8, 1, 4, 8, 9, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert "K must be" in _err(lib)
+    # E too large
+    assert f(FAKE, 2048, 1, 4, 2048, 8, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+             None) == UNSUPPORTED
+    # K too large
+    assert f(FAKE, 128, 1, 4, 128, 65, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+             None) == UNSUPPORTED
+    # workspace too small / NULL
+    assert f(FAKE, 8, 1, 64, 8, 2, None, FAKE, FAKE, FAKE, None, FAKE, 16, None) == WORKSPACE
+    assert f(FAKE, 8, 1, 64, 8, 2, None, FAKE, FAKE, FAKE, None, None, 1 << 20,
+             None) == WORKSPACE
+    # NULL scores, NULL counts, negative stride, misaligned workspace
+    assert f(None, 8, 1, 64, 8, 2, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 8, 1, 64, 8, 2, None, None, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, -8, 1, 64, 8, 2, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == INVALID
+    assert f(FAKE, 8, 1, 64, 8, 2, None, FAKE, FAKE, FAKE, None, FAKE + 4, 1 << 20,
+             None) == INVALID
+    # T*K overflow
+    assert f(FAKE, 64, 1, 1 << 30, 64, 8, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+             None) == INVALID
+
+
+@host_only
+def test_gather_rejects(lib):
+    g = lib.moe_gather_scale
+    assert g(FAKE, 4, 12, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID  # D % 8
+    assert "multiple of 8" in _err(lib)
+    assert g(FAKE + 8, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    assert g(FAKE, 4, 16, None, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    assert g(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 0, None, FAKE, None) == INVALID  # E
+    assert g(FAKE, 4, 16, FAKE, FAKE, -1, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    # nothing to do: OK without touching anything
+    assert g(None, 0, 16, None, None, 0, None, 4, 1, 4, None, None, None) == OK
+    assert g(None, 4, 0, None, None, 8, None, 4, 1, 4, None, None, None) == OK
+    bt = lib.moe_gather_scale_by_token
+    assert bt(FAKE, 4, 16, FAKE, 0, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    assert bt(FAKE, 4, 16, FAKE, 65, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    q = lib.moe_gather_scale_quant
+    assert q(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, None, FAKE, None,
+             None) == INVALID  # out_scale NULL
+    assert q(FAKE, 4, 1 << 17, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, None, FAKE, FAKE,
+             None) == UNSUPPORTED
+    assert q(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, FAKE + 2, None, FAKE, FAKE,
+             None) == INVALID  # misaligned scale_ub
+
+
+@host_only
+def test_scatter_rejects(lib):
+    s = lib.moe_scatter_add
+    assert s(FAKE, 8, FAKE, FAKE, 16, 64, None, FAKE, 16, None) == WORKSPACE
+    assert s(FAKE, 8, FAKE, None, 16, 64, None, FAKE, 1 << 20, None) == INVALID
+    assert s(FAKE, 8, FAKE, FAKE, 16, 60, None, FAKE, 1 << 20, None) == INVALID
+    assert s(FAKE, 8, FAKE + 16, FAKE, 16, 64, None, FAKE + 8, 1 << 20, None) == INVALID
+    assert s(None, 8, None, None, 0, 64, None, None, 0, None) == OK       # a == 0
+    b = lib.moe_scatter_add_by_token
+    assert b(FAKE, 8, FAKE, None, 2, 16, 64, None, None) == INVALID
+    assert b(FAKE, 8, FAKE, FAKE, 0, 16, 64, None, None) == INVALID
+
+
+@host_only
+def test_finalize_rejects(lib):
+    f = lib.moe_finalize_rmsnorm
+    args = dict(y=FAKE, rows=64, w=FAKE, rop=FAKE, sh=FAKE, g=FAKE, eps=1e-6, T=8, K=8,
+                D=256, flags=0, out=FAKE, mc=None, ms=None)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["y"], a["rows"], a["w"], a["rop"], a["sh"], a["g"], a["eps"], a["T"],
+                 a["K"], a["D"], a["flags"], a["out"], a["mc"], a["ms"], None)
+
+    assert call(mc=FAKE) == INVALID                       # codes without scales
+    assert call(mc=FAKE, ms=FAKE, D=264) == INVALID       # D % 32 for MXFP8
+    assert call(flags=2) == INVALID
+    assert call(K=0) == INVALID
+    assert call(K=65) == UNSUPPORTED
+    assert call(D=1 << 17) == UNSUPPORTED
+    assert call(g=None) == INVALID
+    assert call(sh=FAKE + 8) == INVALID
+    assert call(T=0) == OK
+
+
+@host_only
+def test_convert_rejects(lib):
+    assert lib.moe_convert_check(None, 4, None, None, None) == INVALID
+    assert lib.moe_convert_check(None, 0, None, None, None) == OK
+
+
+def test_ops_raise_without_gpu_tensors():
+    import torch
+
+    from combine_moe_shuffle_amd import ops
+    with pytest.raises(ValueError):
+        ops.moe_gather_scale(torch.zeros(4, 16, dtype=torch.bfloat16),
+                             torch.zeros(8, dtype=torch.int32),
+                             torch.zeros(8, dtype=torch.int32), torch.zeros(4, 2))

@@ -1,0 +1,372 @@
+"""GPU parity: every stage through the C ABI against the CPU oracle, on the
+same seeded inputs.
+
+Bar: integer outputs (shuffle) and the bf16 gather are bit-exact; the combine
+is designed bit-exact (same fp32 addition order as the oracle); the finalize
+output is within |gpu - ref| <= 2e-2 + 1e-2 * |ref| (its row sum of squares is
+a tree reduction, the oracle's is sequential); FP8 codes may differ by at most
+one code on at most 0.1 % of elements (they are expected to be exact); MXFP8
+codes and scales are exact when the oracle quantises the GPU's own bf16
+output (the split check), so quantiser parity is separate from RMSNorm
+rounding.
+
+Sizes: small shapes spanning several slices and a ragged tail, the edge cases
+(empty, single token, K = E, valid count 0 / T / beyond T, ties, strided
+scores, tokens with more than 64 rows), and the full workload sizes in the
+launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from combine_moe_shuffle_amd import ops
+from combine_moe_shuffle_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5A5
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    from combine_moe_shuffle_amd import _lib
+    _lib.load()
+    return torch.device("cuda:0")
+
+
+def bf_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def bits_host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def i32_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def scalar_dev(v, dev):
+    return None if v is None else torch.tensor([v], dtype=torch.int32, device=dev)
+
+
+def ordinal(codes):
+    """E4M3 sign-magnitude code -> monotone integer."""
+    c = codes.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def assert_fp8_close(got, want, what):
+    d = np.abs(ordinal(got) - ordinal(want))
+    bad = d > 0
+    assert d.max(initial=0) <= 1, f"{what}: code distance {d.max()}"
+    assert bad.mean() <= 1e-3, f"{what}: {bad.mean():.2e} of codes differ"
+
+
+# ---------------------------------------------------------------- conversions
+def test_device_conversions_match_oracle_encoders(dev):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    allbf = orc.bf16_to_f32(h)
+    allbf = allbf[np.isfinite(allbf)]
+    g = np.random.default_rng(5)
+    rnd = g.integers(0, 2**32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    rnd[:100_000] = (rnd[:100_000] & 0xFFFF0000) | 0x8000          # bf16 ties
+    rnd = rnd.view(np.float32)
+    rnd = rnd[np.isfinite(rnd)]
+    vals = np.concatenate([allbf * np.float32(s) for s in (1.0, 0.125, 3.7, 1e-3, 97.0,
+                                                             2.0 ** -12)] + [rnd])
+    vals = vals.astype(np.float32)
+    say("convert_check", vals.size)
+    bf, e4 = ops.moe_convert_check(torch.from_numpy(vals).to(dev))
+    bf = bf.cpu().numpy().view(np.uint16)
+    e4 = e4.cpu().numpy()
+    fin = np.isfinite(vals)
+    assert np.array_equal(bf[fin], orc.f32_to_bf16(vals)[fin])
+    clipped = np.clip(vals, -448.0, 448.0).astype(np.float32)
+    assert np.array_equal(e4[fin], orc.f32_to_e4m3(clipped)[fin])
+
+
+# ---------------------------------------------------------------- shuffle
+SHUFFLE_CASES = [
+    # (name, T, E, K, vtc, score kind)
+    ("tiny-workload", None, None, None, None, "tiny"),
+    ("quant-workload", None, None, None, None, "quant"),
+    ("zipf-workload", None, None, None, 6000, "zipf"),
+    ("single", 1, 1, 1, None, "normal"),
+    ("K=E", 63, 8, 8, None, "normal"),
+    ("ragged", 200, 257, 3, 137, "normal"),
+    ("wide", 130, 1024, 64, None, "normal"),
+    ("ties", 300, 40, 6, 250, "ties"),
+    ("strided", 150, 48, 5, None, "strided"),
+    ("vtc0", 100, 16, 2, 0, "normal"),
+    ("vtc-beyond", 100, 16, 2, 99999, "normal"),
+    ("vtc-negative", 100, 16, 2, -5, "normal"),
+    ("T0", 0, 16, 2, None, "normal"),
+]
+
+
+def _scores_for(kind, T, E, seed=0):
+    g = np.random.default_rng(seed)
+    if kind == "ties":
+        s = g.integers(0, 4, size=(T, E)).astype(np.float32)
+        s[g.random((T, E)) < 0.3] = -0.0
+        return s
+    if kind == "strided":
+        return g.standard_normal((E, T)).astype(np.float32).T   # (T, E) view
+    return g.standard_normal((T, E)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", SHUFFLE_CASES, ids=[c[0] for c in SHUFFLE_CASES])
+def test_shuffle_bit_exact(dev, case):
+    name, T, E, K, vtc, kind = case
+    if kind in W.WORKLOADS:
+        wl = W.WORKLOADS[kind]
+        s = W.router_scores(wl)
+        T, E, K = wl.T, wl.E, wl.K
+    else:
+        s = _scores_for(kind, T, E)
+    say("shuffle", name, T, E, K, vtc)
+    counts, ei, ti, rop = orc.shuffle(s, K, vtc)
+    if kind == "strided":
+        base = torch.from_numpy(np.ascontiguousarray(s.T)).to(dev)
+        sd = base.t()                                  # strides (1, T)
+    else:
+        sd = torch.from_numpy(np.ascontiguousarray(s)).to(dev)
+    gc, gei, gti, grop = ops.moe_shuffle(sd, K, scalar_dev(vtc, dev))
+    assert np.array_equal(gc.cpu().numpy(), counts)
+    assert np.array_equal(gei.cpu().numpy(), ei)
+    assert np.array_equal(gti.cpu().numpy(), ti)
+    assert np.array_equal(grop.cpu().numpy(), rop)
+    # deterministic: a second run gives the same bits
+    gc2, gei2, gti2, grop2 = ops.moe_shuffle(sd, K, scalar_dev(vtc, dev))
+    assert torch.equal(gti, gti2) and torch.equal(grop, grop2)
+
+
+# ---------------------------------------------------------------- gather
+GATHER_CASES = [
+    # (name, T, D, E, K, vtc)
+    ("tiny-workload", 64, 1024, 8, 2, None),
+    ("ragged-D", 77, 8 * (64 * 7 + 3), 9, 3, 70),      # partial last slice
+    ("short-row", 33, 8, 4, 2, None),                  # one chunk per row
+    ("odd", 129, 8 * 1000, 13, 4, 100),
+    ("vtc0", 16, 512, 4, 2, 0),
+]
+
+
+def _dispatch_case(T, D, E, K, vtc, seed=0):
+    wl = W.WORKLOADS["tiny"]
+    wl = W.Workload(**{**wl.__dict__, "router": "softmax"})
+    inp = W.dispatch_inputs(wl, T=T, D=D, E=E, K=K, vtc=vtc, seed=seed, out0="normal")
+    counts, ei, ti, rop = orc.shuffle(inp.scores, K, vtc)
+    return inp, counts, ei, ti, rop
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+@pytest.mark.parametrize("path", ["rows", "by_token"])
+def test_gather_scale_bit_exact(dev, case, path):
+    name, T, D, E, K, vtc = case
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc)
+    V = int(counts[E])
+    say("gather", path, name, T, D, E, K, V)
+    want = np.full((T * K, D), SENTINEL, np.uint16)
+    orc.gather_scale(inp.x, ti, ei, inp.scores, V, want)
+    out = torch.full((T * K, D), SENTINEL - 65536, dtype=torch.int16,
+                     device=dev).view(torch.bfloat16)
+    x = bf_dev(inp.x, dev)
+    s = torch.from_numpy(inp.scores).to(dev)
+    vr = scalar_dev(V, dev)
+    if path == "rows":
+        ops.moe_gather_scale(x, i32_dev(ti, dev), i32_dev(ei, dev), s, vr, out)
+    else:
+        ops.moe_gather_scale_by_token(x, i32_dev(rop, dev), i32_dev(ei, dev), s, vr, out)
+    assert np.array_equal(bits_host(out), want)
+
+
+@pytest.mark.parametrize("ub", [None, 1200.0, 1e-3])
+@pytest.mark.parametrize("shape", [(96, 8 * (64 * 5 + 7), 6, 2, 90), (40, 5120, 16, 1, None),
+                                   (20, 8, 3, 2, None)], ids=["ragged", "D5120", "D8"])
+def test_gather_scale_quant(dev, ub, shape):
+    T, D, E, K, vtc = shape
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=3)
+    x = inp.x.copy()
+    x[ti[0]] = 0                                   # an all-zero row
+    V = int(counts[E])
+    say("quant", shape, ub, V)
+    wc = np.full((T * K, D), 0x5A, np.uint8)
+    ws = np.full(T * K, -7.0, np.float32)
+    orc.gather_scale_quant(x, ti, ei, inp.scores, ub, V, wc, ws)
+    codes = torch.full((T * K, D), 0x5A, dtype=torch.uint8, device=dev)
+    scale = torch.full((T * K,), -7.0, dtype=torch.float32, device=dev)
+    ubd = None if ub is None else torch.tensor([ub], dtype=torch.float32, device=dev)
+    ops.moe_gather_scale_quant(bf_dev(x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                               torch.from_numpy(inp.scores).to(dev), ubd, scalar_dev(V, dev),
+                               codes, scale)
+    gc, gs = codes.cpu().numpy(), scale.cpu().numpy()
+    assert np.array_equal(gs.view(np.uint32), ws.view(np.uint32))   # scales exact
+    assert np.array_equal(gc[V:], wc[V:])                            # untouched rows
+    assert_fp8_close(gc[:V], wc[:V], "rowwise fp8")
+    assert np.array_equal(gc, wc)                                    # expected exact
+
+
+# ---------------------------------------------------------------- scatter
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+@pytest.mark.parametrize("path", ["general", "by_token"])
+def test_scatter_add_bit_exact(dev, case, path):
+    name, T, D, E, K, vtc = case
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=1)
+    V = int(counts[E])
+    say("scatter", path, name, T, D, K, V)
+    want = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+    out = bf_dev(inp.out0, dev)
+    y = bf_dev(inp.y, dev)
+    if path == "general":
+        ops.moe_scatter_add(out, y, i32_dev(ti, dev), scalar_dev(V, dev))
+    else:
+        ops.moe_scatter_add_by_token(out, y, i32_dev(rop, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+
+
+def test_scatter_add_general_long_lists(dev):
+    """Arbitrary token_indices: a token owning 100 rows (beyond one wave's
+    sort), unsorted rows, rows of no token."""
+    g = np.random.default_rng(9)
+    T, D, a = 12, 8 * 70, 400
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    ti[g.permutation(a)[:100]] = 5
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    V = 350
+    say("scatter long lists", T, D, a, V)
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+
+
+# ---------------------------------------------------------------- finalize
+def _close(got_bits, want_bits, what):
+    g = orc.bf16_to_f32(got_bits).astype(np.float64)
+    r = orc.bf16_to_f32(want_bits).astype(np.float64)
+    err = np.abs(g - r)
+    tol = 2e-2 + 1e-2 * np.abs(r)
+    assert np.all(err <= tol), f"{what}: max abs {err.max():.3e}"
+
+
+FIN_CASES = [
+    # (name, T, D, K, hole_frac, shared, flags, mxfp8)
+    ("decode-1", 1, 7168, 8, 0.0, True, 0, False),
+    ("decode-8", 8, 7168, 8, 0.0, True, 0, False),
+    ("decode-32", 32, 7168, 8, 0.0, True, 0, False),
+    ("decode-128", 128, 7168, 8, 0.0, True, 0, False),
+    ("holes-noshared", 50, 1024, 4, 0.3, False, 0, True),
+    ("bf16-squares", 20, 2048, 8, 0.1, True, 1, False),
+    ("ragged-D", 33, 32 * 49, 3, 0.0, True, 0, True),   # partial last wave
+    ("many-tokens", 2100, 640, 4, 0.05, True, 0, True),  # the many-token shape
+    ("K1", 9, 256, 1, 0.0, False, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", FIN_CASES, ids=[c[0] for c in FIN_CASES])
+def test_finalize_rmsnorm(dev, case):
+    name, T, D, K, holes, with_shared, flags, mx = case
+    wl = W.WORKLOADS["decode"] if D == 7168 else W.WORKLOADS["prefill"]
+    fi = W.finalize_inputs(wl, T=T, D=D, K=K, hole_frac=holes)
+    shared = fi.shared if with_shared else None
+    say("finalize", name, T, D, K, flags, mx)
+    want = orc.finalize_rmsnorm(fi.y, fi.w, fi.row_of_pair, shared, fi.gamma, fi.eps,
+                                flags=flags, mxfp8=False)
+    res = ops.moe_finalize_rmsnorm(bf_dev(fi.y, dev), torch.from_numpy(fi.w).to(dev),
+                                   i32_dev(fi.row_of_pair, dev),
+                                   None if shared is None else bf_dev(shared, dev),
+                                   bf_dev(fi.gamma, dev), fi.eps, flags=flags, mxfp8=mx)
+    out = res[0] if mx else res
+    got = bits_host(out)
+    _close(got, want, name)
+    if mx:
+        codes, scales = res[1].cpu().numpy(), res[2].cpu().numpy()
+        oc, os_ = orc.mxfp8_quantize(got)        # the split check
+        assert np.array_equal(scales, os_)
+        assert_fp8_close(codes, oc, "mxfp8")
+        assert np.array_equal(codes, oc)
+
+
+# ---------------------------------------------------------------- full sizes
+@pytest.fixture(scope="module")
+def zipf_inputs():
+    wl = W.WORKLOADS["zipf"]
+    inp = W.dispatch_inputs(wl)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, wl.K, wl.vtc)
+    return wl, inp, counts, ei, ti, rop
+
+
+def test_zipf_pipeline_full_size(dev, zipf_inputs):
+    """shuffle -> gather (by token) -> scatter (by token) at T=8192, D=7168,
+    E=256, K=8, valid_token_count=6000, as the benchmark launches it (row
+    bound read from counts[E] on the device); every element checked."""
+    wl, inp, counts, ei, ti, rop = zipf_inputs
+    V = int(counts[wl.E])
+    say("zipf pipeline", wl.T, wl.D, wl.E, wl.K, wl.vtc, V)
+    s = torch.from_numpy(inp.scores).to(dev)
+    gc, gei, gti, grop = ops.moe_shuffle(s, wl.K, scalar_dev(wl.vtc, dev))
+    assert np.array_equal(gc.cpu().numpy(), counts)
+    assert np.array_equal(grop.cpu().numpy(), rop)
+    vr = gc[wl.E:]
+    x = bf_dev(inp.x, dev)
+    rows = torch.empty((wl.T * wl.K, wl.D), dtype=torch.bfloat16, device=dev)
+    ops.moe_gather_scale_by_token(x, grop, gei, s, vr, rows)
+    want_rows = np.zeros((wl.T * wl.K, wl.D), np.uint16)
+    orc.gather_scale(inp.x, ti, ei, inp.scores, V, want_rows)
+    assert np.array_equal(bits_host(rows[:V]), want_rows[:V])
+    del want_rows
+    out = torch.zeros((wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    y = bf_dev(inp.y, dev)
+    ops.moe_scatter_add_by_token(out, y, grop, vr)
+    want = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+    assert np.array_equal(bits_host(out), want)
+    # the general combine and the row-order gather agree with the same oracle
+    out2 = torch.zeros_like(out)
+    ops.moe_scatter_add(out2, y, gti, vr)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    rows2 = torch.empty_like(rows)
+    ops.moe_gather_scale(x, gti, gei, s, vr, rows2)
+    assert torch.equal(rows2[:V].view(torch.int16), rows[:V].view(torch.int16))
+
+
+def test_quant_workload_full_size(dev):
+    wl = W.WORKLOADS["quant"]
+    inp = W.dispatch_inputs(wl)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, wl.K, None)
+    V = int(counts[wl.E])
+    say("quant workload", wl.T, wl.D, wl.E, wl.K)
+    s = torch.from_numpy(inp.scores).to(dev)
+    gc, gei, gti, grop = ops.moe_shuffle(s, wl.K)
+    ub = torch.tensor([wl.scale_ub], dtype=torch.float32, device=dev)
+    codes, scale = ops.moe_gather_scale_quant(bf_dev(inp.x, dev), gti, gei, s, ub, gc[wl.E:])
+    wc, ws = orc.gather_scale_quant(inp.x, ti, ei, inp.scores, wl.scale_ub, V)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert_fp8_close(codes.cpu().numpy(), wc, "quant workload")
+    out = torch.zeros((wl.T, wl.D), dtype=torch.bfloat16, device=dev)
+    ops.moe_scatter_add_by_token(out, bf_dev(inp.y, dev), grop, gc[wl.E:])
+    assert np.array_equal(bits_host(out), orc.scatter_add(inp.out0.copy(), inp.y, ti, V))
+
+
+def test_prefill_finalize_full_size(dev):
+    wl = W.WORKLOADS["prefill"]
+    fi = W.finalize_inputs(wl)
+    say("prefill finalize", wl.T, wl.D, wl.K)
+    out, codes, scales = ops.moe_finalize_rmsnorm(
+        bf_dev(fi.y, dev), torch.from_numpy(fi.w).to(dev), i32_dev(fi.row_of_pair, dev),
+        bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev), fi.eps, mxfp8=True)
+    got = bits_host(out)
+    want = orc.finalize_rmsnorm(fi.y, fi.w, fi.row_of_pair, fi.shared, fi.gamma, fi.eps)
+    _close(got, want, "prefill")
+    oc, os_ = orc.mxfp8_quantize(got)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert_fp8_close(codes.cpu().numpy(), oc, "prefill mxfp8")
