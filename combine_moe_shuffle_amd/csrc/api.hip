@@ -4,7 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/moe_shuffle.h"
+#include "moe_shuffle.h"
 #include "launch.hpp"
 
 namespace {

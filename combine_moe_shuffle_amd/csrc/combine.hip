@@ -175,29 +175,62 @@ __global__ void csr_count_kernel(const int* __restrict__ ti, int T, int a,
 }
 
 // Exclusive scan of cnt[0..n) in place (one workgroup); cnt[n] = total.
+// Tiles of kScanThreads * kScanPer counts: one coalesced load of the whole
+// tile, a transpose through LDS so each thread owns kScanPer consecutive
+// counts, a workgroup scan of the per-thread sums, and one coalesced store.
+constexpr int kScanPer = 8;
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(int* __restrict__ cnt, int n) {
-  __shared__ int part[kScanThreads];
+  __shared__ int tile[kScanThreads * kScanPer];
+  __shared__ int wave_tot[kScanThreads / kWave];
   const int tid = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int beg = min(tid * per, n);
-  const int end = min(beg + per, n);
-  int s = 0;
-  for (int i = beg; i < end; ++i) s += cnt[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  constexpr int kTile = kScanThreads * kScanPer;
+  int carry = 0;
+  for (int base = 0; base < n; base += kTile) {
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = base + k * kScanThreads + tid;
+      tile[k * kScanThreads + tid] = i < n ? cnt[i] : 0;
+    }
     __syncthreads();
-    part[tid] += v;
+    int v[kScanPer];
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      v[k] = tile[tid * kScanPer + k];
+      mine += v[k];
+    }
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    if (lane == kWave - 1) wave_tot[wave] = incl;
     __syncthreads();
+    int run = carry + incl - mine;
+    int tile_total = 0;
+    for (int w = 0; w < kScanThreads / kWave; ++w) {
+      const int wt = wave_tot[w];
+      if (w < wave) run += wt;
+      tile_total += wt;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      tile[tid * kScanPer + k] = run;
+      run += v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = base + k * kScanThreads + tid;
+      if (i < n) cnt[i] = tile[k * kScanThreads + tid];
+    }
+    carry += tile_total;
+    __syncthreads();  // tile and wave_tot are reused by the next tile
   }
-  int run = part[tid] - s;
-  for (int i = beg; i < end; ++i) {
-    const int c = cnt[i];
-    cnt[i] = run;
-    run += c;
-  }
-  if (tid == kScanThreads - 1) cnt[n] = part[tid];
+  if (tid == 0) cnt[n] = carry;
 }
 
 __global__ void csr_fill_kernel(const int* __restrict__ ti, int T, int a,
@@ -259,8 +292,8 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 SliceShape combine_shape(int nch) {
-  // kGroup rows * cpl chunks of loads in flight per lane: keep cpl <= 4
-  static const int allowed[] = {4, 3, 2, 1};
+  // kGroup rows * cpl chunks of loads are in flight per lane
+  static const int allowed[] = {2, 4, 3, 1};
   return pick_slices(nch, allowed, 4, 1 << 20);
 }
 
@@ -270,14 +303,6 @@ size_t scatter_add_workspace_bytes(int T, int a) {
   return align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
          2 * align256(static_cast<size_t>(a) * sizeof(int));
 }
-
-#define MOE_DISPATCH_CPL4(CPLV, LAUNCH) \
-  switch (CPLV) {                       \
-    case 1: LAUNCH(1); break;           \
-    case 2: LAUNCH(2); break;           \
-    case 3: LAUNCH(3); break;           \
-    default: LAUNCH(4); break;          \
-  }
 
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
@@ -289,7 +314,7 @@ hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
 #define L(C)                                                                            \
   hipLaunchKernelGGL(scatter_tokens_kernel<C>, grid, block, 0, stream, out, T, in,        \
                      row_of_pair, K, a, D, valid_rows, sh.nsl)
-  MOE_DISPATCH_CPL4(sh.cpl, L)
+  MOE_DISPATCH_CPL(sh.cpl, L)
 #undef L
   return hipGetLastError();
 }
@@ -317,7 +342,7 @@ hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const in
 #define L(C)                                                                            \
   hipLaunchKernelGGL(scatter_csr_kernel<C>, grid, block, 0, stream, out, T, in, cnt, list, \
                      D, sh.nsl)
-  MOE_DISPATCH_CPL4(sh.cpl, L)
+  MOE_DISPATCH_CPL(sh.cpl, L)
 #undef L
   return hipGetLastError();
 }

@@ -62,4 +62,17 @@ struct SliceShape {
 // and that wastes the fewest lanes.
 SliceShape pick_slices(int nch, const int* allowed, int n_allowed, int max_slices);
 
+// Instantiate LAUNCH(cpl) for the run-time chunks-per-lane value (1..8).
+#define MOE_DISPATCH_CPL(CPLV, LAUNCH) \
+  switch (CPLV) {                      \
+    case 1: LAUNCH(1); break;          \
+    case 2: LAUNCH(2); break;          \
+    case 3: LAUNCH(3); break;          \
+    case 4: LAUNCH(4); break;          \
+    case 5: LAUNCH(5); break;          \
+    case 6: LAUNCH(6); break;          \
+    case 7: LAUNCH(7); break;          \
+    default: LAUNCH(8); break;         \
+  }
+
 }  // namespace moe

@@ -1,20 +1,22 @@
 // moe_shuffle: top-k routing and the stable counting sort of the
 // (token, expert) pairs by expert, as three launches with no global atomics:
 //
-//  1. select_rank  (one block per 64 tokens, 16 waves): each wave takes the
-//     top-k of a token with the expert axis spread over its 64 lanes (K rounds
-//     of a wave-wide max over 64-bit keys that order by score, then by lower
-//     expert id). The block then ORs one bit per token into a 64-bit LDS mask
-//     per expert; a pair's rank inside its block and expert is the popcount
-//     of the mask bits of the tokens before it, and the block's per-expert
-//     count is the mask's popcount. Writes (expert | rank << 16) per pair and
-//     the [E][blocks] histogram.
-//  2. scan  (one block): exclusive scan of the histogram in expert-major
-//     order gives every (expert, block) its first row; counts[] follow.
-//  3. place  (one thread per pair): row = offset[expert][block] + rank;
-//     writes token_indices, expert_indices, row_of_pair. Pairs of tokens at
-//     or beyond the valid count keep their natural position t*K + k, which is
-//     exactly the tail order (t, k) after the V valid rows.
+//  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
+//     the top-k of two tokens at once, the expert axis spread over its 64
+//     lanes (K rounds of a DPP wave max over order-preserving score keys, the
+//     lowest tied lane holding the lowest expert id; the two reductions
+//     interleave so their lane-exchange latencies overlap). The workgroup then ORs one bit per
+//     token into a 32-bit LDS mask per expert; a pair's rank inside its
+//     workgroup and expert is the popcount of the mask bits of the tokens
+//     before it, the workgroup's per-expert count the mask's popcount.
+//     Writes (expert | rank << 16) per pair and the [E][blocks] histogram.
+//  2. expert_scan  (one wave per expert): exclusive scan of the expert's row
+//     of the histogram over blocks, in place; its total is counts[e].
+//  3. place  (one thread per pair): each workgroup scans counts[0..E) in LDS
+//     to get every expert's first row, then row = first[e] + offset[e][block]
+//     + rank; writes token_indices, expert_indices, row_of_pair. Pairs of
+//     tokens at or beyond the valid count keep their natural position
+//     t*K + k, which is exactly the tail order (t, k) after the V valid rows.
 //
 // [LY] "mslk/moe/layers.py", MetaShufflingMoE._route (index shuffling of the
 // router scores, per-expert counts) and BaselineMoE._forward (top-k routing).
@@ -25,19 +27,54 @@ namespace moe {
 
 namespace {
 
-constexpr int kTokPerBlock = 64;   // one bit per token in a 64-bit mask
-constexpr int kSelThreads = 1024;  // 16 waves, 4 tokens each
+constexpr int kTokPerBlock = 32;   // one bit per token in a 32-bit mask
+constexpr int kSelThreads = 1024;  // 16 waves, 2 tokens each
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
-constexpr int kScanThreads = 1024;
 
-// Larger key = larger score; equal scores: lower expert id. -0 is folded
-// into +0 so that the two tie, as IEEE comparison says they are equal.
-__device__ __forceinline__ uint64_t topk_key(float s, int e) {
+// Order-preserving map of a score to uint32 (larger score -> larger key).
+// -0 is folded into +0 so that the two tie, as IEEE comparison says they are
+// equal. Every real score maps above 0, which marks an empty candidate.
+__device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One DPP max step on N independent values, written step-major so the N
+// chains interleave and fill each other's DPP hazard slots.
+template <int N, int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t (&v)[N]) {
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    if constexpr (ROW_MASK == 0xF) {
+      // every lane reads a valid source: the move can fold into the max
+      v[q] = max(v[q], static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(
+                           static_cast<int>(v[q]), CTRL, 0xF, 0xF, true)));
+    } else {
+      // lanes of masked rows keep their own value
+      v[q] = max(v[q], static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                           static_cast<int>(v[q]), static_cast<int>(v[q]), CTRL, ROW_MASK,
+                           0xF, false)));
+    }
+  }
+}
+
+// Wave-wide max of N uint32 values at once, uniform results. Quad swaps and
+// the half-row and row mirrors leave each 16-lane row's max in all its lanes;
+// row_bcast15 then folds row 0 into row 1 and row 2 into row 3, row_bcast31
+// folds row 1 into rows 2 and 3, so lane 63 holds the wave max.
+template <int N>
+__device__ __forceinline__ void wave_max_keys(uint32_t (&v)[N], uint32_t (&out)[N]) {
+  dpp_max_step<N, 0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  dpp_max_step<N, 0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  dpp_max_step<N, 0x141, 0xF>(v);  // row_half_mirror
+  dpp_max_step<N, 0x140, 0xF>(v);  // row_mirror
+  dpp_max_step<N, 0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  dpp_max_step<N, 0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+#pragma unroll
+  for (int q = 0; q < N; ++q)
+    out[q] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v[q]), 63));
 }
 
 __device__ __forceinline__ int clamp_count(const int* p, int hi) {
@@ -52,7 +89,7 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
     const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
     const int* __restrict__ vtc_ptr, int* __restrict__ pair, int* __restrict__ hist,
     int nblk) {
-  __shared__ unsigned long long mask[kMaxE];
+  __shared__ uint32_t mask[kMaxE];
   __shared__ int sel[kTokPerBlock * kMaxK];
 
   const int blk = blockIdx.x;
@@ -62,38 +99,85 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
   const int wave = uniform(threadIdx.x >> 6);
   const int nwaves = kSelThreads / kWave;
 
-  for (int e = threadIdx.x; e < E; e += kSelThreads) mask[e] = 0ull;
+  for (int e = threadIdx.x; e < E; e += kSelThreads) mask[e] = 0u;
 
-  // ---- top-k, one token per wave at a time
-  for (int tl = wave; tl < kTokPerBlock; tl += nwaves) {
-    const int t = t0 + tl;
-    if (t >= vtc) break;
-    const float* srow = scores + static_cast<int64_t>(t) * st;
-    uint64_t key[PL];
+  // ---- top-k: wave w owns tokens w and w+16 of the workgroup and works on
+  // the two together. Lane l holds experts l*PL .. l*PL+PL-1,
+  // sorted by (score desc, id asc); a lower lane always holds lower ids, so
+  // among lanes whose best ties with the wave max the lowest lane holds the
+  // lowest expert id.
+  constexpr int kTokPerWave = kTokPerBlock / (kSelThreads / kWave);  // 2
+  uint32_t ku[kTokPerWave][PL];
+  int ke[kTokPerWave][PL];
+  bool live[kTokPerWave];
+  // loads first, all of them, from clamped (always valid) addresses; the
+  // keys of dead tokens and of experts >= E are masked to 0 afterwards
+  float sv[kTokPerWave][PL];
+#pragma unroll
+  for (int q = 0; q < kTokPerWave; ++q) {
+    const int t = t0 + wave + q * nwaves;
+    live[q] = t < vtc;  // wave-uniform
+    const float* srow = scores + static_cast<int64_t>(live[q] ? t : 0) * st;
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
-      const int e = j * kWave + lane;
-      key[j] = (e < E) ? topk_key(srow[static_cast<int64_t>(e) * se], e) : 0ull;
-    }
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int j = 1; j < PL; ++j) best = key[j] > best ? key[j] : best;
-      const uint64_t win = wave_max_u64(best);
-#pragma unroll
-      for (int j = 0; j < PL; ++j)
-        if (key[j] == win) key[j] = 0ull;  // keys are unique: one owner
-      if (lane == 0)
-        sel[tl * K + k] = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(win));
+      const int e = min(lane * PL + j, E - 1);
+      sv[q][j] = srow[static_cast<int64_t>(e) * se];
     }
   }
+#pragma unroll
+  for (int q = 0; q < kTokPerWave; ++q) {
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int e = lane * PL + j;
+      ke[q][j] = e;
+      ku[q][j] = (live[q] && e < E) ? score_key(sv[q][j]) : 0u;
+    }
+    // stable insertion sort, descending key (ties keep ascending id)
+#pragma unroll
+    for (int i = 1; i < PL; ++i) {
+#pragma unroll
+      for (int j = i; j > 0; --j) {
+        const bool sw = ku[q][j] > ku[q][j - 1];
+        const uint32_t a = ku[q][j], b = ku[q][j - 1];
+        const int ea = ke[q][j], eb = ke[q][j - 1];
+        ku[q][j - 1] = sw ? a : b;
+        ku[q][j] = sw ? b : a;
+        ke[q][j - 1] = sw ? ea : eb;
+        ke[q][j] = sw ? eb : ea;
+      }
+    }
+  }
+  int mine[kTokPerWave];  // lane k keeps slot k's expert
+  for (int k = 0; k < K; ++k) {
+    uint32_t head[kTokPerWave], m[kTokPerWave];
+#pragma unroll
+    for (int q = 0; q < kTokPerWave; ++q) head[q] = ku[q][0];
+    wave_max_keys<kTokPerWave>(head, m);
+#pragma unroll
+    for (int q = 0; q < kTokPerWave; ++q) {
+      const uint64_t tied = __ballot(ku[q][0] == m[q]);
+      const int w = __builtin_ctzll(tied);  // lowest lane among the ties
+      const int e_win = __builtin_amdgcn_readlane(ke[q][0], w);
+      const bool pop = lane == w;
+#pragma unroll
+      for (int j = 0; j + 1 < PL; ++j) {
+        ku[q][j] = pop ? ku[q][j + 1] : ku[q][j];
+        ke[q][j] = pop ? ke[q][j + 1] : ke[q][j];
+      }
+      if (pop) ku[q][PL - 1] = 0u;
+      mine[q] = lane == k ? e_win : mine[q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kTokPerWave; ++q)
+    if (live[q] && lane < K) sel[(wave + q * nwaves) * K + lane] = mine[q];
   __syncthreads();
 
   // ---- one bit per valid token in each of its experts' masks
   const int npairs = kTokPerBlock * K;
   for (int p = threadIdx.x; p < npairs; p += kSelThreads) {
     const int tl = p / K;
-    if (t0 + tl < vtc) atomicOr(&mask[sel[p]], 1ull << tl);
+    if (t0 + tl < vtc) atomicOr(&mask[sel[p]], 1u << tl);
   }
   __syncthreads();
 
@@ -103,69 +187,108 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
     const int t = t0 + tl;
     if (t < vtc) {
       const int e = sel[p];
-      const unsigned long long before = mask[e] & ((1ull << tl) - 1ull);
-      pair[static_cast<int64_t>(t0) * K + p] = e | (__popcll(before) << 16);
+      const uint32_t before = mask[e] & ((1u << tl) - 1u);
+      pair[static_cast<int64_t>(t0) * K + p] = e | (__popc(before) << 16);
     }
   }
   for (int e = threadIdx.x; e < E; e += kSelThreads)
-    hist[static_cast<int64_t>(e) * nblk + blk] = __popcll(mask[e]);
+    hist[static_cast<int64_t>(e) * nblk + blk] = __popc(mask[e]);
 }
 
-// Exclusive scan of hist[E*nblk] (expert-major) in place; counts[e] is the
-// row length of expert e, counts[E] the total.
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(int* __restrict__ hist, int E,
-                                                            int nblk,
-                                                            int* __restrict__ counts) {
-  __shared__ int part[kScanThreads];
-  __shared__ int row_start[kMaxE + 1];
-  const int n = E * nblk;
+// One wave per expert: exclusive scan of hist[e][0..nblk) in place (offsets
+// of each block's pairs inside the expert's rows) and counts[e] = its total.
+// Tiles of 256 blocks: lane l loads blocks 4l..4l+3 of the tile at once,
+// scans them locally, and a wave scan of the lane sums adds the rest.
+constexpr int kScanWaves = 4;
+constexpr int kScanPer = 4;
+__global__ __launch_bounds__(kScanWaves* kWave) void expert_scan_kernel(
+    int* __restrict__ hist, int E, int nblk, int* __restrict__ counts) {
+  const int lane = lane_id();
+  const int e = blockIdx.x * kScanWaves + uniform(threadIdx.x >> 6);
+  if (e >= E) return;
+  int* row = hist + static_cast<int64_t>(e) * nblk;
+  int carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += kWave * kScanPer) {
+    int v[kScanPer];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int b = b0 + lane * kScanPer + i;
+      v[i] = b < nblk ? row[b] : 0;
+      mine += v[i];
+    }
+    int incl = mine;  // inclusive wave scan of the lane sums
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    int run = carry + incl - mine;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int b = b0 + lane * kScanPer + i;
+      if (b < nblk) row[b] = run;
+      run += v[i];
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  if (lane == 0) counts[e] = carry;
+}
+
+constexpr int kPlaceThreads = 256;
+__global__ __launch_bounds__(kPlaceThreads) void place_kernel(
+    const int* __restrict__ pair, const int* __restrict__ offs, int nblk, int T, int E, int K,
+    const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
+    int* __restrict__ ei, int* __restrict__ rop) {
+  __shared__ int first[kMaxE];
+  __shared__ int wave_tot[kPlaceThreads / kWave];
   const int tid = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int beg = min(tid * per, n);
-  const int end = min(beg + per, n);
-  for (int e = tid; e <= E; e += kScanThreads) row_start[e] = 0;
-
-  int s = 0;
-  for (int i = beg; i < end; ++i) s += hist[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = part[tid] - s;  // exclusive prefix
-  for (int i = beg; i < end; ++i) {
-    const int c = hist[i];
-    if (i % nblk == 0) row_start[i / nblk] = run;  // nblk > 0 here
-    hist[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  if (tid == kScanThreads - 1) row_start[E] = part[tid];
-  __syncthreads();
-  for (int e = tid; e < E; e += kScanThreads) counts[e] = row_start[e + 1] - row_start[e];
-  if (tid == 0) counts[E] = row_start[E];
-}
-
-__global__ __launch_bounds__(256) void place_kernel(const int* __restrict__ pair,
-                                                    const int* __restrict__ offs, int nblk,
-                                                    int T, int K,
-                                                    const int* __restrict__ vtc_ptr,
-                                                    int* __restrict__ ti, int* __restrict__ ei,
-                                                    int* __restrict__ rop) {
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  // this thread's pair, loaded before the counts scan so the two overlap
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kPlaceThreads + tid;
   const int64_t npairs = static_cast<int64_t>(T) * K;
-  if (p >= npairs) return;
-  const int t = static_cast<int>(p / K);
+  const bool have = p < npairs;
+  const int t = have ? static_cast<int>(p / K) : 0;
   const int vtc = clamp_count(vtc_ptr, T);
+  const int v = (have && t < vtc) ? pair[p] : 0;
+  const int e = v & 0xFFFF;
+  const int rank = v >> 16;
+  const int off = (have && t < vtc) ? offs[static_cast<int64_t>(e) * nblk + t / kTokPerBlock] : 0;
+
+  // first[e] = sum of counts[e'] for e' < e: each thread scans E/256 counts,
+  // then waves and workgroup combine (E <= 1024 -> at most 4 per thread)
+  constexpr int kPer = kMaxE / kPlaceThreads;
+  int c[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ee = tid * kPer + i;
+    c[i] = ee < E ? counts[ee] : 0;
+    mine += c[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = incl - mine;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int ee = tid * kPer + i;
+    if (ee < E) first[ee] = base;
+    base += c[i];
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) counts[E] = vtc * K;
+
+  if (!have) return;
   if (t < vtc) {
-    const int v = pair[p];
-    const int e = v & 0xFFFF;
-    const int rank = v >> 16;
-    const int r = offs[static_cast<int64_t>(e) * nblk + t / kTokPerBlock] + rank;
+    const int r = first[e] + off + rank;
     ti[r] = t;
     ei[r] = e;
     if (rop) rop[p] = r;
@@ -174,6 +297,12 @@ __global__ __launch_bounds__(256) void place_kernel(const int* __restrict__ pair
     ei[p] = -1;
     if (rop) rop[p] = -1;
   }
+}
+
+// counts[0..E] = 0 (no pairs at all)
+__global__ void zero_counts_kernel(int* __restrict__ counts, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) counts[i] = 0;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
@@ -190,16 +319,15 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
                           int K, const int* vtc, int* counts, int* expert_indices,
                           int* token_indices, int* row_of_pair, void* workspace,
                           hipStream_t stream) {
+  if (T == 0) {
+    hipLaunchKernelGGL(zero_counts_kernel, dim3((E + 1 + 255) / 256), dim3(256), 0, stream,
+                       counts, E + 1);
+    return hipGetLastError();
+  }
   const int nblk = (T + kTokPerBlock - 1) / kTokPerBlock;
   char* ws = static_cast<char*>(workspace);
   int* pair = reinterpret_cast<int*>(ws);
   int* hist = reinterpret_cast<int*>(ws + align256(static_cast<size_t>(T) * K * sizeof(int)));
-  if (T == 0) {
-    // no pairs: every count is zero
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist, E, 0,
-                       counts);
-    return hipGetLastError();
-  }
   const int pl = (E + kWave - 1) / kWave;
   const dim3 g1(nblk), b1(kSelThreads);
 #define MOE_SEL(PLV)                                                                     \
@@ -211,12 +339,12 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
   else if (pl <= 8) MOE_SEL(8);
   else MOE_SEL(16);
 #undef MOE_SEL
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist, E, nblk,
-                     counts);
+  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
+                     dim3(kScanWaves * kWave), 0, stream, hist, E, nblk, counts);
   const int64_t npairs = static_cast<int64_t>(T) * K;
-  const int pblocks = static_cast<int>((npairs + 255) / 256);
-  hipLaunchKernelGGL(place_kernel, dim3(pblocks), dim3(256), 0, stream, pair, hist, nblk, T,
-                     K, vtc, token_indices, expert_indices, row_of_pair);
+  const int pblocks = static_cast<int>((npairs + kPlaceThreads - 1) / kPlaceThreads);
+  hipLaunchKernelGGL(place_kernel, dim3(pblocks), dim3(kPlaceThreads), 0, stream, pair, hist,
+                     nblk, T, E, K, vtc, counts, token_indices, expert_indices, row_of_pair);
   return hipGetLastError();
 }
 

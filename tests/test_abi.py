@@ -72,8 +72,8 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # shuffle: T*K pair words + E*ceil(T/64) histogram words, 256-aligned
-    assert lib.moe_shuffle_workspace_bytes(8192, 256, 8) == 8192 * 8 * 4 + 256 * 128 * 4
+    # shuffle: T*K pair words + E*ceil(T/32) histogram words, 256-aligned
+    assert lib.moe_shuffle_workspace_bytes(8192, 256, 8) == 8192 * 8 * 4 + 256 * 256 * 4
     assert lib.moe_shuffle_workspace_bytes(65, 3, 2) == 768 + 256
     assert lib.moe_shuffle_workspace_bytes(-1, 3, 2) == 0
     # scatter: (T+1) counters + a slots + a list entries
