@@ -29,7 +29,7 @@ namespace moe {
 namespace {
 
 constexpr int kRowWaves = 4;
-constexpr int kGroup = 4;  // expert rows whose loads are in flight together
+constexpr int kGroup = 4;  // rows in flight together in the general combine
 constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ int clamp_count(const int* p, int hi) {
@@ -53,40 +53,56 @@ __device__ __forceinline__ int wave_sort_asc(int v, int lane) {
   return v;
 }
 
+// Loads group [i0, i0+G) of the n rows listed in ascending order in lanes
+// 0..n-1 of sorted_rows. Every load is unconditional: positions past n re-read
+// row n-1 (an L2 hit), so the G*CPL loads issue back to back with no branch
+// or wait between them.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void load_rows(u32x4 (&buf)[G][CPL], const uint16_t* __restrict__ in,
+                                          int D, int nch, int base, int sorted_rows, int i0,
+                                          int n) {
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int r = __builtin_amdgcn_readlane(sorted_rows, min(i0 + q, n - 1));
+    const uint16_t* src = in + static_cast<int64_t>(r) * D;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = base + j * kWave;
+      if (FULL || c < nch) buf[q][j] = ld16_stream(src + c * kChunk);
+    }
+  }
+}
+
+// acc += the group's rows that exist (positions i0+q < n), in order.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void add_group(float (&acc)[CPL][8], const u32x4 (&buf)[G][CPL],
+                                          int nch, int base, int i0, int n) {
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    if (i0 + q < n) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = base + j * kWave;
+        if (FULL || c < nch) {
+          float f[8];
+          unpack8(buf[q][j], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
+        }
+      }
+    }
+  }
+}
+
 // acc[j] (this lane's CPL chunks of the slice) += the n rows listed in
 // ascending order in lanes 0..n-1 of `sorted_rows`.
-template <int CPL, bool FULL>
+template <int CPL, int G, bool FULL>
 __device__ __forceinline__ void add_rows(float (&acc)[CPL][8], const uint16_t* __restrict__ in,
                                          int D, int nch, int base, int sorted_rows, int n) {
-  for (int i0 = 0; i0 < n; i0 += kGroup) {
-    u32x4 buf[kGroup][CPL];
-#pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      if (i0 + q < n) {
-        const int r = __builtin_amdgcn_readlane(sorted_rows, i0 + q);
-        const uint16_t* src = in + static_cast<int64_t>(r) * D;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = base + j * kWave;
-          if (FULL || c < nch) buf[q][j] = ld16_stream(src + c * kChunk);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kGroup; ++q) {
-      if (i0 + q < n) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = base + j * kWave;
-          if (FULL || c < nch) {
-            float f[8];
-            unpack8(buf[q][j], f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
-          }
-        }
-      }
-    }
+  for (int i0 = 0; i0 < n; i0 += G) {
+    u32x4 buf[G][CPL];
+    load_rows<CPL, G, FULL>(buf, in, D, nch, base, sorted_rows, i0, n);
+    add_group<CPL, G, FULL>(acc, buf, nch, base, i0, n);
   }
 }
 
@@ -118,19 +134,33 @@ __device__ __forceinline__ void store_acc(const float (&acc)[CPL][8], uint16_t* 
   }
 }
 
-// The whole per-token reduction of one slice: initial row, n expert rows in
-// the ascending order held in lanes 0..n-1 of sorted_rows, one store.
-template <int CPL, bool FULL>
+// The whole per-token reduction of one slice: the initial row and the first
+// G expert rows are loaded together, then added in order; later groups
+// follow; one store. n >= 1.
+template <int CPL, int G, bool FULL>
 __device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
                                              const uint16_t* __restrict__ in, int D, int nch,
                                              int base, int sorted_rows, int n) {
+  u32x4 o0[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    o0[j] = (FULL || c < nch) ? ld16(orow + c * kChunk) : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x4 buf[G][CPL];
+  load_rows<CPL, G, FULL>(buf, in, D, nch, base, sorted_rows, 0, n);
   float acc[CPL][8];
-  load_acc<CPL, FULL>(acc, orow, nch, base);
-  add_rows<CPL, FULL>(acc, in, D, nch, base, sorted_rows, n);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) unpack8(o0[j], acc[j]);
+  add_group<CPL, G, FULL>(acc, buf, nch, base, 0, n);
+  for (int i0 = G; i0 < n; i0 += G) {
+    load_rows<CPL, G, FULL>(buf, in, D, nch, base, sorted_rows, i0, n);
+    add_group<CPL, G, FULL>(acc, buf, nch, base, i0, n);
+  }
   store_acc<CPL, FULL>(acc, orow, nch, base);
 }
 
-template <int CPL>
+template <int CPL, int G>
 __global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
     uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
     const int* __restrict__ rop, int K, int a, int D, const int* __restrict__ vrows,
@@ -152,9 +182,9 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
   const int slice0 = sl * kWave * CPL;
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (slice0 + kWave * CPL <= nch)
-    reduce_slice<CPL, true>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+    reduce_slice<CPL, G, true>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
   else
-    reduce_slice<CPL, false>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+    reduce_slice<CPL, G, false>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
 }
 
 // ---------------------------------------------------------------- general
@@ -265,9 +295,9 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
     const int r = lane < n ? list[beg + lane] : INT_MAX;
     const int sorted_rows = wave_sort_asc(r, lane);
     if (slice0 + kWave * CPL <= nch)
-      reduce_slice<CPL, true>(orow, in, D, nch, base, sorted_rows, n);
+      reduce_slice<CPL, kGroup, true>(orow, in, D, nch, base, sorted_rows, n);
     else
-      reduce_slice<CPL, false>(orow, in, D, nch, base, sorted_rows, n);
+      reduce_slice<CPL, kGroup, false>(orow, in, D, nch, base, sorted_rows, n);
   } else {
     float acc[CPL][8];
     load_acc<CPL, false>(acc, orow, nch, base);
@@ -283,7 +313,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off, kWave));
       prev = m;
-      add_rows<CPL, false>(acc, in, D, nch, base, m, 1);
+      add_rows<CPL, 1, false>(acc, in, D, nch, base, m, 1);
     }
     store_acc<CPL, false>(acc, orow, nch, base);
   }
@@ -307,15 +337,33 @@ size_t scatter_add_workspace_bytes(int T, int a) {
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream) {
-  const SliceShape sh = combine_shape(D / kChunk);
+  // G rows in flight: the next power of two >= K, at most 8, with G * cpl <= 16
+  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 ? 4 : 8));
+  static const int allowed8[] = {2, 1};
+  static const int allowed4[] = {2, 4, 3, 1};
+  const SliceShape sh = G >= 8 ? pick_slices(D / kChunk, allowed8, 2, 1 << 20)
+                               : pick_slices(D / kChunk, allowed4, 4, 1 << 20);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);
-#define L(C)                                                                            \
-  hipLaunchKernelGGL(scatter_tokens_kernel<C>, grid, block, 0, stream, out, T, in,        \
+#define L2(C, GV)                                                                          \
+  hipLaunchKernelGGL((scatter_tokens_kernel<C, GV>), grid, block, 0, stream, out, T, in,  \
                      row_of_pair, K, a, D, valid_rows, sh.nsl)
-  MOE_DISPATCH_CPL(sh.cpl, L)
-#undef L
+#define LG(C)                         \
+  do {                                \
+    if (G == 1) L2(C, 1);             \
+    else if (G == 2) L2(C, 2);        \
+    else if (G == 4) L2(C, 4);        \
+    else L2(C, ((C) <= 2 ? 8 : 4));   \
+  } while (0)
+  switch (sh.cpl) {
+    case 1: LG(1); break;
+    case 2: LG(2); break;
+    case 3: LG(3); break;
+    default: LG(4); break;
+  }
+#undef LG
+#undef L2
   return hipGetLastError();
 }
 
@@ -342,7 +390,12 @@ hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const in
 #define L(C)                                                                            \
   hipLaunchKernelGGL(scatter_csr_kernel<C>, grid, block, 0, stream, out, T, in, cnt, list, \
                      D, sh.nsl)
-  MOE_DISPATCH_CPL(sh.cpl, L)
+  switch (sh.cpl) {
+    case 1: L(1); break;
+    case 2: L(2); break;
+    case 3: L(3); break;
+    default: L(4); break;
+  }
 #undef L
   return hipGetLastError();
 }

@@ -49,16 +49,65 @@ __device__ __forceinline__ uint32_t ue8m0_of(float amax) {
   return static_cast<uint32_t>(byte);
 }
 
+// Loads the expert rows of slots [k0, k0+G). Every load is unconditional:
+// a slot that is not held (or past K) re-reads `safe`, a held row of the same
+// token (an L2 hit), so all G*CPL loads issue back to back.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void load_slots(u32x4 (&buf)[G][CPL], const uint16_t* __restrict__ y,
+                                           int D, int nch, int base, int my_r, int K, int k0,
+                                           int safe) {
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int k = k0 + q;
+    const int r = __builtin_amdgcn_readlane(my_r, min(k, kWave - 1));
+    const int rr = (k < K && r >= 0) ? r : safe;
+    const uint16_t* src = y + static_cast<int64_t>(rr) * D;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = base + j * kWave;
+      if (FULL || c < nch) buf[q][j] = ld16_stream(src + c * kChunk);
+    }
+  }
+}
+
+// acc = fma(w_k, row_k, acc) over the held slots of the group, in slot order
+// (the select keeps acc unchanged for a slot that is not held).
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void fma_slots(float (&acc)[CPL][8], const u32x4 (&buf)[G][CPL],
+                                          int nch, int base, int my_r, float my_w, int K,
+                                          int k0) {
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const int k = k0 + q;
+    const int kq = min(k, kWave - 1);
+    const bool held = k < K && __builtin_amdgcn_readlane(my_r, kq) >= 0;
+    const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), kq));
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = base + j * kWave;
+      if (FULL || c < nch) {
+        float f[8];
+        unpack8(buf[q][j], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float v = __builtin_fmaf(wq, f[i], acc[j][i]);
+          acc[j][i] = held ? v : acc[j][i];
+        }
+      }
+    }
+  }
+}
+
 // FULL: every wave's slice lies inside the row (D == waves * 64 * CPL * 8),
 // so no chunk needs a bounds test and loads/stores are straight-line code.
-template <int CPL, bool MX, bool FULL>
+// G: expert rows in flight per group (>= K where possible: one group).
+template <int CPL, int G, bool MX, bool FULL>
 __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
     const uint16_t* __restrict__ y, int64_t rows, const float* __restrict__ w,
     const int* __restrict__ rop, const uint16_t* __restrict__ shared,
     const uint16_t* __restrict__ gamma, float eps, int K, int D, uint32_t flags,
     uint16_t* __restrict__ out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   __shared__ float wave_ss[kMaxWaves];
-  constexpr int G = CPL >= 8 ? 2 : (CPL >= 4 ? 4 : 8);  // rows in flight per group
 
   const int t = blockIdx.x;
   const int lane = lane_id();
@@ -93,37 +142,15 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
     }
   }
 
-  for (int k0 = 0; k0 < K; k0 += G) {
+  const uint64_t held = __ballot(lane < K && my_r >= 0);
+  if (held != 0) {
+    const int safe = __builtin_amdgcn_readlane(my_r, __builtin_ctzll(held));
     u32x4 buf[G][CPL];
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int r = __builtin_amdgcn_readlane(my_r, min(k0 + q, kWave - 1));
-      if (k0 + q < K && r >= 0) {
-        const uint16_t* src = y + static_cast<int64_t>(r) * D;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = base + j * kWave;
-          if (FULL || c < nch) buf[q][j] = ld16_stream(src + c * kChunk);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < G; ++q) {
-      const int r = __builtin_amdgcn_readlane(my_r, min(k0 + q, kWave - 1));
-      if (k0 + q < K && r >= 0) {
-        const float wq = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(my_w), k0 + q));
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int c = base + j * kWave;
-          if (FULL || c < nch) {
-            float f[8];
-            unpack8(buf[q][j], f);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][i] = __builtin_fmaf(wq, f[i], acc[j][i]);
-          }
-        }
-      }
+    load_slots<CPL, G, FULL>(buf, y, D, nch, base, my_r, K, 0, safe);
+    fma_slots<CPL, G, FULL>(acc, buf, nch, base, my_r, my_w, K, 0);
+    for (int k0 = G; k0 < K; k0 += G) {
+      load_slots<CPL, G, FULL>(buf, y, D, nch, base, my_r, K, k0, safe);
+      fma_slots<CPL, G, FULL>(acc, buf, nch, base, my_r, my_w, K, k0);
     }
   }
 
@@ -244,15 +271,27 @@ hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float*
   const dim3 block(sh.nsl * kWave);
   const bool mx = mx_codes != nullptr;
   const bool full = sh.nsl * kWave * sh.cpl == nch;
-#define L3(C, M, F)                                                                          \
-  hipLaunchKernelGGL((finalize_kernel<C, M, F>), grid, block, 0, stream, y, rows, w,          \
+  // rows in flight per group: the next power of two >= K (at most 8), with
+  // G * cpl <= 16 to bound the registers
+  const int gk = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 ? 4 : 8));
+#define L4(C, GV, M, F)                                                                      \
+  hipLaunchKernelGGL((finalize_kernel<C, GV, M, F>), grid, block, 0, stream, y, rows, w,      \
                      row_of_pair, shared, gamma, eps, K, D, flags, out, mx_codes, mx_scales)
-#define L(C)                   \
-  do {                         \
-    if (mx && full) L3(C, true, true);       \
-    else if (mx) L3(C, true, false);         \
-    else if (full) L3(C, false, true);       \
-    else L3(C, false, false);                \
+#define L3(C, GV)                        \
+  do {                                   \
+    if (mx && full) L4(C, GV, true, true);       \
+    else if (mx) L4(C, GV, true, false);         \
+    else if (full) L4(C, GV, false, true);       \
+    else L4(C, GV, false, false);                \
+  } while (0)
+#define L(C)                                                  \
+  do {                                                        \
+    constexpr int gmax = 16 / (C) < 8 ? 16 / (C) : 8;         \
+    const int g = gk < gmax ? gk : gmax;                      \
+    if (g == 1) L3(C, 1);                                     \
+    else if (g == 2) L3(C, (gmax >= 2 ? 2 : 1));              \
+    else if (g == 4) L3(C, (gmax >= 4 ? 4 : 1));              \
+    else L3(C, (gmax >= 8 ? 8 : 1));                          \
   } while (0)
   switch (sh.cpl) {
     case 1: L(1); break;
@@ -262,6 +301,7 @@ hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float*
   }
 #undef L
 #undef L3
+#undef L4
   return hipGetLastError();
 }
 
