@@ -36,6 +36,14 @@ SIGNATURES = {
     "moe_scatter_add_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_scatter_add": (_status, [_p, _i32, _p, _p, _i32, _i32, _p, _p, _sz, _p]),
     "moe_scatter_add_by_token": (_status, [_p, _i32, _p, _p, _i32, _i32, _i32, _p, _p]),
+    "moe_scatter_add_padded_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_scatter_add_padded": (_status, [_p, _i32, _i32, _p, _i32, _p, _p, _i32, _i32, _p, _sz,
+                                         _p]),
+    "moe_shuffling_workspace_bytes": (_sz, [_i32, _i32, _i64]),
+    "moe_combine_shuffling": (_status, [_p, _i64, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32,
+                                        _i64, _p, _p, _sz, _p]),
+    "moe_split_shuffling": (_status, [_p, _i64, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32,
+                                      _i64, _p, _p, _sz, _p]),
     "moe_finalize_rmsnorm": (_status, [_p, _i64, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _u32,
                                        _p, _p, _p, _p]),
     "moe_convert_check": (_status, [_p, _i64, _p, _p, _p]),

@@ -234,6 +234,97 @@ moe_status_t moe_scatter_add_by_token(moe_bf16_t* out_tokens, int32_t T,
                     "moe_scatter_add_by_token");
 }
 
+size_t moe_scatter_add_padded_workspace_bytes(int32_t T, int32_t T_K, int32_t E) {
+  if (T < 0 || T_K < 0 || E < 1) return 0;
+  return moe::scatter_add_padded_workspace_bytes(T, T_K, E);
+}
+
+moe_status_t moe_scatter_add_padded(const moe_bf16_t* in_tokens, int32_t EP, int32_t T_K,
+                                    const int32_t* token_counts, int32_t E,
+                                    const int32_t* token_indices, moe_bf16_t* out_tokens,
+                                    int32_t T, int32_t D, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  REQUIRE(EP >= 1 && E >= 1 && T_K >= 0 && T >= 0, MOE_ERR_INVALID_ARG,
+          "EP, E >= 1 and T_K, T >= 0 required (EP=%d E=%d T_K=%d T=%d)", EP, E, T_K, T);
+  REQUIRE(E % EP == 0, MOE_ERR_INVALID_ARG, "E must be a multiple of EP (E=%d, EP=%d)", E, EP);
+  REQUIRE(E <= kMaxE, MOE_ERR_UNSUPPORTED, "E > %d is not supported (got %d)", kMaxE, E);
+  REQUIRE(static_cast<int64_t>(EP) * T_K < (int64_t{1} << 31), MOE_ERR_INVALID_ARG,
+          "EP*T_K must be < 2^31");
+  moe_status_t s = check_scatter(out_tokens, T, in_tokens, T_K, D);
+  if (s != MOE_OK) return s;
+  if (T_K == 0 || D == 0 || T == 0) return ok();
+  REQUIRE(token_counts && token_indices, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  const size_t need = moe::scatter_add_padded_workspace_bytes(T, T_K, E);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "scatter_add_padded workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(moe::launch_scatter_add_padded(in_tokens, EP, T_K, token_counts, E,
+                                                   token_indices, out_tokens, T, D, workspace,
+                                                   static_cast<hipStream_t>(stream)),
+                    "moe_scatter_add_padded");
+}
+
+size_t moe_shuffling_workspace_bytes(int32_t EP, int32_t n_local, int64_t em_rows) {
+  if (EP < 1 || n_local < 0 || em_rows < 0) return 0;
+  return moe::shuffling_workspace_bytes(EP * n_local, em_rows);
+}
+
+static moe_status_t shuffling(bool inverse, const moe_bf16_t* in, int64_t in_rows,
+                              moe_bf16_t* out, int64_t out_rows, int32_t D,
+                              const int32_t* counts, int32_t EP, int32_t C, int32_t c_lo,
+                              int32_t c_hi, int64_t rank_stride, int32_t* out_counts,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = inverse ? "moe_split_shuffling" : "moe_combine_shuffling";
+  REQUIRE(EP >= 1 && EP <= moe::kMaxShufflingRanks, MOE_ERR_UNSUPPORTED,
+          "%s: EP must be in [1, %d] (got %d)", what, moe::kMaxShufflingRanks, EP);
+  REQUIRE(C >= 1 && c_lo >= 0 && c_lo <= c_hi && c_hi <= C, MOE_ERR_INVALID_ARG,
+          "%s: need 0 <= c_lo <= c_hi <= C, C >= 1 (C=%d c_lo=%d c_hi=%d)", what, C, c_lo, c_hi);
+  REQUIRE(static_cast<int64_t>(c_hi - c_lo) * EP <= moe::kMaxShufflingSegments,
+          MOE_ERR_UNSUPPORTED, "%s: (c_hi - c_lo) * EP > %d", what,
+          moe::kMaxShufflingSegments);
+  REQUIRE(in_rows >= 0 && out_rows >= 0 && in_rows < (int64_t{1} << 31) &&
+              out_rows < (int64_t{1} << 31),
+          MOE_ERR_INVALID_ARG, "%s: row counts must be in [0, 2^31)", what);
+  REQUIRE(rank_stride < 0 || static_cast<int64_t>(EP) * rank_stride < (int64_t{1} << 31),
+          MOE_ERR_INVALID_ARG, "%s: EP * rank_stride must be < 2^31", what);
+  moe_status_t s = check_rows(D, 8);
+  if (s != MOE_OK) return s;
+  REQUIRE(counts != nullptr, MOE_ERR_INVALID_ARG, "%s: counts is NULL", what);
+  REQUIRE(inverse || out_counts != nullptr, MOE_ERR_INVALID_ARG, "%s: out_counts is NULL",
+          what);
+  REQUIRE((in_rows == 0 || in) && (out_rows == 0 || out), MOE_ERR_INVALID_ARG,
+          "%s: row buffer is NULL", what);
+  REQUIRE(aligned(in, 16) && aligned(out, 16), MOE_ERR_INVALID_ARG,
+          "%s: row buffers must be 16-byte aligned", what);
+  const int64_t em_rows = inverse ? in_rows : out_rows;
+  const size_t need = moe::shuffling_workspace_bytes((c_hi - c_lo) * EP, em_rows);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
+          "%s workspace needs %zu bytes (got %zu)", what, need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return hip_status(moe::launch_shuffling(inverse, in, in_rows, out, out_rows, D, counts, EP, C,
+                                          c_lo, c_hi, rank_stride, out_counts, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                    what);
+}
+
+moe_status_t moe_combine_shuffling(const moe_bf16_t* in, int64_t in_rows, moe_bf16_t* out,
+                                   int64_t out_rows, int32_t D, const int32_t* counts,
+                                   int32_t EP, int32_t C, int32_t c_lo, int32_t c_hi,
+                                   int64_t rank_stride, int32_t* out_counts, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return shuffling(false, in, in_rows, out, out_rows, D, counts, EP, C, c_lo, c_hi,
+                   rank_stride, out_counts, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_split_shuffling(const moe_bf16_t* in, int64_t in_rows, moe_bf16_t* out,
+                                 int64_t out_rows, int32_t D, const int32_t* counts, int32_t EP,
+                                 int32_t C, int32_t c_lo, int32_t c_hi, int64_t rank_stride,
+                                 int32_t* out_counts, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return shuffling(true, in, in_rows, out, out_rows, D, counts, EP, C, c_lo, c_hi,
+                   rank_stride, out_counts, workspace, workspace_bytes, stream);
+}
+
 moe_status_t moe_finalize_rmsnorm(const moe_bf16_t* y_permuted, int64_t rows,
                                   const float* expert_weights, const int32_t* row_of_pair,
                                   const moe_bf16_t* shared, const moe_bf16_t* gamma, float eps,

@@ -19,6 +19,9 @@
 //            first (count with atomics on per-token counters, exclusive scan,
 //            fill); the order inside a token's list then depends on the
 //            atomics, so the reduce kernel sorts each list before adding.
+//  padded    the general path over the static-shape expert-parallel layout
+//            [EP, T_K, D]: each row is read from the slab of the rank that
+//            owns its expert.
 #include <limits.h>
 
 #include "device.hpp"
@@ -319,6 +322,99 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
   }
 }
 
+// ---------------------------------------------------------------- padded
+// [GS] scatter_add_padded_tokens: rows [off_e, off_e + counts[e]) of the
+// shuffle's order belong to expert e and are read from rank e / (E / EP)'s
+// slab of in [EP, T_K, D] at the same row positions.
+constexpr int kMaxPaddedE = 1024;
+
+// prefix[e] = sum of counts[e'] for e' < e (e <= E); prefix[E] is clamped to
+// T_K and is the valid row count V of the CSR build. One workgroup.
+__global__ __launch_bounds__(kScanThreads) void padded_prefix_kernel(
+    const int* __restrict__ counts, int E, int T_K, int* __restrict__ prefix) {
+  __shared__ int wave_tot[kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int v = tid < E ? max(counts[tid], 0) : 0;  // E <= kScanThreads
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    if (w < wave) base += wave_tot[w];
+    total += wave_tot[w];
+  }
+  if (tid < E) prefix[tid] = min(base + incl - v, T_K);
+  if (tid == 0) prefix[E] = min(total, T_K);
+}
+
+// Rank owning row r: the expert e with prefix[e] <= r < prefix[e+1], over E/EP.
+__device__ __forceinline__ int rank_of_row(const int* __restrict__ pre, int E, int epr, int r) {
+  int lo = 0, hi = E;  // invariant: pre[lo] <= r < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo / epr;
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in, int T_K, int E, int EP,
+    const int* __restrict__ prefix, const int* __restrict__ start, const int* __restrict__ list,
+    int D, int nsl) {
+  __shared__ int pre[kMaxPaddedE + 1];
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) pre[e] = prefix[e];
+  __syncthreads();
+  const int lane = lane_id();
+  const int64_t unit =
+      static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int beg = start[t];
+  const int n = start[t + 1] - beg;
+  if (n == 0) return;
+  const int epr = E / EP;
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  const int base = slice0 + lane;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  if (n <= kWave) {
+    const int r = lane < n ? list[beg + lane] : INT_MAX;
+    const int sorted = wave_sort_asc(r, lane);
+    // source row of each sorted row: rank * T_K + row (ascending row order kept)
+    const int src = lane < n ? rank_of_row(pre, E, epr, sorted) * T_K + sorted : 0;
+    if (slice0 + kWave * CPL <= nch)
+      reduce_slice<CPL, kGroup, true>(orow, in, D, nch, base, src, n);
+    else
+      reduce_slice<CPL, kGroup, false>(orow, in, D, nch, base, src, n);
+  } else {
+    float acc[CPL][8];
+    load_acc<CPL, false>(acc, orow, nch, base);
+    int prev = -1;
+    for (int i = 0; i < n; ++i) {
+      int m = INT_MAX;
+      for (int q = lane; q < n; q += kWave) {
+        const int r = list[beg + q];
+        if (r > prev && r < m) m = r;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = min(m, __shfl_xor(m, off, kWave));
+      prev = m;
+      add_rows<CPL, 1, false>(acc, in, D, nch, base, rank_of_row(pre, E, epr, m) * T_K + m, 1);
+    }
+    store_acc<CPL, false>(acc, orow, nch, base);
+  }
+}
+
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 SliceShape combine_shape(int nch) {
@@ -332,6 +428,48 @@ SliceShape combine_shape(int nch) {
 size_t scatter_add_workspace_bytes(int T, int a) {
   return align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
          2 * align256(static_cast<size_t>(a) * sizeof(int));
+}
+
+size_t scatter_add_padded_workspace_bytes(int T, int T_K, int E) {
+  return align256((static_cast<size_t>(E) + 1) * sizeof(int)) +
+         scatter_add_workspace_bytes(T, T_K);
+}
+
+hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const int* counts,
+                                     int E, const int* ti, uint16_t* out, int T, int D,
+                                     void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  int* prefix = reinterpret_cast<int*>(ws);
+  ws += align256((static_cast<size_t>(E) + 1) * sizeof(int));
+  int* cnt = reinterpret_cast<int*>(ws);
+  int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
+  int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
+                                     align256(static_cast<size_t>(T_K) * sizeof(int)));
+  hipLaunchKernelGGL(padded_prefix_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, E,
+                     T_K, prefix);
+  hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
+                     T + 1);
+  const dim3 rgrid((T_K + 255) / 256);
+  hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E,
+                     cnt, slot);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
+  hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E, cnt,
+                     slot, list);
+  const SliceShape sh = combine_shape(D / kChunk);
+  const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
+  const dim3 block(kRowWaves * kWave);
+#define L(C)                                                                             \
+  hipLaunchKernelGGL(scatter_padded_kernel<C>, grid, block, 0, stream, out, T, in, T_K, E, EP, \
+                     prefix, cnt, list, D, sh.nsl)
+  switch (sh.cpl) {
+    case 1: L(1); break;
+    case 2: L(2); break;
+    case 3: L(3); break;
+    default: L(4); break;
+  }
+#undef L
+  return hipGetLastError();
 }
 
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,

@@ -37,9 +37,22 @@ size_t scatter_add_workspace_bytes(int T, int a);
 hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
                               int a, int D, const int* valid_rows, void* workspace,
                               hipStream_t stream);
+size_t scatter_add_padded_workspace_bytes(int T, int T_K, int E);
+hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const int* counts,
+                                     int E, const int* ti, uint16_t* out, int T, int D,
+                                     void* workspace, hipStream_t stream);
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream);
+
+// reorder.hip: expert-parallel re-sort and its inverse
+constexpr int kMaxShufflingSegments = 4096;  // (c_hi - c_lo) * EP
+constexpr int kMaxShufflingRanks = 64;
+size_t shuffling_workspace_bytes(int nseg, int64_t em_rows);
+hipError_t launch_shuffling(bool inverse, const uint16_t* in, int64_t in_rows, uint16_t* out,
+                            int64_t out_rows, int D, const int* counts, int EP, int C, int c_lo,
+                            int c_hi, int64_t rank_stride, int* out_counts, void* workspace,
+                            hipStream_t stream);
 
 // finalize.hip
 hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float* w,

@@ -224,6 +224,78 @@ def moe_scatter_add_by_token(out_tokens, in_tokens, row_of_pair, valid_rows=None
     return out_tokens
 
 
+def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, workspace=None):
+    """Static-shape expert-parallel combine: in_tokens (EP, T_K, D); rows of
+    expert e come from rank e // (E // EP). In place on out_tokens (T, D)."""
+    device = out_tokens.device
+    _need(in_tokens, "in_tokens", torch.bfloat16, 3, device)
+    _need(out_tokens, "out_tokens", torch.bfloat16, 2, device)
+    _need(token_counts, "token_counts", torch.int32, 1, device)
+    _need(token_indices, "token_indices", torch.int32, 1, device)
+    for t, n in ((in_tokens, "in_tokens"), (out_tokens, "out_tokens"),
+                 (token_counts, "token_counts"), (token_indices, "token_indices")):
+        _contig(t, n)
+    EP, T_K, D = in_tokens.shape
+    T = out_tokens.shape[0]
+    E = token_counts.numel()
+    if out_tokens.shape[1] != D or token_indices.numel() != T_K:
+        raise ValueError("shapes must be in (EP, T_K, D), token_indices (T_K,), out (T, D)")
+    lib = _lib.load()
+    need = lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _lib.check(lib.moe_scatter_add_padded(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
+                                          _ptr(token_indices), _ptr(out_tokens), T, D,
+                                          _ptr(workspace), workspace.numel(), _stream()))
+    return out_tokens
+
+
+def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, with_counts,
+               workspace):
+    device = tokens.device
+    _need(tokens, "tokens", torch.bfloat16, 2, device)
+    _contig(tokens, "tokens")
+    _need(counts, "counts", torch.int32, 2, device)
+    _contig(counts, "counts")
+    EP, C = counts.shape
+    c_lo = 0 if c_lo is None else c_lo
+    c_hi = C if c_hi is None else c_hi
+    D = tokens.shape[1]
+    if out is None:
+        out = torch.empty((tokens.shape[0] if out_rows is None else out_rows, D),
+                          dtype=torch.bfloat16, device=device)
+    _need(out, "out", torch.bfloat16, 2, device)
+    _contig(out, "out")
+    oc = torch.empty(c_hi - c_lo + 1, dtype=torch.int32, device=device) if with_counts else None
+    lib = _lib.load()
+    em_rows = out.shape[0] if name == "moe_combine_shuffling" else tokens.shape[0]
+    need = lib.moe_shuffling_workspace_bytes(EP, c_hi - c_lo, em_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _lib.check(getattr(lib, name)(
+        _ptr(tokens), tokens.shape[0], _ptr(out), out.shape[0], D, _ptr(counts), EP, C, c_lo,
+        c_hi, -1 if rank_stride is None else int(rank_stride), _ptr(oc), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out, oc
+
+
+def moe_combine_shuffling(tokens, counts, c_lo=None, c_hi=None, rank_stride=None, out=None,
+                          out_rows=None, workspace=None):
+    """Re-sort rows grouped by (rank, expert column) into expert-major order of
+    the local columns [c_lo, c_hi). counts (EP, C) int32; rank_stride None =
+    packed rank chunks. Returns (out, out_counts[n_local + 1])."""
+    return _shuffling("moe_combine_shuffling", tokens, counts, c_lo, c_hi, rank_stride, out,
+                      out_rows, True, workspace)
+
+
+def moe_split_shuffling(tokens, counts, c_lo=None, c_hi=None, rank_stride=None, out=None,
+                        out_rows=None, workspace=None):
+    """Inverse of moe_combine_shuffling: expert-major rows back to their
+    (rank, column) positions in ``out`` (other rows are not written)."""
+    return _shuffling("moe_split_shuffling", tokens, counts, c_lo, c_hi, rank_stride, out,
+                      out_rows, False, workspace)[0]
+
+
 # ---------------------------------------------------------------- finalize
 def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma, eps,
                          flags=0, out=None, mxfp8=False):
@@ -277,3 +349,6 @@ def moe_convert_check(values):
 gather_scale_dense_tokens = moe_gather_scale
 gather_scale_quant_dense_tokens = moe_gather_scale_quant
 scatter_add_dense_tokens = moe_scatter_add
+scatter_add_padded_tokens = moe_scatter_add_padded
+combine_shuffling = moe_combine_shuffling
+split_shuffling = moe_split_shuffling

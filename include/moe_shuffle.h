@@ -226,6 +226,78 @@ MOE_API moe_status_t moe_scatter_add_by_token(moe_bf16_t *out_tokens, int32_t T,
                                       const int32_t *valid_rows, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_scatter_add_padded -- the static-shape expert-parallel combine.
+ *
+ * [GS] scatter_add_padded_tokens, as [LY] _combine_outputs uses it after the
+ * static (all-gather) exchange of _static_comm_forward. in_tokens is
+ * [EP, T_K, D]: rank r's slab holds, at the row positions of the experts it
+ * owns, those rows' expert outputs. token_counts [E] are the per-expert
+ * counts of the shuffle (moe_shuffle's counts[0..E)); expert e's rows are
+ * [off_e, off_e + counts[e]) with off_e the exclusive prefix of counts, and
+ * are read from rank e / (E / EP). Each is added into
+ * out_tokens[token_indices[row]] with moe_scatter_add's order and rounding:
+ * per token, the initial value, then its rows in ascending row index, in
+ * fp32, rounded once to bf16; tokens with no row are not written.
+ *
+ * in_tokens [EP, T_K, D] bf16; token_counts [E] int32 (device; the row total
+ * is clamped to T_K); token_indices [T_K] int32; out_tokens [T, D] bf16
+ * in/out. E % EP == 0, 1 <= E <= 1024, D % 8 == 0, EP * T_K < 2^31.
+ * workspace >= moe_scatter_add_padded_workspace_bytes(T, T_K, E), 256-byte
+ * aligned.
+ * ---------------------------------------------------------------------- */
+MOE_API size_t moe_scatter_add_padded_workspace_bytes(int32_t T, int32_t T_K, int32_t E);
+MOE_API moe_status_t moe_scatter_add_padded(const moe_bf16_t *in_tokens, int32_t EP,
+                                            int32_t T_K, const int32_t *token_counts,
+                                            int32_t E, const int32_t *token_indices,
+                                            moe_bf16_t *out_tokens, int32_t T, int32_t D,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine_shuffling / moe_split_shuffling -- the expert-parallel
+ * receive-side re-sort and its inverse.
+ *
+ * [LY] _dynamic_comm_forward and _static_comm_forward call combine_shuffling
+ * on the rows received from EP ranks before the expert GEMMs and
+ * split_shuffling on the GEMM output before sending it back; the source of
+ * both is absent from the pages, and this is the reading of their use.
+ * Rows are grouped by source rank, and inside a rank's chunk by expert
+ * column c in [0, C): segment (r, c) holds counts[r*C + c] rows. Rank r's
+ * chunk starts at row r * rank_stride, or right after rank r-1's chunk when
+ * rank_stride < 0 (packed, the dynamic exchange; a fixed stride is the
+ * static exchange's [EP, T, D] buffer).
+ *   combine: out[0..total) = the segments of the local columns [c_lo, c_hi)
+ *            in expert-major order (for each local column, ranks 0..EP-1);
+ *            out_counts[l] = rows of column c_lo + l, out_counts[c_hi-c_lo]
+ *            = total. Rows of out beyond total are not written.
+ *   split:   the inverse: in[0..total) (expert-major) goes back to the
+ *            (rank, column) positions in out; other rows of out are not
+ *            written. out_counts (nullable) as for combine.
+ * Rows are copied bit for bit. Rows whose position falls outside in_rows /
+ * out_rows are skipped.
+ *
+ * in [in_rows, D] bf16, out [out_rows, D] bf16; counts [EP, C] int32
+ * (device); out_counts [c_hi - c_lo + 1] int32. 1 <= EP <= 64,
+ * (c_hi - c_lo) * EP <= 4096, 0 <= c_lo <= c_hi <= C, D % 8 == 0, rows and
+ * EP * rank_stride < 2^31. workspace >=
+ * moe_shuffling_workspace_bytes(EP, c_hi - c_lo, expert-major rows), where
+ * the expert-major rows are out_rows for combine and in_rows for split.
+ * ---------------------------------------------------------------------- */
+MOE_API size_t moe_shuffling_workspace_bytes(int32_t EP, int32_t n_local, int64_t em_rows);
+MOE_API moe_status_t moe_combine_shuffling(const moe_bf16_t *in, int64_t in_rows,
+                                           moe_bf16_t *out, int64_t out_rows, int32_t D,
+                                           const int32_t *counts, int32_t EP, int32_t C,
+                                           int32_t c_lo, int32_t c_hi, int64_t rank_stride,
+                                           int32_t *out_counts, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+MOE_API moe_status_t moe_split_shuffling(const moe_bf16_t *in, int64_t in_rows,
+                                         moe_bf16_t *out, int64_t out_rows, int32_t D,
+                                         const int32_t *counts, int32_t EP, int32_t C,
+                                         int32_t c_lo, int32_t c_hi, int64_t rank_stride,
+                                         int32_t *out_counts, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_finalize_rmsnorm -- the MoE tail: weighted top-k reduction, shared
  * expert add, RMSNorm, optional MXFP8 output.
  *

@@ -78,9 +78,14 @@ def _load():
                                          _u16p, ctypes.c_float, _int, _int,
                                          _int, ctypes.c_uint, _u16p, _u8p, _u8p]
     lib.orc_mxfp8_quantize.argtypes = [_u16p, _int, _int, _u8p, _u8p]
+    lib.orc_shuffling.argtypes = [_int, _u16p, _ll, _u16p, _ll, _int, _i32p, _int, _int,
+                                  _int, _int, _ll, _i32p]
+    lib.orc_scatter_add_padded.argtypes = [_u16p, _int, _u16p, _int, _int, _i32p,
+                                           _int, _i32p, _int]
     for name in ("orc_topk", "orc_shuffle", "orc_gather_scale",
                  "orc_gather_scale_quant", "orc_scatter_add",
-                 "orc_finalize_rmsnorm", "orc_mxfp8_quantize"):
+                 "orc_finalize_rmsnorm", "orc_mxfp8_quantize",
+                 "orc_scatter_add_padded", "orc_shuffling"):
         getattr(lib, name).restype = _int
     _lib = lib
     return lib
@@ -216,6 +221,19 @@ def scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None):
     return out_tokens
 
 
+def scatter_add_padded(out_tokens, in_tokens, token_counts, token_indices):
+    """In place on out_tokens (uint16 (T,D)); in_tokens uint16 (EP, T_K, D)."""
+    T, D = out_tokens.shape
+    EP, T_K, D2 = in_tokens.shape
+    assert D2 == D
+    counts = np.ascontiguousarray(token_counts, dtype=np.int32)
+    ti = np.ascontiguousarray(token_indices, dtype=np.int32)
+    _check(_load().orc_scatter_add_padded(_p(out_tokens, _u16p), T, _p(in_tokens, _u16p), EP,
+                                          T_K, _p(counts, _i32p), counts.size, _p(ti, _i32p),
+                                          D), "scatter_add_padded")
+    return out_tokens
+
+
 def finalize_rmsnorm(y, expert_weights, row_of_pair, shared, gamma, eps,
                      flags=0, mxfp8=False):
     """Returns out (T,D) uint16, and (codes (T,D) uint8, scales (T,D/32) uint8)
@@ -241,3 +259,38 @@ def mxfp8_quantize(o_bits: np.ndarray):
     _check(_load().orc_mxfp8_quantize(_p(o_bits, _u16p), rows, D, _p(codes, _u8p),
                                       _p(scales, _u8p)), "mxfp8_quantize")
     return codes, scales
+
+
+def _shuffling(inverse, in_rows_arr, counts, c_lo, c_hi, rank_stride, out):
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    EP, C = counts.shape
+    oc = np.zeros(c_hi - c_lo + 1, dtype=np.int32)
+    _check(_load().orc_shuffling(int(inverse), _p(in_rows_arr, _u16p), in_rows_arr.shape[0],
+                                 _p(out, _u16p), out.shape[0], in_rows_arr.shape[1],
+                                 _p(counts, _i32p), EP, C, c_lo, c_hi,
+                                 -1 if rank_stride is None else int(rank_stride),
+                                 _p(oc, _i32p)), "shuffling")
+    return out, oc
+
+
+def combine_shuffling(tokens, counts, c_lo=None, c_hi=None, rank_stride=None, out=None):
+    """tokens uint16 (rows, D) grouped by (rank, column); counts (EP, C).
+    Returns (out rows in expert-major order of columns [c_lo, c_hi),
+    out_counts [n_local + 1]). rank_stride None = packed rank chunks."""
+    EP, C = np.asarray(counts).shape
+    c_lo = 0 if c_lo is None else c_lo
+    c_hi = C if c_hi is None else c_hi
+    if out is None:
+        out = np.zeros_like(tokens)
+    return _shuffling(0, np.ascontiguousarray(tokens), counts, c_lo, c_hi, rank_stride, out)
+
+
+def split_shuffling(tokens, counts, c_lo=None, c_hi=None, rank_stride=None, out=None):
+    """Inverse of combine_shuffling: rows in expert-major order back to their
+    (rank, column) positions in ``out`` (other rows of out untouched)."""
+    EP, C = np.asarray(counts).shape
+    c_lo = 0 if c_lo is None else c_lo
+    c_hi = C if c_hi is None else c_hi
+    if out is None:
+        out = np.zeros_like(tokens)
+    return _shuffling(1, np.ascontiguousarray(tokens), counts, c_lo, c_hi, rank_stride, out)[0]

@@ -360,6 +360,138 @@ int orc_scatter_add(uint16_t *out /* [T*D] in/out */, int T,
     return ORC_OK;
 }
 
+/* [GS] scatter_add_padded_tokens: the static-shape expert-parallel combine.
+ * in is [EP, T_K, D]: rank r's slab holds, at the row positions of the
+ * experts it owns, the outputs of those rows. counts [E] are the per-expert
+ * row counts of the shuffle; the rows of expert e are [off_e, off_e +
+ * counts[e]) with off_e the exclusive prefix of counts, and they come from
+ * rank e / (E / EP). Each such row is added into out[token_indices[row]].
+ * Same fixed order as orc_scatter_add: per token, the initial value then
+ * its rows in ascending row index, fp32, one bf16 rounding; tokens with no
+ * row are not written. E % EP == 0 and sum(counts) <= T_K are required. */
+int orc_scatter_add_padded(uint16_t *out /* [T*D] in/out */, int T,
+                           const uint16_t *in /* [EP*T_K*D] */, int EP, int T_K,
+                           const int *counts /* [E] */, int E,
+                           const int *token_indices /* [T_K] */, int D)
+{
+    if (T < 0 || D < 0 || EP < 1 || E < 1 || E % EP != 0 || T_K < 0) return ORC_BAD;
+    long long V = 0;
+    for (int e = 0; e < E; ++e) {
+        if (counts[e] < 0) return ORC_BAD;
+        V += counts[e];
+    }
+    if (V > T_K) return ORC_BAD;
+    int *rank_of_row = (int *)malloc(sizeof(int) * (size_t)(V > 0 ? V : 1));
+    long long off = 0;
+    for (int e = 0; e < E; ++e) {
+        for (int i = 0; i < counts[e]; ++i) rank_of_row[off + i] = e / (E / EP);
+        off += counts[e];
+    }
+    /* bucket rows by token in ascending row order */
+    int *cnt = (int *)calloc((size_t)T + 1, sizeof(int));
+    for (long long r = 0; r < V; ++r) {
+        int t = token_indices[r];
+        if (t < 0 || t >= T) { free(cnt); free(rank_of_row); return ORC_BAD; }
+        cnt[t + 1] += 1;
+    }
+    for (int t = 0; t < T; ++t) cnt[t + 1] += cnt[t];
+    int *fill = (int *)malloc(sizeof(int) * (size_t)(T > 0 ? T : 1));
+    int *rows = (int *)malloc(sizeof(int) * (size_t)(V > 0 ? V : 1));
+    for (int t = 0; t < T; ++t) fill[t] = cnt[t];
+    for (long long r = 0; r < V; ++r) rows[fill[token_indices[r]]++] = (int)r;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)(D > 0 ? D : 1));
+    for (int t = 0; t < T; ++t) {
+        if (cnt[t + 1] == cnt[t]) continue;
+        uint16_t *o = out + (long long)t * D;
+        for (int d = 0; d < D; ++d) acc[d] = orc_bf16_to_f32(o[d]);
+        for (int j = cnt[t]; j < cnt[t + 1]; ++j) {
+            int r = rows[j];
+            const uint16_t *src =
+                in + ((long long)rank_of_row[r] * T_K + r) * (long long)D;
+            for (int d = 0; d < D; ++d) acc[d] = acc[d] + orc_bf16_to_f32(src[d]);
+        }
+        for (int d = 0; d < D; ++d) o[d] = orc_f32_to_bf16(acc[d]);
+    }
+    free(acc);
+    free(rows);
+    free(fill);
+    free(cnt);
+    free(rank_of_row);
+    return ORC_OK;
+}
+
+/* [LY] combine_shuffling / split_shuffling (their source is absent; this is
+ * the reading of how _dynamic_comm_forward and _static_comm_forward use
+ * them). Rows arrive grouped by source rank, and inside a rank's chunk by
+ * expert column c in [0, C): segment (r, c) holds counts[r*C + c] rows.
+ * Rank r's chunk starts at r * rank_stride, or, with rank_stride < 0, right
+ * after rank r-1's chunk (packed). combine gathers the columns of the local
+ * expert range [c_lo, c_hi) into expert-major order -- for each local column,
+ * the segments of ranks 0..EP-1 in turn -- and writes out_counts[l] = rows of
+ * column c_lo + l and out_counts[c_hi - c_lo] = their total. split is the
+ * inverse: rows in that expert-major order go back to their (rank, column)
+ * positions. Rows are copied bit for bit. */
+static int shuffling_table(const int *counts, int EP, int C, int c_lo, int c_hi,
+                           long long rank_stride, long long *src_start,
+                           long long *dst_start, long long *total)
+{
+    if (EP < 1 || C < 1 || c_lo < 0 || c_hi > C || c_lo > c_hi) return ORC_BAD;
+    int nl = c_hi - c_lo;
+    long long chunk = 0;  /* start of rank r's chunk */
+    for (int r = 0; r < EP; ++r) {
+        long long base = rank_stride >= 0 ? (long long)r * rank_stride : chunk;
+        long long off = 0;
+        for (int c = 0; c < C; ++c) {
+            if (counts[r * C + c] < 0) return ORC_BAD;
+            if (c >= c_lo && c < c_hi) src_start[(c - c_lo) * EP + r] = base + off;
+            off += counts[r * C + c];
+        }
+        chunk = base + off;
+    }
+    long long run = 0;
+    for (int l = 0; l < nl; ++l)
+        for (int r = 0; r < EP; ++r) {
+            dst_start[l * EP + r] = run;
+            run += counts[r * C + c_lo + l];
+        }
+    *total = run;
+    return ORC_OK;
+}
+
+int orc_shuffling(int inverse, const uint16_t *in, long long in_rows,
+                  uint16_t *out, long long out_rows, int D, const int *counts,
+                  int EP, int C, int c_lo, int c_hi, long long rank_stride,
+                  int *out_counts /* [c_hi - c_lo + 1], may be NULL */)
+{
+    if (D < 0) return ORC_BAD;
+    int nseg = (c_hi - c_lo) * EP;
+    long long *src = (long long *)malloc(sizeof(long long) * (size_t)(nseg > 0 ? nseg : 1));
+    long long *dst = (long long *)malloc(sizeof(long long) * (size_t)(nseg > 0 ? nseg : 1));
+    long long total = 0;
+    int rc = shuffling_table(counts, EP, C, c_lo, c_hi, rank_stride, src, dst, &total);
+    for (int q = 0; rc == ORC_OK && q < nseg; ++q) {
+        int r = q % EP, l = q / EP;
+        long long len = counts[r * C + c_lo + l];
+        for (long long j = 0; j < len; ++j) {
+            long long a = src[q] + j, b = dst[q] + j; /* a: rank-major, b: expert-major */
+            long long from = inverse ? b : a, to = inverse ? a : b;
+            if (from >= in_rows || to >= out_rows) { rc = ORC_BAD; break; }
+            memcpy(out + to * D, in + from * D, sizeof(uint16_t) * (size_t)D);
+        }
+    }
+    if (rc == ORC_OK && out_counts) {
+        for (int l = 0; l < c_hi - c_lo; ++l) {
+            long long n = 0;
+            for (int r = 0; r < EP; ++r) n += counts[r * C + c_lo + l];
+            out_counts[l] = (int)n;
+        }
+        out_counts[c_hi - c_lo] = (int)total;
+    }
+    free(src);
+    free(dst);
+    return rc;
+}
+
 /* ------------------------------------------------------------------------ */
 /* MXFP8 of bf16 rows.                                                       */
 /* ------------------------------------------------------------------------ */

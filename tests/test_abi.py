@@ -149,6 +149,50 @@ def test_scatter_rejects(lib):
 
 
 @host_only
+def test_scatter_padded_rejects(lib):
+    p = lib.moe_scatter_add_padded
+    ws = 1 << 22
+    assert p(FAKE, 3, 64, FAKE, 8, FAKE, FAKE, 16, 64, FAKE, ws, None) == INVALID   # E % EP
+    assert p(FAKE, 2, 64, FAKE, 2048, FAKE, FAKE, 16, 64, FAKE, ws, None) == UNSUPPORTED
+    assert p(FAKE, 2, 64, FAKE, 8, FAKE, FAKE, 16, 60, FAKE, ws, None) == INVALID   # D % 8
+    assert p(FAKE, 2, 64, None, 8, FAKE, FAKE, 16, 64, FAKE, ws, None) == INVALID
+    assert p(FAKE, 2, 64, FAKE, 8, FAKE, FAKE, 16, 64, FAKE, 8, None) == WORKSPACE
+    assert p(FAKE, 1 << 10, 1 << 22, FAKE, 1 << 10, FAKE, FAKE, 16, 64, FAKE, ws,
+             None) == INVALID                                                     # EP*T_K
+    assert p(None, 2, 0, None, 8, None, None, 16, 64, None, 0, None) == OK        # T_K == 0
+    assert lib.moe_scatter_add_padded_workspace_bytes(16, 64, 8) == 256 + 256 + 2 * 256
+
+
+@host_only
+def test_shuffling_rejects(lib):
+    c, sp = lib.moe_combine_shuffling, lib.moe_split_shuffling
+    ws = 1 << 22
+    args = [FAKE, 64, FAKE, 64, 64, FAKE, 4, 8, 0, 8, -1, FAKE, FAKE, ws, None]
+
+    def call(f, **kw):
+        a = list(args)
+        names = ["in_", "in_rows", "out", "out_rows", "D", "counts", "EP", "C", "lo", "hi",
+                 "stride", "oc", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(c, EP=0) == UNSUPPORTED
+    assert call(c, EP=65) == UNSUPPORTED
+    assert call(c, lo=5, hi=4) == INVALID
+    assert call(c, hi=9) == INVALID
+    assert call(c, C=4096, hi=4096, EP=2) == UNSUPPORTED      # 8192 segments > 4096
+    assert call(c, D=60) == INVALID
+    assert call(c, counts=None) == INVALID
+    assert call(c, oc=None) == INVALID                        # required for combine
+    assert call(c, wsb=8) == WORKSPACE
+    assert call(c, in_=FAKE + 8) == INVALID
+    assert call(c, stride=1 << 30) == INVALID                 # EP * stride >= 2^31
+    assert call(sp, in_rows=1 << 31) == INVALID
+    assert lib.moe_shuffling_workspace_bytes(4, 8, 64) == 2 * 256 + 256
+
+
+@host_only
 def test_finalize_rejects(lib):
     f = lib.moe_finalize_rmsnorm
     args = dict(y=FAKE, rows=64, w=FAKE, rop=FAKE, sh=FAKE, g=FAKE, eps=1e-6, T=8, K=8,

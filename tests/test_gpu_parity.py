@@ -250,6 +250,85 @@ def test_scatter_add_general_long_lists(dev):
     assert np.array_equal(bits_host(out), want)
 
 
+# ---------------------------------------------------------------- padded combine
+PADDED_CASES = [
+    # (name, T, D, E, K, EP)
+    ("ep1", 40, 256, 8, 2, 1),
+    ("ep2-ragged-D", 77, 8 * (64 * 5 + 3), 10, 3, 2),
+    ("ep4", 129, 1024, 16, 4, 4),
+    ("ep8-wide", 64, 8 * 1000, 64, 8, 8),
+]
+
+
+@pytest.mark.parametrize("case", PADDED_CASES, ids=[c[0] for c in PADDED_CASES])
+def test_scatter_add_padded_bit_exact(dev, case):
+    name, T, D, E, K, EP = case
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, None, seed=2)
+    g = np.random.default_rng(5)
+    slabs = W.to_bf16_bits(g.standard_normal((EP, T * K, D)).astype(np.float32))
+    say("padded", name, T, D, E, K, EP)
+    want = orc.scatter_add_padded(inp.out0.copy(), slabs, counts[:E], ti)
+    out = bf_dev(inp.out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts[:E], dev), i32_dev(ti, dev),
+                               out)
+    assert np.array_equal(bits_host(out), want)
+
+
+def test_scatter_add_padded_long_lists(dev):
+    """A token owning 100 rows (beyond one wave's sort), empty experts, and a
+    count total below T_K."""
+    g = np.random.default_rng(12)
+    T, D, E, EP, T_K = 10, 8 * 40, 12, 4, 300
+    counts = np.array([30, 0, 25, 40, 0, 0, 35, 20, 10, 0, 50, 20], np.int32)  # 230 rows
+    ti = g.integers(0, T, size=T_K).astype(np.int32)
+    ti[g.permutation(230)[:100]] = 3
+    slabs = W.to_bf16_bits(g.standard_normal((EP, T_K, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("padded long lists", T, D, E, EP, T_K)
+    want = orc.scatter_add_padded(out0.copy(), slabs, counts, ti)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts, dev), i32_dev(ti, dev), out)
+    assert np.array_equal(bits_host(out), want)
+
+
+# ---------------------------------------------------------------- EP re-sort
+SHUFFLING_CASES = [
+    # (name, EP, C, c_lo, c_hi, packed, max count, D)
+    ("dynamic-ep4", 4, 16, 0, 16, True, 9, 256),
+    ("dynamic-ep8-ragged-D", 8, 32, 0, 32, True, 7, 8 * (64 * 3 + 5)),
+    ("static-ep8-local-range", 8, 64, 16, 24, False, 12, 1024),
+    ("static-ep2-empty-range", 2, 8, 3, 3, False, 5, 64),
+    ("static-ep64", 64, 32, 0, 32, False, 3, 512),
+]
+
+
+@pytest.mark.parametrize("case", SHUFFLING_CASES, ids=[c[0] for c in SHUFFLING_CASES])
+def test_combine_split_shuffling_bit_exact(dev, case):
+    name, EP, C, lo, hi, packed, mx, D = case
+    g = np.random.default_rng(21)
+    counts = g.integers(0, mx + 1, size=(EP, C)).astype(np.int32)
+    counts[0, :2] = 0                                    # empty segments
+    stride = None if packed else int(counts.sum(axis=1).max() + 3)
+    rows = int(counts.sum()) if packed else EP * stride
+    tok = W.to_bf16_bits(g.standard_normal((rows, D)).astype(np.float32))
+    say("shuffling", name, EP, C, lo, hi, rows, D)
+    want, woc = orc.combine_shuffling(tok, counts, lo, hi, stride,
+                                      out=np.full((rows, D), SENTINEL, np.uint16))
+    out0 = torch.full((rows, D), SENTINEL - 65536, dtype=torch.int16,
+                      device=dev).view(torch.bfloat16)
+    out, oc = ops.moe_combine_shuffling(bf_dev(tok, dev), i32_dev(counts, dev), lo, hi, stride,
+                                        out=out0)
+    assert np.array_equal(oc.cpu().numpy(), woc)
+    assert np.array_equal(bits_host(out), want)
+    # split back into a fresh buffer: the moved rows return, others untouched
+    wback = orc.split_shuffling(want, counts, lo, hi, stride,
+                                out=np.full((rows, D), SENTINEL, np.uint16))
+    back0 = torch.full((rows, D), SENTINEL - 65536, dtype=torch.int16,
+                       device=dev).view(torch.bfloat16)
+    back = ops.moe_split_shuffling(out, i32_dev(counts, dev), lo, hi, stride, out=back0)
+    assert np.array_equal(bits_host(back), wback)
+
+
 # ---------------------------------------------------------------- finalize
 def _close(got_bits, want_bits, what):
     g = orc.bf16_to_f32(got_bits).astype(np.float64)
