@@ -18,6 +18,8 @@ for the DeepSeek-V4.1 finalize presets):
                                         popularity, valid_token_count = 6000
   decode   T in {1,8,32,128}, D=7168, K=8   finalize + RMSNorm
   prefill  T=16384, D=5120, E=128, K=4      finalize + RMSNorm + MXFP8
+  mhc      T=16384, D=5120, E=128, K=4, hc=4 finalize + mHC post-mix and
+                                        collapse + RMSNorm + MXFP8 (swizzled)
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ import numpy as np
 import torch
 
 # tensor ids: one generator per tensor
-_X, _LOGITS, _Y, _OUT0, _PERM, _W, _SHARED, _GAMMA, _ZIPF, _GUMBEL, _HOLES = range(11)
+(_X, _LOGITS, _Y, _OUT0, _PERM, _W, _SHARED, _GAMMA, _ZIPF, _GUMBEL, _HOLES,
+ _RESID, _POST, _COMB, _PRE) = range(15)
 
 
 @dataclass(frozen=True)
@@ -46,6 +49,7 @@ class Workload:
     eps: float = 1e-6                # finalize RMSNorm epsilon
     mxfp8: bool = False
     sweep_T: tuple = field(default_factory=tuple)
+    hc: int = 0                      # mHC residual streams (0: plain finalize)
 
 
 WORKLOADS = {
@@ -57,6 +61,7 @@ WORKLOADS = {
     "decode": Workload("decode", 3, T=128, D=7168, E=256, K=8,
                        sweep_T=(1, 8, 32, 128)),
     "prefill": Workload("prefill", 4, T=16384, D=5120, E=128, K=4, mxfp8=True),
+    "mhc": Workload("mhc", 5, T=16384, D=5120, E=128, K=4, mxfp8=True, hc=4),
 }
 
 
@@ -190,3 +195,32 @@ def finalize_inputs(wl: Workload, T: int | None = None, D: int | None = None,
     g = rng(wl.cfg_id, _GAMMA, seed).uniform(0.5, 1.5, size=D).astype(np.float32)
     return FinalizeInputs(y=y, w=np.ascontiguousarray(w), row_of_pair=rop,
                           shared=shared, gamma=to_bf16_bits(g), eps=wl.eps)
+
+
+@dataclass
+class MhcInputs:
+    residual: np.ndarray     # (T, hc, D) bf16 bits: the hc residual streams
+    post: np.ndarray         # (T, hc) fp32 post-mix
+    comb: np.ndarray         # (T, hc, hc) fp32 residual mix [source, target]
+    pre: np.ndarray          # (T, hc) fp32 pre-mix of the collapse
+
+
+def mhc_inputs(wl: Workload, T: int | None = None, D: int | None = None,
+               hc: int | None = None, seed: int = 0) -> MhcInputs:
+    """Inputs of the mHC stage, shaped like those of a trained hyper-connection
+    layer: residual streams N(0,1) bf16; post = 2*sigmoid(N(0,1)) in (0, 2);
+    pre = sigmoid(N(0,1)) in (0, 1); comb a doubly stochastic matrix per token
+    (20 alternating row/column normalisations of exp(N(0,1)), in fp64)."""
+    T = wl.T if T is None else T
+    D = wl.D if D is None else D
+    hc = (wl.hc or 4) if hc is None else hc
+    residual = normal_bf16(rng(wl.cfg_id, _RESID, seed), (T, hc, D))
+    post = 2.0 / (1.0 + np.exp(-rng(wl.cfg_id, _POST, seed).standard_normal((T, hc))))
+    pre = 1.0 / (1.0 + np.exp(-rng(wl.cfg_id, _PRE, seed).standard_normal((T, hc))))
+    c = np.exp(rng(wl.cfg_id, _COMB, seed).standard_normal((T, hc, hc)))
+    for _ in range(20):
+        c = c / c.sum(axis=2, keepdims=True)
+        c = c / c.sum(axis=1, keepdims=True)
+    return MhcInputs(residual=residual, post=post.astype(np.float32),
+                     comb=np.ascontiguousarray(c.astype(np.float32)),
+                     pre=pre.astype(np.float32))

@@ -74,9 +74,17 @@ def _load():
                                            _int, _ll, _u8p, _f32p]
     lib.orc_scatter_add.argtypes = [_u16p, _int, _u16p, _i32p, _int, _int, _int,
                                     _ll]
-    lib.orc_finalize_rmsnorm.argtypes = [_u16p, _ll, _f32p, _i32p, _u16p,
+    lib.orc_mxfp8_scale_bytes.argtypes = [_int, _int, _int]
+    lib.orc_mxfp8_scale_bytes.restype = _ll
+    lib.orc_mxfp8_swizzle_offset.argtypes = [_int, _int, _int]
+    lib.orc_mxfp8_swizzle_offset.restype = _ll
+    lib.orc_mxfp8_swizzle.argtypes = [_u8p, _int, _int, _u8p]
+    lib.orc_finalize_rmsnorm.argtypes = [_u16p, _ll, ctypes.c_void_p, _i32p, _u16p,
                                          _u16p, ctypes.c_float, _int, _int,
                                          _int, ctypes.c_uint, _u16p, _u8p, _u8p]
+    lib.orc_finalize_mhc.argtypes = [_u16p, _ll, ctypes.c_void_p, _i32p, _u16p, _u16p,
+                                     _f32p, _f32p, _f32p, _u16p, ctypes.c_float, _int, _int,
+                                     _int, _int, ctypes.c_uint, _u16p, _u16p, _u8p, _u8p]
     lib.orc_mxfp8_quantize.argtypes = [_u16p, _int, _int, _u8p, _u8p]
     lib.orc_shuffling.argtypes = [_int, _u16p, _ll, _u16p, _ll, _int, _i32p, _int, _int,
                                   _int, _int, _ll, _i32p]
@@ -84,8 +92,8 @@ def _load():
                                            _int, _i32p, _int]
     for name in ("orc_topk", "orc_shuffle", "orc_gather_scale",
                  "orc_gather_scale_quant", "orc_scatter_add",
-                 "orc_finalize_rmsnorm", "orc_mxfp8_quantize",
-                 "orc_scatter_add_padded", "orc_shuffling"):
+                 "orc_finalize_rmsnorm", "orc_finalize_mhc", "orc_mxfp8_quantize",
+                 "orc_scatter_add_padded", "orc_shuffling", "orc_mxfp8_swizzle"):
         getattr(lib, name).restype = _int
     _lib = lib
     return lib
@@ -236,18 +244,75 @@ def scatter_add_padded(out_tokens, in_tokens, token_counts, token_indices):
 
 def finalize_rmsnorm(y, expert_weights, row_of_pair, shared, gamma, eps,
                      flags=0, mxfp8=False):
-    """Returns out (T,D) uint16, and (codes (T,D) uint8, scales (T,D/32) uint8)
-    when ``mxfp8``."""
+    """Returns out (T,D) uint16, and (codes (T,D) uint8, scales) when
+    ``mxfp8``; scales are (T, D/32) row-major, or with flags bit 2 the
+    swizzled byte buffer. expert_weights: fp32 (T,K), or uint16 bf16 bits
+    with flags bit 1."""
     T, K = row_of_pair.shape
     rows, D = y.shape
+    w = np.ascontiguousarray(expert_weights)
+    assert w.dtype == (np.uint16 if flags & 2 else np.float32)
     out = np.empty((T, D), dtype=np.uint16)
     codes = np.empty((T, D), dtype=np.uint8) if mxfp8 else None
-    scales = np.empty((T, D // 32), dtype=np.uint8) if mxfp8 else None
+    if mxfp8 and flags & 4:
+        scales = np.empty(mxfp8_scale_bytes(T, D, True), dtype=np.uint8)
+    else:
+        scales = np.empty((T, D // 32), dtype=np.uint8) if mxfp8 else None
     _check(_load().orc_finalize_rmsnorm(
-        _p(y, _u16p), rows, _p(expert_weights, _f32p), _p(row_of_pair, _i32p),
+        _p(y, _u16p), rows, w.ctypes.data, _p(row_of_pair, _i32p),
         _p(shared, _u16p), _p(gamma, _u16p), float(eps), T, K, D, int(flags),
         _p(out, _u16p), _p(codes, _u8p), _p(scales, _u8p)), "finalize_rmsnorm")
     return (out, codes, scales) if mxfp8 else out
+
+
+def finalize_mhc(y, expert_weights, row_of_pair, shared, residual, post, comb, pre,
+                 gamma, eps, flags=0, mxfp8=False):
+    """mHC finalize: returns (residual_out (T,hc,D) uint16, out (T,D) uint16 or
+    None, codes, scales). ``pre`` None: residual only (out, codes and scales
+    are None). residual (T,hc,D) bf16 bits; post and pre (T,hc) fp32; comb
+    (T,hc,hc) fp32 indexed [source, target]. Weights and flags as in
+    finalize_rmsnorm."""
+    T, K = row_of_pair.shape
+    rows, D = y.shape
+    hc = residual.shape[1]
+    assert residual.shape == (T, hc, D)
+    w = np.ascontiguousarray(expert_weights)
+    assert w.dtype == (np.uint16 if flags & 2 else np.float32)
+    post = np.ascontiguousarray(post, dtype=np.float32).reshape(T, hc)
+    comb = np.ascontiguousarray(comb, dtype=np.float32).reshape(T, hc, hc)
+    if pre is not None:
+        pre = np.ascontiguousarray(pre, dtype=np.float32).reshape(T, hc)
+    res_out = np.empty((T, hc, D), dtype=np.uint16)
+    out = np.empty((T, D), dtype=np.uint16) if pre is not None else None
+    codes = scales = None
+    if mxfp8:
+        codes = np.empty((T, D), dtype=np.uint8)
+        scales = (np.empty(mxfp8_scale_bytes(T, D, True), dtype=np.uint8) if flags & 4
+                  else np.empty((T, D // 32), dtype=np.uint8))
+    _check(_load().orc_finalize_mhc(
+        _p(y, _u16p), rows, w.ctypes.data, _p(row_of_pair, _i32p), _p(shared, _u16p),
+        _p(np.ascontiguousarray(residual), _u16p), _p(post, _f32p), _p(comb, _f32p),
+        _p(pre, _f32p), _p(gamma, _u16p), float(eps), T, K, D, hc, int(flags),
+        _p(res_out, _u16p), _p(out, _u16p), _p(codes, _u8p), _p(scales, _u8p)),
+        "finalize_mhc")
+    return res_out, out, codes, scales
+
+
+def mxfp8_scale_bytes(M: int, D: int, swizzled: bool) -> int:
+    return int(_load().orc_mxfp8_scale_bytes(M, D, int(bool(swizzled))))
+
+
+def mxfp8_swizzle(rowmajor: np.ndarray) -> np.ndarray:
+    """(M, cols) uint8 scales -> the swizzled 128x4 byte buffer."""
+    rowmajor = np.ascontiguousarray(rowmajor, dtype=np.uint8)
+    M, cols = rowmajor.shape
+    out = np.empty(mxfp8_scale_bytes(M, 32 * cols, True), dtype=np.uint8)
+    _check(_load().orc_mxfp8_swizzle(_p(rowmajor, _u8p), M, cols, _p(out, _u8p)), "swizzle")
+    return out
+
+
+def mxfp8_swizzle_offset(m: int, k: int, cols: int) -> int:
+    return int(_load().orc_mxfp8_swizzle_offset(m, k, cols))
 
 
 def mxfp8_quantize(o_bits: np.ndarray):

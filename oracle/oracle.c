@@ -524,6 +524,43 @@ int orc_mxfp8_quantize(const uint16_t *o, int rows, int D, uint8_t *codes,
     return ORC_OK;
 }
 
+/* Byte size of an MXFP8 scale buffer for M rows of D elements: row-major
+ * [M, D/32], or (swizzled) M rounded up to 128 times D/32 rounded up to 4
+ * ([MH] mxfp8_scale_bytes; the layout below is this oracle's reading). */
+long long orc_mxfp8_scale_bytes(int M, int D, int swizzled)
+{
+    long long cols = D / 32;
+    if (!swizzled) return (long long)M * cols;
+    long long mp = ((long long)M + 127) / 128 * 128;
+    long long kp = (cols + 3) / 4 * 4;
+    return mp * kp;
+}
+
+/* [MH] _LamportMHCDeviceKernel writes the MXFP8 scales "in the swizzled
+ * 128x4 layout" of the MXFP8 GEMMs, zeroing the scales of the padding rows up
+ * to a multiple of 128; the index helper is absent from the pages. Reading:
+ * 128-row x 4-column tiles of 512 bytes in row-tile-major order; inside a
+ * tile, row m and column k sit at (m % 32) * 16 + ((m % 128) / 32) * 4 +
+ * (k % 4). Padding rows (and columns up to a multiple of 4) are zero. */
+long long orc_mxfp8_swizzle_offset(int m, int k, int cols)
+{
+    long long kt_n = (cols + 3) / 4;
+    long long tile = (long long)(m / 128) * kt_n + (k / 4);
+    return tile * 512 + (m % 32) * 16 + ((m % 128) / 32) * 4 + (k % 4);
+}
+
+int orc_mxfp8_swizzle(const uint8_t *rowmajor /* [M, cols] */, int M, int cols,
+                      uint8_t *out /* orc_mxfp8_scale_bytes(M, 32*cols, 1) */)
+{
+    if (M < 0 || cols < 0) return ORC_BAD;
+    long long n = orc_mxfp8_scale_bytes(M, 32 * cols, 1);
+    memset(out, 0, (size_t)n);
+    for (int m = 0; m < M; ++m)
+        for (int k = 0; k < cols; ++k)
+            out[orc_mxfp8_swizzle_offset(m, k, cols)] = rowmajor[(long long)m * cols + k];
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Finalize: weighted top-k reduction + shared add + RMSNorm (+ MXFP8).      */
 /* ------------------------------------------------------------------------ */
@@ -543,9 +580,60 @@ int orc_mxfp8_quantize(const uint16_t *o, int rows, int D, uint8_t *codes,
  *       reciprocal square root (computed in double and rounded once).
  *  [MH] MXFP8 of the bf16 output, per 32-element block: UE8M0 byte from the
  *       block max (orc_ue8m0_from_amax); codes = E4M3(o * 2^(127 - byte)).
- *       Scales are stored row-major, [T, D/32].
+ *       Scales are stored row-major, [T, D/32]; with flags bit 2 in the
+ *       swizzled 128x4 layout (orc_mxfp8_swizzle), D % 128 == 0.
+ *  flags bit 1: the weights are bf16 (uint16 bits), widened exactly.
  * mx_codes and mx_scales are both NULL or both set; shared may be NULL. */
-int orc_finalize_rmsnorm(const uint16_t *y, long long rows, const float *w,
+/* RMSNorm of one bf16 row ([MH] _LamportMHCDeviceKernel; [K3] routed role):
+ * ss = sum of x^2 in fp32, sequential in d (flags bit 0: each square rounded
+ * to bf16 first); inv = correctly rounded 1/sqrt(ss/D + eps); out =
+ * bf16((x * inv) * gamma). */
+static void rmsnorm_row(const uint16_t *x, const uint16_t *gamma, float eps, int D,
+                        unsigned flags, uint16_t *out)
+{
+    float ss = 0.0f;
+    for (int d = 0; d < D; ++d) {
+        float v = orc_bf16_to_f32(x[d]);
+        float sq = v * v;
+        if (flags & 1u) sq = orc_bf16_to_f32(orc_f32_to_bf16(sq));
+        ss = ss + sq;
+    }
+    float mean = ss / (float)D;
+    float arg = mean + eps;
+    float inv = (float)(1.0 / sqrt((double)arg));
+    for (int d = 0; d < D; ++d) {
+        float v = orc_bf16_to_f32(x[d]) * inv;
+        v = v * orc_bf16_to_f32(gamma[d]);
+        out[d] = orc_f32_to_bf16(v);
+    }
+}
+
+/* The routed sum of one token into h (bf16): fp32 fma over the held slots in
+ * slot order, then + shared, one bf16 rounding. Returns ORC_BAD on a row
+ * index >= rows. */
+static int finalize_sum_row(const uint16_t *y, long long rows, const void *w,
+                            const int *row_of_pair, const uint16_t *shared, int t,
+                            int K, int D, unsigned flags, uint16_t *h)
+{
+    for (int k = 0; k < K; ++k)
+        if (row_of_pair[(long long)t * K + k] >= rows) return ORC_BAD;
+    for (int d = 0; d < D; ++d) {
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            long long r = row_of_pair[(long long)t * K + k];
+            if (r < 0) continue;
+            float wk = (flags & 2u)
+                           ? orc_bf16_to_f32(((const uint16_t *)w)[(long long)t * K + k])
+                           : ((const float *)w)[(long long)t * K + k];
+            acc = fmaf(wk, orc_bf16_to_f32(y[r * D + d]), acc);
+        }
+        if (shared) acc = acc + orc_bf16_to_f32(shared[(long long)t * D + d]);
+        h[d] = orc_f32_to_bf16(acc);
+    }
+    return ORC_OK;
+}
+
+int orc_finalize_rmsnorm(const uint16_t *y, long long rows, const void *w,
                          const int *row_of_pair, const uint16_t *shared,
                          const uint16_t *gamma, float eps, int T, int K, int D,
                          unsigned flags, uint16_t *out, uint8_t *mx_codes,
@@ -554,45 +642,91 @@ int orc_finalize_rmsnorm(const uint16_t *y, long long rows, const float *w,
     if (T < 0 || K < 1 || D < 1) return ORC_BAD;
     if ((mx_codes == NULL) != (mx_scales == NULL)) return ORC_BAD;
     if (mx_codes && D % 32 != 0) return ORC_BAD;
+    int swizzled = (flags & 4u) != 0;
+    if (swizzled && (!mx_codes || D % 128 != 0)) return ORC_BAD;
+    uint8_t *rm_scales = NULL;
+    if (swizzled) rm_scales = (uint8_t *)malloc((size_t)T * (size_t)(D / 32) + 1);
     uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)D);
     for (int t = 0; t < T; ++t) {
-        for (int k = 0; k < K; ++k) {
-            long long r = row_of_pair[(long long)t * K + k];
-            if (r >= rows) { free(h); return ORC_BAD; }
+        if (finalize_sum_row(y, rows, w, row_of_pair, shared, t, K, D, flags, h) != ORC_OK) {
+            free(h);
+            if (rm_scales) free(rm_scales);
+            return ORC_BAD;
         }
-        for (int d = 0; d < D; ++d) {
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k) {
-                long long r = row_of_pair[(long long)t * K + k];
-                if (r < 0) continue;
-                acc = fmaf(w[(long long)t * K + k],
-                           orc_bf16_to_f32(y[r * D + d]), acc);
-            }
-            if (shared) acc = acc + orc_bf16_to_f32(shared[(long long)t * D + d]);
-            h[d] = orc_f32_to_bf16(acc);
-        }
-        float ss = 0.0f;
-        for (int d = 0; d < D; ++d) {
-            float hv = orc_bf16_to_f32(h[d]);
-            float sq = hv * hv;
-            if (flags & 1u) sq = orc_bf16_to_f32(orc_f32_to_bf16(sq));
-            ss = ss + sq;
-        }
-        float mean = ss / (float)D;
-        float arg = mean + eps;
-        float inv = (float)(1.0 / sqrt((double)arg));
         uint16_t *o = out + (long long)t * D;
-        for (int d = 0; d < D; ++d) {
-            float v = orc_bf16_to_f32(h[d]) * inv;
-            v = v * orc_bf16_to_f32(gamma[d]);
-            o[d] = orc_f32_to_bf16(v);
-        }
+        rmsnorm_row(h, gamma, eps, D, flags, o);
         if (mx_codes)
             orc_mxfp8_quantize(o, 1, D, mx_codes + (long long)t * D,
-                               mx_scales + (long long)t * (D / 32));
+                               (swizzled ? rm_scales : mx_scales) + (long long)t * (D / 32));
+    }
+    if (swizzled) {
+        orc_mxfp8_swizzle(rm_scales, T, D / 32, mx_scales);
+        free(rm_scales);
     }
     free(h);
     return ORC_OK;
+}
+
+/* [MH] AllReduceMHC.finalize with _LamportMHCDeviceKernel's mHC post-mix and
+ * collapse, on one GPU (the tensor-parallel all-reduce is the identity, so
+ * the reduced bf16 value is the finalize sum h of orc_finalize_rmsnorm).
+ * Per token t and stream target j (hc streams):
+ *   mixed = h * post[t][j]; for each source stream s in order:
+ *       mixed = fma(residual[t][s], comb[t][s][j], mixed)
+ *   residual_out[t][j] = bf16(mixed)
+ *   collapse = fma(f32(residual_out[t][j]), pre[t][j], collapse)  (j in order)
+ * then prenorm = bf16(collapse) is RMS-normalised into out (+ MXFP8) as in
+ * orc_finalize_rmsnorm. comb is indexed [source][target]. Reading: each
+ * "a + b * c" accumulation of the page is one fused multiply-add. With
+ * pre == NULL only residual_out is written (gamma, out, MXFP8 unused). */
+int orc_finalize_mhc(const uint16_t *y, long long rows, const void *w,
+                     const int *row_of_pair, const uint16_t *shared,
+                     const uint16_t *residual /* [T, hc, D] */, const float *post /* [T, hc] */,
+                     const float *comb /* [T, hc, hc] */, const float *pre /* [T, hc] */,
+                     const uint16_t *gamma, float eps, int T, int K, int D, int hc,
+                     unsigned flags, uint16_t *residual_out /* [T, hc, D] */,
+                     uint16_t *out, uint8_t *mx_codes, uint8_t *mx_scales)
+{
+    if (T < 0 || K < 1 || D < 1 || hc < 1) return ORC_BAD;
+    if ((mx_codes == NULL) != (mx_scales == NULL)) return ORC_BAD;
+    if (mx_codes && (D % 32 != 0 || pre == NULL)) return ORC_BAD;
+    if (pre && (gamma == NULL || out == NULL)) return ORC_BAD;
+    int swizzled = (flags & 4u) != 0;
+    if (swizzled && (!mx_codes || D % 128 != 0)) return ORC_BAD;
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)D);
+    uint16_t *pn = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)D);
+    uint8_t *rm_scales = swizzled ? (uint8_t *)malloc((size_t)T * (size_t)(D / 32) + 1) : NULL;
+    int rc = ORC_OK;
+    for (int t = 0; t < T && rc == ORC_OK; ++t) {
+        rc = finalize_sum_row(y, rows, w, row_of_pair, shared, t, K, D, flags, h);
+        if (rc != ORC_OK) break;
+        for (int d = 0; d < D; ++d) {
+            float hv = orc_bf16_to_f32(h[d]);
+            float collapse = 0.0f;
+            for (int j = 0; j < hc; ++j) {
+                float mixed = hv * post[(long long)t * hc + j];
+                for (int src = 0; src < hc; ++src) {
+                    float rv = orc_bf16_to_f32(residual[((long long)t * hc + src) * D + d]);
+                    mixed = fmaf(rv, comb[((long long)t * hc + src) * hc + j], mixed);
+                }
+                uint16_t mb = orc_f32_to_bf16(mixed);
+                residual_out[((long long)t * hc + j) * D + d] = mb;
+                if (pre) collapse = fmaf(orc_bf16_to_f32(mb), pre[(long long)t * hc + j], collapse);
+            }
+            pn[d] = orc_f32_to_bf16(collapse);
+        }
+        if (!pre) continue;
+        uint16_t *o = out + (long long)t * D;
+        rmsnorm_row(pn, gamma, eps, D, flags, o);
+        if (mx_codes)
+            orc_mxfp8_quantize(o, 1, D, mx_codes + (long long)t * D,
+                               (swizzled ? rm_scales : mx_scales) + (long long)t * (D / 32));
+    }
+    if (rc == ORC_OK && swizzled) orc_mxfp8_swizzle(rm_scales, T, D / 32, mx_scales);
+    if (rm_scales) free(rm_scales);
+    free(pn);
+    free(h);
+    return rc;
 }
 
 /* Element-wise helpers over arrays, exported so that the tests can run the
