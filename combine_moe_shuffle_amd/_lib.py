@@ -44,8 +44,11 @@ SIGNATURES = {
                                         _i64, _p, _p, _sz, _p]),
     "moe_split_shuffling": (_status, [_p, _i64, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32,
                                       _i64, _p, _p, _sz, _p]),
+    "moe_mxfp8_scale_bytes": (_sz, [_i32, _i32, _u32]),
     "moe_finalize_rmsnorm": (_status, [_p, _i64, _p, _p, _p, _p, _f32, _i32, _i32, _i32, _u32,
                                        _p, _p, _p, _p]),
+    "moe_finalize_mhc": (_status, [_p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _f32, _i32, _i32,
+                                   _i32, _i32, _u32, _p, _p, _p, _p, _p]),
     "moe_convert_check": (_status, [_p, _i64, _p, _p, _p]),
 }
 

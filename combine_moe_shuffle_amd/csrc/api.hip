@@ -34,7 +34,9 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxQuantD = 65536;     // 16 waves * 64 lanes * 8 chunks * 8
-constexpr int kMaxFinalizeD = 65536;  // same bound for the finalize workgroup
+constexpr int kMaxFinalizeD = 65536;
+constexpr int kMaxMhcD = 32768;      // 16 waves x 64 lanes x 4 chunks x 8
+constexpr int kMaxMhcStreams = 4;  // same bound for the finalize workgroup
 
 #define REQUIRE(cond, status, ...) \
   do {                             \
@@ -325,8 +327,15 @@ moe_status_t moe_split_shuffling(const moe_bf16_t* in, int64_t in_rows, moe_bf16
                    rank_stride, out_counts, workspace, workspace_bytes, stream);
 }
 
+size_t moe_mxfp8_scale_bytes(int32_t M, int32_t D, uint32_t flags) {
+  if (M < 0 || D < 0) return 0;
+  const size_t cols = static_cast<size_t>(D) / 32;
+  if (!(flags & MOE_FINALIZE_MX_SWIZZLED)) return static_cast<size_t>(M) * cols;
+  return (static_cast<size_t>(M) + 127) / 128 * 128 * ((cols + 3) / 4 * 4);
+}
+
 moe_status_t moe_finalize_rmsnorm(const moe_bf16_t* y_permuted, int64_t rows,
-                                  const float* expert_weights, const int32_t* row_of_pair,
+                                  const void* expert_weights, const int32_t* row_of_pair,
                                   const moe_bf16_t* shared, const moe_bf16_t* gamma, float eps,
                                   int32_t T, int32_t K, int32_t D, uint32_t flags,
                                   moe_bf16_t* out, uint8_t* mx_codes, uint8_t* mx_scales,
@@ -334,11 +343,14 @@ moe_status_t moe_finalize_rmsnorm(const moe_bf16_t* y_permuted, int64_t rows,
   REQUIRE(T >= 0 && rows >= 0, MOE_ERR_INVALID_ARG, "T and rows must be >= 0");
   REQUIRE(K >= 1, MOE_ERR_INVALID_ARG, "K must be >= 1 (got %d)", K);
   REQUIRE(K <= kMaxK, MOE_ERR_UNSUPPORTED, "K > %d is not supported (got %d)", kMaxK, K);
-  REQUIRE((flags & ~MOE_FINALIZE_BF16_SQUARES) == 0, MOE_ERR_INVALID_ARG,
-          "unknown flags 0x%x", flags);
+  constexpr uint32_t kKnown =
+      MOE_FINALIZE_BF16_SQUARES | MOE_FINALIZE_BF16_WEIGHTS | MOE_FINALIZE_MX_SWIZZLED;
+  REQUIRE((flags & ~kKnown) == 0, MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   REQUIRE((mx_codes == nullptr) == (mx_scales == nullptr), MOE_ERR_INVALID_ARG,
           "mx_codes and mx_scales must both be NULL or both be set");
-  moe_status_t s = check_rows(D, mx_codes ? 32 : 8);
+  REQUIRE(!(flags & MOE_FINALIZE_MX_SWIZZLED) || mx_codes != nullptr, MOE_ERR_INVALID_ARG,
+          "the swizzled scale layout needs MXFP8 outputs");
+  moe_status_t s = check_rows(D, (flags & MOE_FINALIZE_MX_SWIZZLED) ? 128 : (mx_codes ? 32 : 8));
   if (s != MOE_OK) return s;
   REQUIRE(D <= kMaxFinalizeD, MOE_ERR_UNSUPPORTED, "D > %d is not supported (got %d)",
           kMaxFinalizeD, D);
@@ -349,13 +361,61 @@ moe_status_t moe_finalize_rmsnorm(const moe_bf16_t* y_permuted, int64_t rows,
   REQUIRE(aligned(y_permuted, 16) && aligned(gamma, 16) && aligned(out, 16) &&
               aligned(shared, 16) && aligned(mx_codes, 16),
           MOE_ERR_INVALID_ARG, "row buffers must be 16-byte aligned");
-  REQUIRE(aligned(expert_weights, 4) && aligned(row_of_pair, 4), MOE_ERR_INVALID_ARG,
-          "expert_weights / row_of_pair must be 4-byte aligned");
+  REQUIRE(aligned(expert_weights, (flags & MOE_FINALIZE_BF16_WEIGHTS) ? 2 : 4) &&
+              aligned(row_of_pair, 4),
+          MOE_ERR_INVALID_ARG, "expert_weights / row_of_pair misaligned");
   return hip_status(moe::launch_finalize_rmsnorm(y_permuted, rows, expert_weights, row_of_pair,
                                                  shared, gamma, eps, T, K, D, flags, out,
                                                  mx_codes, mx_scales,
                                                  static_cast<hipStream_t>(stream)),
                     "moe_finalize_rmsnorm");
+}
+
+moe_status_t moe_finalize_mhc(const moe_bf16_t* y_permuted, int64_t rows,
+                              const void* expert_weights, const int32_t* row_of_pair,
+                              const moe_bf16_t* shared, const moe_bf16_t* residual,
+                              const float* post, const float* comb, const float* pre,
+                              const moe_bf16_t* gamma, float eps, int32_t T, int32_t K, int32_t D,
+                              int32_t hc, uint32_t flags, moe_bf16_t* residual_out,
+                              moe_bf16_t* out, uint8_t* mx_codes, uint8_t* mx_scales,
+                              void* stream) {
+  REQUIRE(T >= 0 && rows >= 0, MOE_ERR_INVALID_ARG, "T and rows must be >= 0");
+  REQUIRE(K >= 1, MOE_ERR_INVALID_ARG, "K must be >= 1 (got %d)", K);
+  REQUIRE(K <= kMaxK, MOE_ERR_UNSUPPORTED, "K > %d is not supported (got %d)", kMaxK, K);
+  REQUIRE(hc >= 1, MOE_ERR_INVALID_ARG, "hc must be >= 1 (got %d)", hc);
+  REQUIRE(hc <= kMaxMhcStreams, MOE_ERR_UNSUPPORTED, "hc > %d is not supported (got %d)",
+          kMaxMhcStreams, hc);
+  constexpr uint32_t kKnown =
+      MOE_FINALIZE_BF16_SQUARES | MOE_FINALIZE_BF16_WEIGHTS | MOE_FINALIZE_MX_SWIZZLED;
+  REQUIRE((flags & ~kKnown) == 0, MOE_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  REQUIRE((mx_codes == nullptr) == (mx_scales == nullptr), MOE_ERR_INVALID_ARG,
+          "mx_codes and mx_scales must both be NULL or both be set");
+  REQUIRE(pre != nullptr || (mx_codes == nullptr && out == nullptr), MOE_ERR_INVALID_ARG,
+          "without pre (residual only) out and the MXFP8 outputs must be NULL");
+  REQUIRE(!(flags & MOE_FINALIZE_MX_SWIZZLED) || mx_codes != nullptr, MOE_ERR_INVALID_ARG,
+          "the swizzled scale layout needs MXFP8 outputs");
+  moe_status_t s = check_rows(D, (flags & MOE_FINALIZE_MX_SWIZZLED) ? 128 : (mx_codes ? 32 : 8));
+  if (s != MOE_OK) return s;
+  REQUIRE(D <= kMaxMhcD, MOE_ERR_UNSUPPORTED, "D > %d is not supported (got %d)", kMaxMhcD, D);
+  if (T == 0 || D == 0) return ok();
+  REQUIRE(expert_weights && row_of_pair && residual && post && comb && residual_out,
+          MOE_ERR_INVALID_ARG, "a required pointer is NULL");
+  REQUIRE(pre == nullptr || (gamma != nullptr && out != nullptr), MOE_ERR_INVALID_ARG,
+          "gamma and out are required with pre");
+  REQUIRE(y_permuted != nullptr || rows == 0, MOE_ERR_INVALID_ARG, "y_permuted is NULL");
+  REQUIRE(aligned(y_permuted, 16) && aligned(gamma, 16) && aligned(out, 16) &&
+              aligned(shared, 16) && aligned(mx_codes, 16) && aligned(residual, 16) &&
+              aligned(residual_out, 16),
+          MOE_ERR_INVALID_ARG, "row buffers must be 16-byte aligned");
+  REQUIRE(aligned(expert_weights, (flags & MOE_FINALIZE_BF16_WEIGHTS) ? 2 : 4) &&
+              aligned(row_of_pair, 4) && aligned(post, 4) && aligned(comb, 4) &&
+              aligned(pre, 4),
+          MOE_ERR_INVALID_ARG, "weights, row_of_pair or mix coefficients misaligned");
+  return hip_status(moe::launch_finalize_mhc(y_permuted, rows, expert_weights, row_of_pair,
+                                             shared, residual, post, comb, pre, gamma, eps, T,
+                                             K, D, hc, flags, residual_out, out, mx_codes,
+                                             mx_scales, static_cast<hipStream_t>(stream)),
+                    "moe_finalize_mhc");
 }
 
 moe_status_t moe_convert_check(const float* in, int64_t n, moe_bf16_t* bf16_out,

@@ -98,50 +98,43 @@ __device__ __forceinline__ void fma_slots(float (&acc)[CPL][8], const u32x4 (&bu
   }
 }
 
-// FULL: every wave's slice lies inside the row (D == waves * 64 * CPL * 8),
-// so no chunk needs a bounds test and loads/stores are straight-line code.
-// G: expert rows in flight per group (>= K where possible: one group).
-template <int CPL, int G, bool MX, bool FULL>
-__global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
-    const uint16_t* __restrict__ y, int64_t rows, const float* __restrict__ w,
-    const int* __restrict__ rop, const uint16_t* __restrict__ shared,
-    const uint16_t* __restrict__ gamma, float eps, int K, int D, uint32_t flags,
-    uint16_t* __restrict__ out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ float wave_ss[kMaxWaves];
+// Byte offset of MXFP8 scale (row m, block column k) in the swizzled layout:
+// 128-row x 4-column tiles of 512 bytes, row-tile-major; inside a tile, row m
+// and column k at (m % 32) * 16 + ((m % 128) / 32) * 4 + (k % 4).
+__device__ __forceinline__ int64_t swizzled_scale_offset(int m, int k, int cols) {
+  const int64_t tile = static_cast<int64_t>(m >> 7) * ((cols + 3) >> 2) + (k >> 2);
+  return tile * 512 + (m & 31) * 16 + ((m & 127) >> 5) * 4 + (k & 3);
+}
 
-  const int t = blockIdx.x;
-  const int lane = lane_id();
-  const int wave = uniform(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int nch = D >> 3;
-  const int base = wave * kWave * CPL + lane;
-
-  // lane k holds slot k (K <= 64): its row (or -1) and weight
-  int my_r = -1;
-  float my_w = 0.0f;
+// Per-token set-up shared by both kernels: lane k holds slot k (K <= 64), its
+// permuted row (or -1) and its weight (fp32, or bf16 widened exactly with
+// flags bit 1). A row >= rows is out of range and treated as not held.
+__device__ __forceinline__ void load_pairs(int t, int K, int64_t rows, const void* w,
+                                           const int* __restrict__ rop, uint32_t flags,
+                                           int lane, int& my_r, float& my_w) {
+  my_r = -1;
+  my_w = 0.0f;
   if (lane < K) {
-    my_r = rop[static_cast<int64_t>(t) * K + lane];
-    my_w = w[static_cast<int64_t>(t) * K + lane];
-    if (my_r >= rows) my_r = -1;  // out of range: treated as not held
+    const int64_t i = static_cast<int64_t>(t) * K + lane;
+    my_r = rop[i];
+    my_w = (flags & 2u) ? bf16_lo(static_cast<const uint16_t*>(w)[i])
+                        : static_cast<const float*>(w)[i];
+    if (my_r >= rows) my_r = -1;
   }
+}
 
+// h = bf16(sum over held slots of w_k * y[r_k] (fp32 fma, slot order)
+// [+ shared]) for this lane's chunks; sh holds the shared row's chunks.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void routed_sum(u32x4 (&h)[CPL], const u32x4 (&sh)[CPL],
+                                           bool has_shared, const uint16_t* __restrict__ y,
+                                           int D, int nch, int base, int lane, int K, int my_r,
+                                           float my_w) {
   float acc[CPL][8];
 #pragma unroll
   for (int j = 0; j < CPL; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
-
-  // shared output and gamma are independent of the slot loop: issue early
-  u32x4 sh[CPL], gm[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = base + j * kWave;
-    if (FULL || c < nch) {
-      if (shared) sh[j] = ld16_stream(shared + static_cast<int64_t>(t) * D + c * kChunk);
-      gm[j] = ld16(gamma + c * kChunk);
-    }
-  }
-
   const uint64_t held = __ballot(lane < K && my_r >= 0);
   if (held != 0) {
     const int safe = __builtin_amdgcn_readlane(my_r, __builtin_ctzll(held));
@@ -153,23 +146,40 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
       fma_slots<CPL, G, FULL>(acc, buf, nch, base, my_r, my_w, K, k0);
     }
   }
-
-  // h = bf16(acc [+ shared]); keep h as packed bf16 and its square sum
-  u32x4 h[CPL];
-  float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = base + j * kWave;
     if (FULL || c < nch) {
-      if (shared) {
+      if (has_shared) {
         float f[8];
         unpack8(sh[j], f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
       }
       h[j] = pack8(acc[j]);
+    }
+  }
+}
+
+// RMSNorm of the bf16 row x (this lane's chunks) and its optional MXFP8:
+// ss in fp32 (flags bit 0: squares rounded to bf16), lane tree then waves in
+// order through LDS; inv = correctly rounded 1/sqrt(ss/D + eps);
+// out = bf16((x * inv) * gamma); MXFP8 of the bf16 output.
+template <int CPL, bool MX, bool FULL>
+__device__ __forceinline__ void norm_out(const u32x4 (&x)[CPL], const u32x4 (&gm)[CPL],
+                                         float* wave_ss, int t, int D, int nch, int base,
+                                         int lane, int wave, int nwaves, float eps,
+                                         uint32_t flags, uint16_t* __restrict__ out,
+                                         uint8_t* __restrict__ codes,
+                                         uint8_t* __restrict__ scales) {
+  const int cols = D >> 5;
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) {
       float hf[8];
-      unpack8(h[j], hf);
+      unpack8(x[j], hf);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float sq = hf[i] * hf[i];
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     float hf[8], g[8], o[8];
-    unpack8(h[j], hf);
+    unpack8(x[j], hf);
     unpack8(gm[j], g);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = (hf[i] * inv) * g[i];
@@ -232,11 +242,162 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
       const int c = base + j * kWave;
       if (FULL || c < nch) {
         st8_stream(codes + static_cast<int64_t>(t) * D + c * kChunk, cw[j]);
-        if ((lane & 3) == 0)
-          scales[static_cast<int64_t>(t) * (D >> 5) + (c >> 2)] = static_cast<uint8_t>(bytes[j]);
+        if ((lane & 3) == 0) {
+          const int64_t so = (flags & 4u) ? swizzled_scale_offset(t, c >> 2, cols)
+                                          : static_cast<int64_t>(t) * cols + (c >> 2);
+          scales[so] = static_cast<uint8_t>(bytes[j]);
+        }
       }
     }
   }
+}
+
+// Workgroup T + i (swizzled scales only) zeroes padding row T + i's scales.
+__device__ __forceinline__ void zero_pad_scales(int t, int cols, uint8_t* __restrict__ scales) {
+  for (int k = threadIdx.x; k < cols; k += blockDim.x)
+    scales[swizzled_scale_offset(t, k, cols)] = 0;
+}
+
+// FULL: every wave's slice lies inside the row (D == waves * 64 * CPL * 8),
+// so no chunk needs a bounds test and loads/stores are straight-line code.
+// G: expert rows in flight per group (>= K where possible: one group).
+template <int CPL, int G, bool MX, bool FULL>
+__global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
+    const uint16_t* __restrict__ y, int64_t rows, const void* __restrict__ w,
+    const int* __restrict__ rop, const uint16_t* __restrict__ shared,
+    const uint16_t* __restrict__ gamma, float eps, int T, int K, int D, uint32_t flags,
+    uint16_t* __restrict__ out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ float wave_ss[kMaxWaves];
+
+  const int t = blockIdx.x;
+  if (t >= T) {
+    if constexpr (MX) zero_pad_scales(t, D >> 5, scales);
+    return;
+  }
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int nch = D >> 3;
+  const int base = wave * kWave * CPL + lane;
+
+  int my_r;
+  float my_w;
+  load_pairs(t, K, rows, w, rop, flags, lane, my_r, my_w);
+
+  // shared output and gamma are independent of the slot loop: issue early
+  u32x4 sh[CPL], gm[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) {
+      if (shared) sh[j] = ld16_stream(shared + static_cast<int64_t>(t) * D + c * kChunk);
+      gm[j] = ld16(gamma + c * kChunk);
+    }
+  }
+
+  u32x4 h[CPL];
+  routed_sum<CPL, G, FULL>(h, sh, shared != nullptr, y, D, nch, base, lane, K, my_r, my_w);
+  norm_out<CPL, MX, FULL>(h, gm, wave_ss, t, D, nch, base, lane, wave, nwaves, eps, flags, out,
+                          codes, scales);
+}
+
+// The mHC tail ([MH] _LamportMHCDeviceKernel) after the routed sum h:
+//   for each target stream j: mixed = h * post[t][j], then for each source
+//   stream s in order mixed = fma(residual[t][s], comb[t][s][j], mixed);
+//   residual_out[t][j] = bf16(mixed); collapse = fma(bf16 mixed, pre[t][j],
+//   collapse) over j in order; prenorm = bf16(collapse) goes through the same
+//   RMSNorm (+ MXFP8). NORM = false (pre == NULL): only residual_out.
+// comb is [source][target]. The mixing coefficients are per token, so every
+// lane of the workgroup reads the same ones (scalar loads).
+template <int CPL, int G, int HC, bool MX, bool FULL, bool NORM>
+__global__ __launch_bounds__(kMaxWaves* kWave) void finalize_mhc_kernel(
+    const uint16_t* __restrict__ y, int64_t rows, const void* __restrict__ w,
+    const int* __restrict__ rop, const uint16_t* __restrict__ shared,
+    const uint16_t* __restrict__ residual, const float* __restrict__ post,
+    const float* __restrict__ comb, const float* __restrict__ pre,
+    const uint16_t* __restrict__ gamma, float eps, int T, int K, int D, uint32_t flags,
+    uint16_t* __restrict__ residual_out, uint16_t* __restrict__ out,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  __shared__ float wave_ss[kMaxWaves];
+
+  const int t = blockIdx.x;
+  if (t >= T) {
+    if constexpr (MX) zero_pad_scales(t, D >> 5, scales);
+    return;
+  }
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int nch = D >> 3;
+  const int base = wave * kWave * CPL + lane;
+
+  int my_r;
+  float my_w;
+  load_pairs(t, K, rows, w, rop, flags, lane, my_r, my_w);
+
+  // shared, gamma and the hc residual streams do not depend on the slots
+  u32x4 sh[CPL], gm[CPL], rs[HC][CPL];
+  const uint16_t* rrow = residual + static_cast<int64_t>(t) * HC * D;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) {
+      if (shared) sh[j] = ld16_stream(shared + static_cast<int64_t>(t) * D + c * kChunk);
+      if constexpr (NORM) gm[j] = ld16(gamma + c * kChunk);
+#pragma unroll
+      for (int s = 0; s < HC; ++s)
+        rs[s][j] = ld16_stream(rrow + static_cast<int64_t>(s) * D + c * kChunk);
+    }
+  }
+  float pm[HC], cm[HC][HC], qm[HC];
+#pragma unroll
+  for (int a = 0; a < HC; ++a) {
+    pm[a] = post[static_cast<int64_t>(t) * HC + a];
+    if constexpr (NORM) qm[a] = pre[static_cast<int64_t>(t) * HC + a];
+#pragma unroll
+    for (int b = 0; b < HC; ++b) cm[a][b] = comb[(static_cast<int64_t>(t) * HC + a) * HC + b];
+  }
+
+  u32x4 h[CPL];
+  routed_sum<CPL, G, FULL>(h, sh, shared != nullptr, y, D, nch, base, lane, K, my_r, my_w);
+
+  uint16_t* orow = residual_out + static_cast<int64_t>(t) * HC * D;
+  u32x4 pn[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) {
+      float hf[8], rf[HC][8], col[8];
+      unpack8(h[j], hf);
+#pragma unroll
+      for (int s = 0; s < HC; ++s) unpack8(rs[s][j], rf[s]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) col[i] = 0.0f;
+#pragma unroll
+      for (int tg = 0; tg < HC; ++tg) {
+        float mx[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float m = hf[i] * pm[tg];
+#pragma unroll
+          for (int s = 0; s < HC; ++s) m = __builtin_fmaf(rf[s][i], cm[s][tg], m);
+          mx[i] = m;
+        }
+        const u32x4 mb = pack8(mx);
+        st16_stream(orow + static_cast<int64_t>(tg) * D + c * kChunk, mb);
+        if constexpr (NORM) {
+          float mf[8];
+          unpack8(mb, mf);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) col[i] = __builtin_fmaf(mf[i], qm[tg], col[i]);
+        }
+      }
+      if constexpr (NORM) pn[j] = pack8(col);
+    }
+  }
+  if constexpr (NORM)
+    norm_out<CPL, MX, FULL>(pn, gm, wave_ss, t, D, nch, base, lane, wave, nwaves, eps, flags,
+                            out, codes, scales);
 }
 
 // fp32 -> bf16 and fp32 -> E4M3 (after the +-448 clamp) through the same
@@ -255,7 +416,7 @@ __global__ void convert_kernel(const float* __restrict__ in, int64_t n,
 
 }  // namespace
 
-hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float* w,
+hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const void* w,
                                    const int* row_of_pair, const uint16_t* shared,
                                    const uint16_t* gamma, float eps, int T, int K, int D,
                                    uint32_t flags, uint16_t* out, uint8_t* mx_codes,
@@ -267,7 +428,10 @@ hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float*
   static const int large_t[] = {2, 4, 8, 1};
   const SliceShape sh = T < 2048 ? pick_slices(nch, small_t, 4, kMaxWaves)
                                   : pick_slices(nch, large_t, 4, kMaxWaves);
-  const dim3 grid(static_cast<unsigned>(T));
+  // with swizzled MXFP8 scales, one more workgroup per padding row (up to a
+  // multiple of 128 rows) zeroes that row's scales
+  const int pad_rows = (mx_codes && (flags & 4u)) ? (T + 127) / 128 * 128 - T : 0;
+  const dim3 grid(static_cast<unsigned>(T + pad_rows));
   const dim3 block(sh.nsl * kWave);
   const bool mx = mx_codes != nullptr;
   const bool full = sh.nsl * kWave * sh.cpl == nch;
@@ -276,7 +440,7 @@ hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float*
   const int gk = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 ? 4 : 8));
 #define L4(C, GV, M, F)                                                                      \
   hipLaunchKernelGGL((finalize_kernel<C, GV, M, F>), grid, block, 0, stream, y, rows, w,      \
-                     row_of_pair, shared, gamma, eps, K, D, flags, out, mx_codes, mx_scales)
+                     row_of_pair, shared, gamma, eps, T, K, D, flags, out, mx_codes, mx_scales)
 #define L3(C, GV)                        \
   do {                                   \
     if (mx && full) L4(C, GV, true, true);       \
@@ -302,6 +466,70 @@ hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float*
 #undef L
 #undef L3
 #undef L4
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_mhc(const uint16_t* y, int64_t rows, const void* w,
+                               const int* row_of_pair, const uint16_t* shared,
+                               const uint16_t* residual, const float* post, const float* comb,
+                               const float* pre, const uint16_t* gamma, float eps, int T, int K,
+                               int D, int hc, uint32_t flags, uint16_t* residual_out,
+                               uint16_t* out, uint8_t* mx_codes, uint8_t* mx_scales,
+                               hipStream_t stream) {
+  // one chunk per lane where the row fits 16 waves (the hc streams take
+  // registers), else two or four
+  const int nch = D / kChunk;
+  static const int allowed[] = {1, 2, 4};
+  const SliceShape sh = pick_slices(nch, allowed, 3, kMaxWaves);
+  const bool norm = pre != nullptr;
+  const bool mx = norm && mx_codes != nullptr;
+  const int pad_rows = (mx && (flags & 4u)) ? (T + 127) / 128 * 128 - T : 0;
+  const dim3 grid(static_cast<unsigned>(T + pad_rows));
+  const dim3 block(sh.nsl * kWave);
+  const bool full = sh.nsl * kWave * sh.cpl == nch;
+  // rows in flight per group: as for the plain finalize, with G * cpl <= 8
+  // (the hc residual streams hold registers too)
+  const int gk = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 ? 4 : 8));
+#define L6(C, GV, H, M, F, N)                                                                 \
+  hipLaunchKernelGGL((finalize_mhc_kernel<C, GV, H, M, F, N>), grid, block, 0, stream, y,     \
+                     rows, w, row_of_pair, shared, residual, post, comb, pre, gamma, eps, T, K, \
+                     D, flags, residual_out, out, mx_codes, mx_scales)
+#define L5(C, GV, H)                                \
+  do {                                              \
+    if (!norm && full) L6(C, GV, H, false, true, false);  \
+    else if (!norm) L6(C, GV, H, false, false, false);    \
+    else if (mx && full) L6(C, GV, H, true, true, true);  \
+    else if (mx) L6(C, GV, H, true, false, true);         \
+    else if (full) L6(C, GV, H, false, true, true);       \
+    else L6(C, GV, H, false, false, true);                \
+  } while (0)
+#define L4(C, GV)                    \
+  do {                               \
+    switch (hc) {                    \
+      case 1: L5(C, GV, 1); break;   \
+      case 2: L5(C, GV, 2); break;   \
+      case 3: L5(C, GV, 3); break;   \
+      default: L5(C, GV, 4); break;  \
+    }                                \
+  } while (0)
+#define L(C)                                                  \
+  do {                                                        \
+    constexpr int gmax = 8 / (C);                             \
+    const int g = gk < gmax ? gk : gmax;                      \
+    if (g == 1) L4(C, 1);                                     \
+    else if (g == 2) L4(C, 2);                                \
+    else if (g == 4) L4(C, (gmax >= 4 ? 4 : 2));              \
+    else L4(C, (gmax >= 8 ? 8 : 2));                          \
+  } while (0)
+  switch (sh.cpl) {
+    case 1: L(1); break;
+    case 2: L(2); break;
+    default: L(4); break;
+  }
+#undef L
+#undef L4
+#undef L5
+#undef L6
   return hipGetLastError();
 }
 

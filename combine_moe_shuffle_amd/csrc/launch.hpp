@@ -55,11 +55,18 @@ hipError_t launch_shuffling(bool inverse, const uint16_t* in, int64_t in_rows, u
                             hipStream_t stream);
 
 // finalize.hip
-hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const float* w,
+hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const void* w,
                                    const int* row_of_pair, const uint16_t* shared,
                                    const uint16_t* gamma, float eps, int T, int K, int D,
                                    uint32_t flags, uint16_t* out, uint8_t* mx_codes,
                                    uint8_t* mx_scales, hipStream_t stream);
+hipError_t launch_finalize_mhc(const uint16_t* y, int64_t rows, const void* w,
+                               const int* row_of_pair, const uint16_t* shared,
+                               const uint16_t* residual, const float* post, const float* comb,
+                               const float* pre, const uint16_t* gamma, float eps, int T, int K,
+                               int D, int hc, uint32_t flags, uint16_t* residual_out,
+                               uint16_t* out, uint8_t* mx_codes, uint8_t* mx_scales,
+                               hipStream_t stream);
 hipError_t launch_convert_check(const float* in, int64_t n, uint16_t* bf16_out,
                                 uint8_t* e4m3_out, hipStream_t stream);
 

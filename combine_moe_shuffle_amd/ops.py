@@ -297,40 +297,129 @@ def moe_split_shuffling(tokens, counts, c_lo=None, c_hi=None, rank_stride=None, 
 
 
 # ---------------------------------------------------------------- finalize
-def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma, eps,
-                         flags=0, out=None, mxfp8=False):
-    """Weighted top-k reduction + shared add + RMSNorm (+ MXFP8).
+BF16_SQUARES = 1
+BF16_WEIGHTS = 2
+MX_SWIZZLED = 4
 
-    Returns out (T, D) bf16, or (out, codes (T, D) uint8, scales (T, D/32)
-    uint8) with ``mxfp8``."""
+
+def _finalize_common(y_permuted, expert_weights, row_of_pair, shared, gamma, flags, mxfp8,
+                     scale_layout):
+    """Checks of the finalize inputs shared by both finalize entry points;
+    returns (flags, T, K, rows, D)."""
     device = y_permuted.device
     _need(y_permuted, "y_permuted", torch.bfloat16, 2, device)
-    _need(expert_weights, "expert_weights", torch.float32, 2, device)
+    if expert_weights.dtype == torch.bfloat16:
+        flags |= BF16_WEIGHTS
+        _need(expert_weights, "expert_weights", torch.bfloat16, 2, device)
+    else:
+        _need(expert_weights, "expert_weights", torch.float32, 2, device)
     _need(row_of_pair, "row_of_pair", torch.int32, 2, device)
-    _need(gamma, "gamma", torch.bfloat16, 1, device)
     for t, n in ((y_permuted, "y_permuted"), (expert_weights, "expert_weights"),
-                 (row_of_pair, "row_of_pair"), (gamma, "gamma")):
+                 (row_of_pair, "row_of_pair")):
         _contig(t, n)
+    if scale_layout not in ("rowmajor", "swizzled"):
+        raise ValueError("scale_layout must be 'rowmajor' or 'swizzled'")
+    if scale_layout == "swizzled":
+        if not mxfp8:
+            raise ValueError("the swizzled scale layout needs mxfp8=True")
+        flags |= MX_SWIZZLED
     T, K = row_of_pair.shape
     rows, D = y_permuted.shape
     if tuple(expert_weights.shape) != (T, K):
         raise ValueError("expert_weights must be (T, K) like row_of_pair")
-    if gamma.numel() != D:
-        raise ValueError("gamma must have D entries")
+    if gamma is not None:
+        _need(gamma, "gamma", torch.bfloat16, 1, device)
+        _contig(gamma, "gamma")
+        if gamma.numel() != D:
+            raise ValueError("gamma must have D entries")
     if shared is not None:
         _need(shared, "shared", torch.bfloat16, 2, device)
         _contig(shared, "shared")
         if tuple(shared.shape) != (T, D):
             raise ValueError("shared must be (T, D)")
+    return flags, T, K, rows, D
+
+
+def _mx_outputs(T, D, flags, device):
+    codes = torch.empty((T, D), dtype=torch.uint8, device=device)
+    if flags & MX_SWIZZLED:
+        nbytes = _lib.load().moe_mxfp8_scale_bytes(T, D, flags)
+        scales = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    else:
+        scales = torch.empty((T, D // 32), dtype=torch.uint8, device=device)
+    return codes, scales
+
+
+def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma, eps,
+                         flags=0, out=None, mxfp8=False, scale_layout="rowmajor"):
+    """Weighted top-k reduction + shared add + RMSNorm (+ MXFP8).
+
+    expert_weights may be fp32 or bf16 (the bf16-weight flag is set from the
+    dtype). scale_layout "rowmajor" gives scales (T, D/32); "swizzled" gives
+    the 128x4-tiled byte buffer with zeroed padding rows. Returns out (T, D)
+    bf16, or (out, codes (T, D) uint8, scales uint8) with ``mxfp8``."""
+    if gamma is None:
+        raise ValueError("gamma is required")
+    flags, T, K, rows, D = _finalize_common(y_permuted, expert_weights, row_of_pair, shared,
+                                            gamma, flags, mxfp8, scale_layout)
+    device = y_permuted.device
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
-    codes = torch.empty((T, D), dtype=torch.uint8, device=device) if mxfp8 else None
-    scales = torch.empty((T, D // 32), dtype=torch.uint8, device=device) if mxfp8 else None
+    codes, scales = _mx_outputs(T, D, flags, device) if mxfp8 else (None, None)
     _lib.check(_lib.load().moe_finalize_rmsnorm(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
         _stream()))
     return (out, codes, scales) if mxfp8 else out
+
+
+def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, post, comb,
+                     pre, gamma, eps, flags=0, residual_out=None, out=None, mxfp8=False,
+                     scale_layout="rowmajor"):
+    """The finalize of a hyper-connection layer: routed sum h, mHC post-mix
+    of the hc residual streams, pre-mix collapse, RMSNorm (+ MXFP8).
+
+    residual (T, hc, D) bf16; post (T, hc) or (T, hc, 1) fp32; comb (T, hc, hc)
+    fp32 indexed [source, target]; pre (T, hc) fp32, or None for residual
+    only (then gamma is ignored and no layer input is produced). Returns
+    (residual_out (T, hc, D) bf16, out (T, D) bf16 or None), plus codes and
+    scales with ``mxfp8``."""
+    if pre is None and mxfp8:
+        raise ValueError("residual-only mode has no layer input to quantise")
+    flags, T, K, rows, D = _finalize_common(y_permuted, expert_weights, row_of_pair, shared,
+                                            gamma if pre is not None else None, flags, mxfp8,
+                                            scale_layout)
+    device = y_permuted.device
+    _need(residual, "residual", torch.bfloat16, 3, device)
+    _contig(residual, "residual")
+    hc = residual.shape[1]
+    if tuple(residual.shape) != (T, hc, D):
+        raise ValueError("residual must be (T, hc, D)")
+    for t, n, numel in ((post, "post", T * hc), (comb, "comb", T * hc * hc),
+                        (pre, "pre", T * hc)):
+        if t is None:
+            continue
+        _need(t, n, torch.float32, None, device)
+        _contig(t, n)
+        if t.numel() != numel or t.shape[0] != T:
+            raise ValueError(f"{n} has the wrong shape")
+    if pre is not None and gamma is None:
+        raise ValueError("gamma is required with pre")
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    elif residual_out.data_ptr() == residual.data_ptr():
+        raise ValueError("residual_out must not alias residual")
+    if pre is not None and out is None:
+        out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
+    if pre is None:
+        out = None
+    codes, scales = _mx_outputs(T, D, flags, device) if mxfp8 else (None, None)
+    _lib.check(_lib.load().moe_finalize_mhc(
+        _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
+        _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),
+        _ptr(gamma) if pre is not None else None, float(eps), T, K, D, hc, int(flags),
+        _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream()))
+    return (residual_out, out, codes, scales) if mxfp8 else (residual_out, out)
 
 
 def moe_convert_check(values):

@@ -316,27 +316,75 @@ MOE_API moe_status_t moe_split_shuffling(const moe_bf16_t *in, int64_t in_rows,
  * MXFP8 (mx_codes and mx_scales both set; D % 32 == 0): for each 32-element
  * block j of out[t, :]: amax = max |out|; p = amax * fp32(1/448);
  *   byte = clamp(ceil(log2 p) + 127, 0, 254) (0 when p == 0);
- *   mx_scales[t*(D/32) + j] = byte  (row-major, no padding);
- *   mx_codes[t, 32j+i] = e4m3_rne(clamp(out * 2^(127-byte), -448, 448)).
+ *   mx_codes[t, 32j+i] = e4m3_rne(clamp(out * 2^(127-byte), -448, 448));
+ *   scale layout: row-major mx_scales[t*(D/32) + j], or with
+ *   MOE_FINALIZE_MX_SWIZZLED the 128x4-tiled layout [MH] writes for MXFP8
+ *   GEMMs (its index helper is absent from the pages; the reading here:
+ *   128-row x 4-column tiles of 512 bytes in row-tile-major order, row m and
+ *   column j of a tile at (m%32)*16 + ((m%128)/32)*4 + j%4), with the
+ *   scales of the padding rows up to a multiple of 128 written as zero;
+ *   D % 128 == 0. moe_mxfp8_scale_bytes gives the buffer size of either.
  *
  * y_permuted    [rows, D] bf16 unweighted expert outputs in permuted order
- * expert_weights [T, K] fp32;  row_of_pair [T, K] int32 (-1: slot not held;
- *               values must be < rows)
+ * expert_weights [T, K] fp32, or bf16 with MOE_FINALIZE_BF16_WEIGHTS ([K3]
+ *               reads bf16 weights and widens them exactly)
+ * row_of_pair   [T, K] int32 (-1: slot not held; values must be < rows)
  * shared        [T, D] bf16, nullable;  gamma [D] bf16
  * out           [T, D] bf16;  mx_codes [T, D] uint8 (16-byte aligned) and
- *               mx_scales [T, D/32] uint8: both NULL or both set
- * flags         bit 0: bf16-rounded squares; other bits must be 0
+ *               mx_scales (moe_mxfp8_scale_bytes(T, D, flags) bytes): both
+ *               NULL or both set
+ * flags         MOE_FINALIZE_BF16_SQUARES | MOE_FINALIZE_BF16_WEIGHTS |
+ *               MOE_FINALIZE_MX_SWIZZLED; other bits must be 0
  * D % 8 == 0, D <= 65536; K <= 64.
  * ---------------------------------------------------------------------- */
 #define MOE_FINALIZE_BF16_SQUARES 1u
+#define MOE_FINALIZE_BF16_WEIGHTS 2u
+#define MOE_FINALIZE_MX_SWIZZLED 4u
+MOE_API size_t moe_mxfp8_scale_bytes(int32_t M, int32_t D, uint32_t flags);
 MOE_API moe_status_t moe_finalize_rmsnorm(const moe_bf16_t *y_permuted, int64_t rows,
-                                  const float *expert_weights,
+                                  const void *expert_weights,
                                   const int32_t *row_of_pair,
                                   const moe_bf16_t *shared,
                                   const moe_bf16_t *gamma, float eps, int32_t T,
                                   int32_t K, int32_t D, uint32_t flags,
                                   moe_bf16_t *out, uint8_t *mx_codes,
                                   uint8_t *mx_scales, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_finalize_mhc -- the MoE tail of a hyper-connection (mHC) layer: the
+ * routed sum h of moe_finalize_rmsnorm, mixed into the hc residual streams,
+ * and the normalised collapse of the mixed streams as the next layer input.
+ * [MH] AllReduceMHC.finalize and _LamportMHCDeviceKernel: the consumer's
+ * residual add becomes the mHC post-mix and pre-mix collapse, which the
+ * unchanged RMSNorm normalises; on one GPU the all-reduce is the identity.
+ * Per token t and element d (h as in moe_finalize_rmsnorm, bf16):
+ *   for each target stream j = 0..hc-1:
+ *     mixed = f32(h) * post[t, j]
+ *     for each source stream s = 0..hc-1: mixed = fma(f32(residual[t, s, d]),
+ *                                                      comb[t, s, j], mixed)
+ *     residual_out[t, j, d] = bf16_rne(mixed)
+ *     collapse = fma(f32(residual_out[t, j, d]), pre[t, j], collapse)
+ *   prenorm = bf16_rne(collapse); out[t, :] = RMSNorm of prenorm with gamma
+ *   and eps, and its optional MXFP8, exactly as moe_finalize_rmsnorm does
+ *   for h (same flags). The pages write each "a + b * c" step of the mix and
+ *   the collapse; here each is one fused multiply-add.
+ * Residual only (pre == NULL; out, mx_codes and mx_scales must be NULL,
+ * gamma is ignored): only residual_out is written, for a consumer that
+ * collapses the streams itself.
+ *
+ * residual, residual_out [T, hc, D] bf16 (16-byte aligned; they must not
+ * overlap); post [T, hc] fp32; comb [T, hc, hc] fp32 indexed [source,
+ * target]; pre [T, hc] fp32 or NULL. Other arguments as for
+ * moe_finalize_rmsnorm. 1 <= hc <= 4; D % 8 == 0, D <= 32768; K <= 64.
+ * ---------------------------------------------------------------------- */
+MOE_API moe_status_t moe_finalize_mhc(const moe_bf16_t *y_permuted, int64_t rows,
+                                      const void *expert_weights, const int32_t *row_of_pair,
+                                      const moe_bf16_t *shared, const moe_bf16_t *residual,
+                                      const float *post, const float *comb, const float *pre,
+                                      const moe_bf16_t *gamma, float eps, int32_t T, int32_t K,
+                                      int32_t D, int32_t hc, uint32_t flags,
+                                      moe_bf16_t *residual_out, moe_bf16_t *out,
+                                      uint8_t *mx_codes, uint8_t *mx_scales, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_convert_check -- the device conversions the kernels use, exposed so that

@@ -205,12 +205,51 @@ def test_finalize_rejects(lib):
 
     assert call(mc=FAKE) == INVALID                       # codes without scales
     assert call(mc=FAKE, ms=FAKE, D=264) == INVALID       # D % 32 for MXFP8
-    assert call(flags=2) == INVALID
+    assert call(flags=8) == INVALID                       # unknown bit
+    assert call(flags=4) == INVALID                       # swizzled scales without MXFP8
+    assert call(flags=4, mc=FAKE, ms=FAKE, D=288) == INVALID  # swizzled needs D % 128
+    assert call(flags=2, w=FAKE + 2, T=0) == OK           # bf16 weights: 2-byte alignment
+    assert lib.moe_mxfp8_scale_bytes(130, 512, 0) == 130 * 16
+    assert lib.moe_mxfp8_scale_bytes(130, 512, 4) == 256 * 16
+    assert lib.moe_mxfp8_scale_bytes(1, 128, 4) == 128 * 4
     assert call(K=0) == INVALID
     assert call(K=65) == UNSUPPORTED
     assert call(D=1 << 17) == UNSUPPORTED
     assert call(g=None) == INVALID
     assert call(sh=FAKE + 8) == INVALID
+    assert call(T=0) == OK
+
+
+@host_only
+def test_finalize_mhc_rejects(lib):
+    f = lib.moe_finalize_mhc
+    args = dict(y=FAKE, rows=64, w=FAKE, rop=FAKE, sh=FAKE, res=FAKE, post=FAKE, comb=FAKE,
+                pre=FAKE, g=FAKE, eps=1e-6, T=8, K=8, D=256, hc=4, flags=0, ro=FAKE,
+                out=FAKE, mc=None, ms=None)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["y"], a["rows"], a["w"], a["rop"], a["sh"], a["res"], a["post"], a["comb"],
+                 a["pre"], a["g"], a["eps"], a["T"], a["K"], a["D"], a["hc"], a["flags"],
+                 a["ro"], a["out"], a["mc"], a["ms"], None)
+
+    assert call(hc=0) == INVALID
+    assert call(hc=5) == UNSUPPORTED
+    assert call(pre=None) == INVALID                      # residual only: out must be NULL
+    assert call(pre=None, out=None, mc=FAKE, ms=FAKE) == INVALID  # and no MXFP8
+    assert call(pre=None, out=None, g=None, T=0) == OK
+    assert call(mc=FAKE) == INVALID                       # codes without scales
+    assert call(flags=8) == INVALID
+    assert call(flags=4) == INVALID                       # swizzled scales without MXFP8
+    assert call(D=260) == INVALID                         # D % 8
+    assert call(D=1 << 16) == UNSUPPORTED
+    assert call(K=65) == UNSUPPORTED
+    assert call(res=None) == INVALID
+    assert call(comb=None) == INVALID
+    assert call(ro=None) == INVALID
+    assert call(g=None) == INVALID                        # gamma needed with pre
+    assert call(ro=FAKE + 8) == INVALID                   # 16-byte rows
+    assert call(post=FAKE + 2) == INVALID
     assert call(T=0) == OK
 
 

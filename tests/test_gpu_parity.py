@@ -376,6 +376,84 @@ def test_finalize_rmsnorm(dev, case):
         assert np.array_equal(codes, oc)
 
 
+FIN_VARIANT_CASES = [
+    # (name, T, D, K, holes, bf16 weights, swizzled scales)
+    ("bf16-weights", 40, 1024, 8, 0.1, True, False),
+    ("swizzled-130", 130, 1024, 4, 0.0, False, True),
+    ("swizzled-1", 1, 7168, 8, 0.0, True, True),
+    ("swizzled-256", 256, 512, 2, 0.2, False, True),
+]
+
+
+@pytest.mark.parametrize("case", FIN_VARIANT_CASES, ids=[c[0] for c in FIN_VARIANT_CASES])
+def test_finalize_variants(dev, case):
+    name, T, D, K, holes, bfw, swz = case
+    fi = W.finalize_inputs(W.WORKLOADS["prefill"], T=T, D=D, K=K, hole_frac=holes)
+    flags = (2 if bfw else 0)
+    w = W.to_bf16_bits(fi.w) if bfw else fi.w
+    say("finalize variant", name, T, D, K, bfw, swz)
+    want = orc.finalize_rmsnorm(fi.y, w, fi.row_of_pair, fi.shared, fi.gamma, fi.eps,
+                                flags=flags)
+    wd = bf_dev(w, dev) if bfw else torch.from_numpy(w).to(dev)
+    out, codes, scales = ops.moe_finalize_rmsnorm(
+        bf_dev(fi.y, dev), wd, i32_dev(fi.row_of_pair, dev), bf_dev(fi.shared, dev),
+        bf_dev(fi.gamma, dev), fi.eps, mxfp8=True,
+        scale_layout="swizzled" if swz else "rowmajor")
+    got = bits_host(out)
+    _close(got, want, name)
+    oc, rm = orc.mxfp8_quantize(got)            # split check on the GPU's own output
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    want_scales = orc.mxfp8_swizzle(rm) if swz else rm
+    assert np.array_equal(scales.cpu().numpy(), want_scales)
+
+
+MHC_CASES = [
+    # (name, T, D, K, holes, hc, mode, swizzled, flags)
+    #   mode: "mx" (layer input + MXFP8), "norm" (layer input), "res" (residual only)
+    ("hc4-mx", 40, 1024, 8, 0.1, 4, "mx", False, 0),
+    ("hc4-swizzled-130", 130, 5120, 4, 0.0, 4, "mx", True, 0),
+    ("hc1", 17, 7168, 8, 0.0, 1, "norm", False, 0),
+    ("hc3-ragged", 33, 32 * 49, 3, 0.2, 3, "mx", False, 0),   # partial last wave
+    ("hc2-residual-only", 20, 2048, 2, 0.0, 2, "res", False, 0),
+    ("hc4-wide", 5, 16384 + 8192, 2, 0.0, 4, "norm", False, 0),  # four chunks per lane
+    ("hc4-flags", 64, 2048, 8, 0.1, 4, "mx", True, 1 | 2),     # bf16 squares + weights
+    ("hc4-T1", 1, 5120, 4, 0.0, 4, "mx", True, 0),
+]
+
+
+@pytest.mark.parametrize("case", MHC_CASES, ids=[c[0] for c in MHC_CASES])
+def test_finalize_mhc(dev, case):
+    name, T, D, K, holes, hc, mode, swz, flags = case
+    wl = W.WORKLOADS["mhc"]
+    fi = W.finalize_inputs(wl, T=T, D=D, K=K, hole_frac=holes)
+    m = W.mhc_inputs(wl, T=T, D=D, hc=hc)
+    bfw = bool(flags & 2)
+    w = W.to_bf16_bits(fi.w) if bfw else fi.w
+    mx = mode == "mx"
+    pre = None if mode == "res" else m.pre
+    say("finalize mhc", name, T, D, K, hc, mode, swz, flags)
+    want = orc.finalize_mhc(fi.y, w, fi.row_of_pair, fi.shared, m.residual, m.post, m.comb,
+                            pre, fi.gamma if pre is not None else None, fi.eps, flags=flags)
+    wd = bf_dev(w, dev) if bfw else torch.from_numpy(w).to(dev)
+    f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    res = ops.moe_finalize_mhc(
+        bf_dev(fi.y, dev), wd, i32_dev(fi.row_of_pair, dev), bf_dev(fi.shared, dev),
+        bf_dev(m.residual, dev), f32(m.post), f32(m.comb), None if pre is None else f32(pre),
+        bf_dev(fi.gamma, dev), fi.eps, flags=flags & 1, mxfp8=mx,
+        scale_layout="swizzled" if swz else "rowmajor")
+    got_res = bits_host(res[0])
+    _close(got_res, want[0], name + " residual_out")
+    if pre is None:
+        assert res[1] is None
+        return
+    got = bits_host(res[1])
+    _close(got, want[1], name)
+    if mx:
+        oc, rm = orc.mxfp8_quantize(got)        # split check on the GPU's own output
+        assert np.array_equal(res[2].cpu().numpy(), oc)
+        assert np.array_equal(res[3].cpu().numpy(), orc.mxfp8_swizzle(rm) if swz else rm)
+
+
 # ---------------------------------------------------------------- full sizes
 @pytest.fixture(scope="module")
 def zipf_inputs():
@@ -449,3 +527,25 @@ def test_prefill_finalize_full_size(dev):
     oc, os_ = orc.mxfp8_quantize(got)
     assert np.array_equal(scales.cpu().numpy(), os_)
     assert_fp8_close(codes.cpu().numpy(), oc, "prefill mxfp8")
+
+
+def test_mhc_finalize_full_size(dev):
+    """The hc = 4 mHC finalize at T=16384, D=5120, K=4 with MXFP8 and swizzled
+    scales, as the benchmark launches it."""
+    wl = W.WORKLOADS["mhc"]
+    fi = W.finalize_inputs(wl)
+    m = W.mhc_inputs(wl)
+    say("mhc finalize", wl.T, wl.D, wl.K, wl.hc)
+    f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    res_out, out, codes, scales = ops.moe_finalize_mhc(
+        bf_dev(fi.y, dev), f32(fi.w), i32_dev(fi.row_of_pair, dev), bf_dev(fi.shared, dev),
+        bf_dev(m.residual, dev), f32(m.post), f32(m.comb), f32(m.pre), bf_dev(fi.gamma, dev),
+        fi.eps, mxfp8=True, scale_layout="swizzled")
+    want = orc.finalize_mhc(fi.y, fi.w, fi.row_of_pair, fi.shared, m.residual, m.post, m.comb,
+                            m.pre, fi.gamma, fi.eps)
+    _close(bits_host(res_out), want[0], "mhc residual_out")
+    got = bits_host(out)
+    _close(got, want[1], "mhc out")
+    oc, rm = orc.mxfp8_quantize(got)
+    assert np.array_equal(scales.cpu().numpy(), orc.mxfp8_swizzle(rm))
+    assert_fp8_close(codes.cpu().numpy(), oc, "mhc mxfp8")
