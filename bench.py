@@ -4,12 +4,19 @@
 
 A step is one pass of the path over one batch of synthetic input, already
 resident in HBM:
-  zipf     (default; T=8192, D=7168, E=256, K=8, valid_token_count=6000)
-           moe_shuffle -> moe_gather_scale_by_token -> moe_scatter_add_by_token
-  quant    (T=4096, D=5120, E=16, K=1)
-           moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
-  prefill  (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
-  decode   (T=128, D=7168, K=8)   moe_finalize_rmsnorm
+  zipf      (default; T=8192, D=7168, E=256, K=8, valid_token_count=6000)
+            moe_shuffle -> moe_gather_scale_by_token -> moe_scatter_add_by_token
+  quant     (T=4096, D=5120, E=16, K=1)
+            moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
+  prefill   (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
+  decode    (T=128, D=7168, K=8)   moe_finalize_rmsnorm
+  prefill-swizzled  prefill with bf16 routing weights and 128x4-tiled scales
+  mhc       (T=16384, D=5120, K=4, hc=4) moe_finalize_mhc with MXFP8
+            (128x4-tiled scales)
+  padded    the zipf routing combined from a static (EP=8, T*K, D) buffer:
+            moe_scatter_add_padded
+  shuffling rows from EP=8 source ranks for one rank's 32 local experts:
+            moe_combine_shuffling -> moe_split_shuffling
 W untimed steps, then exactly K timed steps between two device
 synchronisations (wall clock, and a HIP event pair around the region). Then
 the same K steps once more with HIP events around every stage on the stream
@@ -19,8 +26,9 @@ longest stage is the roofline kernel: its algorithmic bytes per launch
 (unique inputs read once, outputs written once, valid rows only) over that
 duration, against the 8 TB/s HBM peak.
 
-One JSON line on stdout. value = valid tokens per second of the whole step.
-cpu_baseline = the CPU oracle (single-threaded C) timed on the same step.
+One JSON line on stdout. value = valid tokens (routed rows for padded and
+shuffling) per second of the whole step. cpu_baseline = the CPU oracle
+(single-threaded C) timed on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -30,6 +38,7 @@ import json
 import os
 import sys
 import time
+from types import SimpleNamespace
 
 import numpy as np
 
@@ -38,6 +47,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+WORKLOAD_CHOICES = ["zipf", "quant", "prefill", "decode", "prefill-swizzled", "mhc", "padded",
+                    "shuffling"]
+DISPATCH_METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1xMI355X"
 
 
 def parse():
@@ -45,8 +57,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="zipf",
-                   choices=["zipf", "quant", "prefill", "decode"])
+    p.add_argument("--workload", default="zipf", choices=WORKLOAD_CHOICES)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many "
@@ -66,16 +77,262 @@ class Timer:
     """HIP events around named stages on the current stream."""
 
     def __init__(self, torch, names, steps):
-        self.torch = torch
         self.ev = {n: [(torch.cuda.Event(enable_timing=True),
                         torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
                    for n in names}
+
+    def mark(self, name, i, k):
+        self.ev[name][i][k].record()
 
     def mean_ms(self, name):
         pairs = self.ev[name]
         return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
 
 
+def _mark(tm, name, i, k):
+    if tm is not None:
+        tm.mark(name, i, k)
+
+
+# ------------------------------------------------------------------ workloads
+def setup_dispatch(ctx, wl, with_cpu):
+    torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
+    inp = W.dispatch_inputs(wl)
+    T, D, E, K = wl.T, wl.D, wl.E, wl.K
+    vtc = wl.vtc if wl.vtc is not None else T
+    a = T * K
+    V = vtc * K
+    scores = torch.from_numpy(inp.scores).to(dev)
+    x = ctx.bf(inp.x)
+    y = ctx.bf(inp.y)
+    out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    vtc_d = torch.tensor([vtc], dtype=torch.int32, device=dev) if wl.vtc else None
+    quant = wl.quant
+    if quant:
+        rows = torch.empty((a, D), dtype=torch.uint8, device=dev)
+        rscale = torch.empty(a, dtype=torch.float32, device=dev)
+        ub = torch.tensor([wl.scale_ub], dtype=torch.float32, device=dev)
+    else:
+        rows = torch.empty((a, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, ctx.lib.moe_shuffle_workspace_bytes(T, E, K)), dtype=torch.uint8,
+                     device=dev)
+    shuf_out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
+                torch.empty(a, dtype=torch.int32, device=dev),
+                torch.empty(a, dtype=torch.int32, device=dev),
+                torch.empty((T, K), dtype=torch.int32, device=dev))
+
+    def step(tm=None, i=0):
+        _mark(tm, "shuffle", i, 0)
+        counts, ei, ti, rop = ops.moe_shuffle(scores, K, vtc_d, workspace=ws, out=shuf_out)
+        _mark(tm, "shuffle", i, 1)
+        vr = counts[E:]
+        _mark(tm, "gather", i, 0)
+        if quant:
+            ops.moe_gather_scale_quant(x, ti, ei, scores, ub, vr, rows, rscale)
+        else:
+            ops.moe_gather_scale_by_token(x, rop, ei, scores, vr, rows)
+        _mark(tm, "gather", i, 1)
+        _mark(tm, "scatter", i, 0)
+        ops.moe_scatter_add_by_token(out, y, rop, vr)
+        _mark(tm, "scatter", i, 1)
+
+    # algorithmic bytes per launch (unique data read once, written once)
+    row_b = D * 2
+    shuffle_bytes = T * E * 4 + 3 * a * 4 + (E + 1) * 4
+    if quant:
+        gather_bytes = V * row_b + V * D + V * 4 + 2 * V * 4 + V * 4
+    else:
+        gather_bytes = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
+    scatter_bytes = V * row_b + 2 * vtc * row_b + T * K * 4
+    return SimpleNamespace(
+        names=["shuffle", "gather", "scatter"], step=step,
+        stage_bytes={"shuffle": shuffle_bytes, "gather": gather_bytes,
+                     "scatter": scatter_bytes},
+        units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
+        config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} valid_token_count={vtc}",
+                "tokens": T, "hidden": D, "experts": E, "top_k": K,
+                "valid_token_count": vtc, "routed_rows": V,
+                "stages": "shuffle -> " + ("gather_scale_quant" if quant else
+                                           "gather_scale_by_token") +
+                " -> scatter_add_by_token"},
+        dtype="bf16" if not quant else "bf16->fp8e4m3",
+        kernel_src={"shuffle": ["shuffle.hip"], "gather": ["gather.hip"],
+                    "scatter": ["combine.hip"]},
+        cpu=cpu_baseline_dispatch(ctx.orc, inp, wl, vtc) if with_cpu else None)
+
+
+def setup_finalize(ctx, wl, with_cpu, variant=False):
+    """variant: bf16 routing weights and the 128x4-tiled scale layout."""
+    torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
+    fi = W.finalize_inputs(wl)
+    T, D, K = wl.T, wl.D, wl.K
+    w = W.to_bf16_bits(fi.w) if variant else fi.w
+    yd = ctx.bf(fi.y)
+    wd = ctx.bf(w) if variant else torch.from_numpy(w).to(dev)
+    ropd = torch.from_numpy(fi.row_of_pair).to(dev)
+    shd = ctx.bf(fi.shared)
+    gd = ctx.bf(fi.gamma)
+    outd = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    mx = wl.mxfp8
+    layout = "swizzled" if variant else "rowmajor"
+    sbytes = ctx.lib.moe_mxfp8_scale_bytes(T, D, 4 if variant else 0) if mx else 0
+    codes = torch.empty((T, D), dtype=torch.uint8, device=dev) if mx else None
+    scales = torch.empty(sbytes, dtype=torch.uint8, device=dev) if mx else None
+
+    def step(tm=None, i=0):
+        _mark(tm, "finalize", i, 0)
+        ops.moe_finalize_rmsnorm(yd, wd, ropd, shd, gd, wl.eps, out=outd, mxfp8=mx,
+                                 scale_layout=layout, mx_codes=codes, mx_scales=scales)
+        _mark(tm, "finalize", i, 1)
+
+    row_b = D * 2
+    fin_bytes = T * K * row_b + 2 * T * row_b + row_b + T * K * (6 if variant else 8)
+    if mx:
+        fin_bytes += T * D + sbytes
+    name = wl.name + ("-swizzled" if variant else "")
+    return SimpleNamespace(
+        names=["finalize"], step=step, stage_bytes={"finalize": fin_bytes},
+        units_per_step=T, unit="tokens/s",
+        metric="finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
+        config={"workload": f"{name}: T={T} D={D} K={K}" + (" MXFP8" if mx else "") +
+                (" bf16 weights, 128x4-tiled scales" if variant else ""),
+                "tokens": T, "hidden": D, "top_k": K,
+                "stages": "finalize_rmsnorm" + (" + mxfp8" if mx else "")},
+        dtype="bf16" if not mx else "bf16->mxfp8", kernel_src={"finalize": ["finalize.hip"]},
+        traffic_key=name,
+        cpu=cpu_baseline_finalize(ctx.orc, fi, wl, w, 2 if variant else 0, name)
+        if with_cpu else None)
+
+
+def setup_mhc(ctx, wl, with_cpu):
+    torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
+    fi = W.finalize_inputs(wl)
+    m = W.mhc_inputs(wl)
+    T, D, K, hc = wl.T, wl.D, wl.K, wl.hc
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    yd, wd, ropd = ctx.bf(fi.y), f32(fi.w), torch.from_numpy(fi.row_of_pair).to(dev)
+    shd, gd = ctx.bf(fi.shared), ctx.bf(fi.gamma)
+    resd, postd, combd, pred = ctx.bf(m.residual), f32(m.post), f32(m.comb), f32(m.pre)
+    res_out = torch.empty_like(resd)
+    outd = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    sbytes = ctx.lib.moe_mxfp8_scale_bytes(T, D, 4)
+    codes = torch.empty((T, D), dtype=torch.uint8, device=dev)
+    scales = torch.empty(sbytes, dtype=torch.uint8, device=dev)
+
+    def step(tm=None, i=0):
+        _mark(tm, "finalize_mhc", i, 0)
+        ops.moe_finalize_mhc(yd, wd, ropd, shd, resd, postd, combd, pred, gd, wl.eps,
+                             residual_out=res_out, out=outd, mxfp8=True,
+                             scale_layout="swizzled", mx_codes=codes, mx_scales=scales)
+        _mark(tm, "finalize_mhc", i, 1)
+
+    row_b = D * 2
+    nbytes = (T * K * row_b + T * row_b + 2 * T * hc * row_b + T * row_b + row_b + T * K * 8 +
+              T * hc * 8 + T * hc * hc * 4 + T * D + sbytes)
+    return SimpleNamespace(
+        names=["finalize_mhc"], step=step, stage_bytes={"finalize_mhc": nbytes},
+        units_per_step=T, unit="tokens/s",
+        metric="mHC finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
+        config={"workload": f"{wl.name}: T={T} D={D} K={K} hc={hc} MXFP8 128x4-tiled scales",
+                "tokens": T, "hidden": D, "top_k": K, "hc": hc,
+                "stages": "finalize_mhc + mxfp8"},
+        dtype="bf16->mxfp8", kernel_src={"finalize_mhc": ["finalize.hip"]},
+        cpu=cpu_baseline_mhc(ctx.orc, fi, m, wl) if with_cpu else None)
+
+
+def _device_normal_bf16(torch, shape, seed, dev):
+    """Seeded N(0,1) bf16 tensor made on the device, one leading slice at a
+    time (a host draw of several GB would dominate the set-up)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    for i in range(shape[0]):
+        out[i].copy_(torch.randn(shape[1:], generator=g, device=dev))
+    return out
+
+
+def setup_padded(ctx, wl, with_cpu):
+    torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
+    T, D, E, K, EP = wl.T, wl.D, wl.E, wl.K, wl.ep
+    inp = W.dispatch_inputs(wl, with_y=False)
+    vtc = wl.vtc
+    scores = torch.from_numpy(inp.scores).to(dev)
+    counts, ei, ti, rop = ops.moe_shuffle(scores, K, torch.tensor([vtc], dtype=torch.int32,
+                                                                  device=dev))
+    counts_e = counts[:E].contiguous()
+    V = int(counts[E].item())
+    T_K = T * K
+    slabs = _device_normal_bf16(torch, (EP, T_K, D), 6000 + wl.cfg_id, dev)
+    out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, ctx.lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E)),
+                     dtype=torch.uint8, device=dev)
+
+    def step(tm=None, i=0):
+        _mark(tm, "padded_scatter", i, 0)
+        ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
+        _mark(tm, "padded_scatter", i, 1)
+
+    row_b = D * 2
+    nbytes = V * row_b + 2 * vtc * row_b + V * 4 + E * 4
+    return SimpleNamespace(
+        names=["padded_scatter"], step=step, stage_bytes={"padded_scatter": nbytes},
+        units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
+        config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} EP={EP} "
+                            f"valid_token_count={vtc} static (EP, T*K, D) buffer",
+                "tokens": T, "hidden": D, "experts": E, "top_k": K, "ep": EP,
+                "valid_token_count": vtc, "routed_rows": V,
+                "stages": "scatter_add_padded"},
+        dtype="bf16", kernel_src={"padded_scatter": ["combine.hip"]},
+        cpu=cpu_baseline_padded(ctx.orc, ctx.W, wl) if with_cpu else None)
+
+
+def setup_shuffling(ctx, wl, with_cpu):
+    torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
+    T, D, E, K, EP = wl.T, wl.D, wl.E, wl.K, wl.ep
+    EG = E // EP  # rank 0's local experts: columns [0, EG)
+    per_src = []
+    for r in range(EP):  # source rank r routes its own T tokens
+        sc = torch.from_numpy(W.router_scores(wl, seed=r)).to(dev)
+        c, _, _, _ = ops.moe_shuffle(sc, K, None, row_of_pair=False)
+        per_src.append(c[:EG])
+    counts = torch.stack(per_src).contiguous()  # (EP, EG): rows rank r sends per expert
+    rows = int(counts.sum().item())
+    tokens = _device_normal_bf16(torch, (1, rows, D), 7000 + wl.cfg_id, dev)[0]
+    em = torch.empty_like(tokens)
+    back = torch.empty_like(tokens)
+    ws_bytes = max(1, ctx.lib.moe_shuffling_workspace_bytes(EP, EG, rows))
+    ws_c = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(tm=None, i=0):
+        _mark(tm, "combine_shuffling", i, 0)
+        ops.moe_combine_shuffling(tokens, counts, 0, EG, None, out=em, workspace=ws_c)
+        _mark(tm, "combine_shuffling", i, 1)
+        _mark(tm, "split_shuffling", i, 0)
+        ops.moe_split_shuffling(em, counts, 0, EG, None, out=back, workspace=ws_s)
+        _mark(tm, "split_shuffling", i, 1)
+
+    row_b = D * 2
+    nb = 2 * rows * row_b + EP * EG * 4 + (EG + 1) * 4
+    return SimpleNamespace(
+        names=["combine_shuffling", "split_shuffling"], step=step,
+        stage_bytes={"combine_shuffling": nb, "split_shuffling": nb},
+        units_per_step=rows, unit="rows/s",
+        metric="EP re-sort (combine_shuffling + split_shuffling) routed rows/s and achieved "
+               "HBM GB/s (% of peak), 1xMI355X",
+        config={"workload": f"{wl.name}: EP={EP} source ranks x T={T} tokens, E={E}, K={K}, "
+                            f"softmax routing; rank 0's {EG} local experts, {rows} rows, "
+                            f"D={D}, packed layout",
+                "ep": EP, "tokens_per_rank": T, "experts": E, "top_k": K,
+                "local_experts": EG, "rows": rows, "hidden": D,
+                "stages": "combine_shuffling -> split_shuffling"},
+        dtype="bf16", kernel_src={"combine_shuffling": ["reorder.hip"],
+                                  "split_shuffling": ["reorder.hip"]},
+        cpu=cpu_baseline_shuffling(ctx.orc, counts.cpu().numpy(), D, wl)
+        if with_cpu else None)
+
+
+# ------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.gpus != 1:
@@ -86,139 +343,51 @@ def main():
     import torch
 
     import oracle as orc
-    from combine_moe_shuffle_amd import ops
+    from combine_moe_shuffle_amd import _lib, ops
     from combine_moe_shuffle_amd import workloads as W
 
     dev = torch.device("cuda:0")
-    wl = W.WORKLOADS[args.workload]
 
     def bf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
             torch.bfloat16)
 
-    steps, warm = args.steps, args.warmup
-    cpu = None
-
-    if args.workload in ("zipf", "quant"):
-        inp = W.dispatch_inputs(wl)
-        T, D, E, K = wl.T, wl.D, wl.E, wl.K
-        vtc = wl.vtc if wl.vtc is not None else T
-        a = T * K
-        V = vtc * K
-        scores = torch.from_numpy(inp.scores).to(dev)
-        x = bf(inp.x)
-        y = bf(inp.y)
-        out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
-        vtc_d = torch.tensor([vtc], dtype=torch.int32, device=dev) if wl.vtc else None
-        quant = wl.quant
-        if quant:
-            rows = torch.empty((a, D), dtype=torch.uint8, device=dev)
-            rscale = torch.empty(a, dtype=torch.float32, device=dev)
-            ub = torch.tensor([wl.scale_ub], dtype=torch.float32, device=dev)
-        else:
-            rows = torch.empty((a, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(max(1, _lib_ws(T, E, K)), dtype=torch.uint8, device=dev)
-        shuf_out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
-                    torch.empty(a, dtype=torch.int32, device=dev),
-                    torch.empty(a, dtype=torch.int32, device=dev),
-                    torch.empty((T, K), dtype=torch.int32, device=dev))
-        names = ["shuffle", "gather", "scatter"]
-
-        def step(tm=None, i=0):
-            def mark(n, k):
-                if tm is not None:
-                    tm.ev[n][i][k].record()
-            mark("shuffle", 0)
-            counts, ei, ti, rop = ops.moe_shuffle(scores, K, vtc_d, workspace=ws, out=shuf_out)
-            mark("shuffle", 1)
-            vr = counts[E:]
-            mark("gather", 0)
-            if quant:
-                ops.moe_gather_scale_quant(x, ti, ei, scores, ub, vr, rows, rscale)
-            else:
-                ops.moe_gather_scale_by_token(x, rop, ei, scores, vr, rows)
-            mark("gather", 1)
-            mark("scatter", 0)
-            ops.moe_scatter_add_by_token(out, y, rop, vr)
-            mark("scatter", 1)
-
-        # algorithmic bytes per launch (unique data read once, written once)
-        row_b = D * 2
-        shuffle_bytes = T * E * 4 + 3 * a * 4 + (E + 1) * 4
-        if quant:
-            gather_bytes = V * row_b + V * D + V * 4 + 2 * V * 4 + V * 4
-        else:
-            gather_bytes = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
-        scatter_bytes = V * row_b + 2 * vtc * row_b + T * K * 4
-        stage_bytes = {"shuffle": shuffle_bytes, "gather": gather_bytes,
-                       "scatter": scatter_bytes}
-        tokens_per_step = vtc
-        workload_cfg = {"workload": f"{wl.name}: T={T} D={D} E={E} K={K} "
-                        f"valid_token_count={vtc}", "tokens": T, "hidden": D,
-                        "experts": E, "top_k": K, "valid_token_count": vtc,
-                        "routed_rows": V,
-                        "stages": "shuffle -> " + ("gather_scale_quant" if quant else
-                                                   "gather_scale_by_token") +
-                        " -> scatter_add_by_token"}
-        dtype = "bf16" if not quant else "bf16->fp8e4m3"
-        kernel_src = {"shuffle": ["shuffle.hip"], "gather": ["gather.hip"],
-                      "scatter": ["combine.hip"]}
-
-        if not args.no_cpu_baseline:
-            cpu = cpu_baseline_dispatch(orc, inp, wl, vtc)
+    ctx = SimpleNamespace(torch=torch, ops=ops, W=W, orc=orc, dev=dev, bf=bf, lib=_lib.load())
+    with_cpu = not args.no_cpu_baseline
+    name = args.workload
+    if name in ("zipf", "quant"):
+        s = setup_dispatch(ctx, W.WORKLOADS[name], with_cpu)
+    elif name in ("prefill", "decode"):
+        s = setup_finalize(ctx, W.WORKLOADS[name], with_cpu)
+    elif name == "prefill-swizzled":
+        s = setup_finalize(ctx, W.WORKLOADS["prefill"], with_cpu, variant=True)
+    elif name == "mhc":
+        s = setup_mhc(ctx, W.WORKLOADS["mhc"], with_cpu)
+    elif name == "padded":
+        s = setup_padded(ctx, W.WORKLOADS["padded"], with_cpu)
     else:
-        T_ = wl.T
-        fi = W.finalize_inputs(wl)
-        T, D, K = T_, wl.D, wl.K
-        yd = bf(fi.y)
-        wd = torch.from_numpy(fi.w).to(dev)
-        ropd = torch.from_numpy(fi.row_of_pair).to(dev)
-        shd = bf(fi.shared)
-        gd = bf(fi.gamma)
-        outd = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-        names = ["finalize"]
-        mx = wl.mxfp8
-
-        def step(tm=None, i=0):
-            if tm is not None:
-                tm.ev["finalize"][i][0].record()
-            ops.moe_finalize_rmsnorm(yd, wd, ropd, shd, gd, wl.eps, out=outd, mxfp8=mx)
-            if tm is not None:
-                tm.ev["finalize"][i][1].record()
-
-        row_b = D * 2
-        fin_bytes = T * K * row_b + 2 * T * row_b + row_b + T * K * 8
-        if mx:
-            fin_bytes += T * D + T * (D // 32)
-        stage_bytes = {"finalize": fin_bytes}
-        tokens_per_step = T
-        workload_cfg = {"workload": f"{wl.name}: T={T} D={D} K={K}" +
-                        (" MXFP8" if mx else ""), "tokens": T, "hidden": D, "top_k": K,
-                        "stages": "finalize_rmsnorm" + (" + mxfp8" if mx else "")}
-        dtype = "bf16" if not mx else "bf16->mxfp8"
-        kernel_src = {"finalize": ["finalize.hip"]}
-        if not args.no_cpu_baseline:
-            cpu = cpu_baseline_finalize(orc, fi, wl)
+        s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
+    steps, warm = args.steps, args.warmup
 
     # ---- warmup, then exactly `steps` timed steps (no event inside a step:
     # each event record between kernels costs the stream ~10 us)
     for _ in range(warm):
-        step()
+        s.step()
     torch.cuda.synchronize()
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = time.perf_counter()
     region[0].record()
-    for i in range(steps):
-        step()
+    for _ in range(steps):
+        s.step()
     region[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     region_ms = region[0].elapsed_time(region[1])
     # ---- the same steps again with HIP events around every stage: the
     # per-kernel durations behind the roofline
-    tm = Timer(torch, names, steps)
+    tm = Timer(torch, s.names, steps)
     for i in range(steps):
-        step(tm, i)
+        s.step(tm, i)
     torch.cuda.synchronize()
     if args.copy_bytes > 0:
         n = args.copy_bytes // 2
@@ -229,18 +398,16 @@ def main():
         torch.cuda.synchronize()
 
     ms_step = elapsed * 1e3 / steps
-    stage_ms = {n: tm.mean_ms(n) for n in names}
-    total_bytes = sum(stage_bytes.values())
-    dom = max(names, key=lambda n: stage_ms[n])
-    achieved = stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    traffic = load_traffic(dom, kernel_src[dom], wl.name)
+    stage_ms = {n: tm.mean_ms(n) for n in s.names}
+    total_bytes = sum(s.stage_bytes.values())
+    dom = max(s.names, key=lambda n: stage_ms[n])
+    achieved = s.stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = load_traffic(dom, s.kernel_src[dom], getattr(s, "traffic_key", name))
 
     line = {
-        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1xMI355X"
-        if args.workload in ("zipf", "quant") else
-        "finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
-        "value": tokens_per_step / (ms_step * 1e-3),
-        "unit": "tokens/s",
+        "metric": s.metric,
+        "value": s.units_per_step / (ms_step * 1e-3),
+        "unit": s.unit,
         "n_gpus": 1,
         "steps": steps,
         "warmup": warm,
@@ -249,25 +416,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": s.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": workload_cfg,
+        "config": s.config,
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "stage_us": {n: round(stage_ms[n] * 1e3, 2) for n in names},
-        "stage_gbps": {n: round(stage_bytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)
-                       for n in names},
+        "stage_us": {n: round(stage_ms[n] * 1e3, 2) for n in s.names},
+        "stage_gbps": {n: round(s.stage_bytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)
+                       for n in s.names},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "bytes_per_launch": stage_bytes[dom], "traffic": traffic},
-        "cpu_baseline": cpu,
+                     "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic},
+        "cpu_baseline": s.cpu,
     }
     print(json.dumps(line), flush=True)
-
-
-def _lib_ws(T, E, K):
-    from combine_moe_shuffle_amd import _lib
-    return _lib.load().moe_shuffle_workspace_bytes(T, E, K)
 
 
 def load_traffic(kernel, srcs, workload):
@@ -284,6 +446,7 @@ def load_traffic(kernel, srcs, workload):
     return rec.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------------ CPU oracle
 def _median_time(fn, reps):
     ts = []
     for _ in range(reps):
@@ -315,21 +478,76 @@ def cpu_baseline_dispatch(orc, inp, wl, vtc):
                       f"{t:.2f} s each"}
 
 
-def cpu_baseline_finalize(orc, fi, wl):
+def cpu_baseline_finalize(orc, fi, wl, w, flags, name):
     T = wl.T
     n = min(T, 4096)
     sub = slice(0, n)
 
     def run():
-        orc.finalize_rmsnorm(fi.y, np.ascontiguousarray(fi.w[sub]),
+        orc.finalize_rmsnorm(fi.y, np.ascontiguousarray(w[sub]),
                              np.ascontiguousarray(fi.row_of_pair[sub]),
                              np.ascontiguousarray(fi.shared[sub]), fi.gamma, fi.eps,
-                             mxfp8=wl.mxfp8)
+                             flags=flags | (4 if flags & 2 else 0), mxfp8=wl.mxfp8)
 
     t = _median_time(run, 3)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {T} tokens of the {wl.name} finalize; median of 3 "
+            "sample": f"first {n} of {T} tokens of the {name} finalize; median of 3 "
                       f"runs, {t:.2f} s each"}
+
+
+def cpu_baseline_mhc(orc, fi, m, wl):
+    n = min(wl.T, 2048)
+    sub = slice(0, n)
+    c = np.ascontiguousarray
+
+    def run():
+        orc.finalize_mhc(fi.y, c(fi.w[sub]), c(fi.row_of_pair[sub]), c(fi.shared[sub]),
+                         c(m.residual[sub]), c(m.post[sub]), c(m.comb[sub]), c(m.pre[sub]),
+                         fi.gamma, fi.eps, flags=4, mxfp8=True)
+
+    t = _median_time(run, 3)
+    return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of the mhc finalize; median of 3 runs, "
+                      f"{t:.2f} s each"}
+
+
+def cpu_baseline_padded(orc, W, wl):
+    """The oracle's padded combine on a T=1024 draw of the same routing
+    (valid_token_count scaled to 750); every rank's slab holds the same
+    N(0,1) rows (the oracle reads one row per routed pair either way)."""
+    T = 1024
+    vtc = wl.vtc * T // wl.T
+    inp = W.dispatch_inputs(wl, T=T, vtc=vtc, with_y=False)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, wl.K, vtc)
+    g = np.random.default_rng(6000)
+    slab = W.to_bf16_bits(g.standard_normal((T * wl.K, wl.D), dtype=np.float32))
+    slabs = np.ascontiguousarray(np.broadcast_to(slab, (wl.ep,) + slab.shape))
+    out0 = np.zeros((T, wl.D), np.uint16)
+
+    def run():
+        orc.scatter_add_padded(out0.copy(), slabs, counts[:wl.E], ti)
+
+    t = _median_time(run, 3)
+    return {"value": vtc / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"T={T} tokens of the same routing ({vtc} valid), EP={wl.ep}; median "
+                      f"of 3 runs, {t:.2f} s each"}
+
+
+def cpu_baseline_shuffling(orc, counts, D, wl):
+    """The oracle's combine + split on the same counts; the rows are zeros
+    (a row copy does not depend on its values)."""
+    rows = int(counts.sum())
+    EG = counts.shape[1]
+    tok = np.zeros((rows, D), np.uint16)
+
+    def run():
+        em, _ = orc.combine_shuffling(tok, counts, 0, EG, None, out=np.empty_like(tok))
+        orc.split_shuffling(em, counts, 0, EG, None, out=np.empty_like(tok))
+
+    t = _median_time(run, 3)
+    return {"value": rows / t, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole step ({rows} rows, combine + split); median of 3 runs, "
+                      f"{t:.2f} s each"}
 
 
 if __name__ == "__main__":

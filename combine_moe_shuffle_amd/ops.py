@@ -340,24 +340,32 @@ def _finalize_common(y_permuted, expert_weights, row_of_pair, shared, gamma, fla
     return flags, T, K, rows, D
 
 
-def _mx_outputs(T, D, flags, device):
-    codes = torch.empty((T, D), dtype=torch.uint8, device=device)
-    if flags & MX_SWIZZLED:
-        nbytes = _lib.load().moe_mxfp8_scale_bytes(T, D, flags)
-        scales = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    else:
-        scales = torch.empty((T, D // 32), dtype=torch.uint8, device=device)
+def _mx_outputs(T, D, flags, device, codes=None, scales=None):
+    """MXFP8 output buffers: the caller's (checked) or new ones."""
+    nbytes = _lib.load().moe_mxfp8_scale_bytes(T, D, flags)
+    if codes is None:
+        codes = torch.empty((T, D), dtype=torch.uint8, device=device)
+    if scales is None:
+        shape = (nbytes,) if flags & MX_SWIZZLED else (T, D // 32)
+        scales = torch.empty(shape, dtype=torch.uint8, device=device)
+    for t, n, numel in ((codes, "mx_codes", T * D), (scales, "mx_scales", nbytes)):
+        _need(t, n, torch.uint8, None, device)
+        _contig(t, n)
+        if t.numel() < numel:
+            raise ValueError(f"{n} needs {numel} bytes")
     return codes, scales
 
 
 def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma, eps,
-                         flags=0, out=None, mxfp8=False, scale_layout="rowmajor"):
+                         flags=0, out=None, mxfp8=False, scale_layout="rowmajor",
+                         mx_codes=None, mx_scales=None):
     """Weighted top-k reduction + shared add + RMSNorm (+ MXFP8).
 
     expert_weights may be fp32 or bf16 (the bf16-weight flag is set from the
     dtype). scale_layout "rowmajor" gives scales (T, D/32); "swizzled" gives
     the 128x4-tiled byte buffer with zeroed padding rows. Returns out (T, D)
-    bf16, or (out, codes (T, D) uint8, scales uint8) with ``mxfp8``."""
+    bf16, or (out, codes (T, D) uint8, scales uint8) with ``mxfp8``
+    (written into mx_codes / mx_scales when given)."""
     if gamma is None:
         raise ValueError("gamma is required")
     flags, T, K, rows, D = _finalize_common(y_permuted, expert_weights, row_of_pair, shared,
@@ -365,7 +373,8 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
     device = y_permuted.device
     if out is None:
         out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
-    codes, scales = _mx_outputs(T, D, flags, device) if mxfp8 else (None, None)
+    codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
+                     else (None, None))
     _lib.check(_lib.load().moe_finalize_rmsnorm(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
@@ -375,7 +384,7 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
 
 def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, post, comb,
                      pre, gamma, eps, flags=0, residual_out=None, out=None, mxfp8=False,
-                     scale_layout="rowmajor"):
+                     scale_layout="rowmajor", mx_codes=None, mx_scales=None):
     """The finalize of a hyper-connection layer: routed sum h, mHC post-mix
     of the hc residual streams, pre-mix collapse, RMSNorm (+ MXFP8).
 
@@ -413,7 +422,8 @@ def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, 
         out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
     if pre is None:
         out = None
-    codes, scales = _mx_outputs(T, D, flags, device) if mxfp8 else (None, None)
+    codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
+                     else (None, None))
     _lib.check(_lib.load().moe_finalize_mhc(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),

@@ -20,6 +20,9 @@ for the DeepSeek-V4.1 finalize presets):
   prefill  T=16384, D=5120, E=128, K=4      finalize + RMSNorm + MXFP8
   mhc      T=16384, D=5120, E=128, K=4, hc=4 finalize + mHC post-mix and
                                         collapse + RMSNorm + MXFP8 (swizzled)
+  padded   the zipf routing, combined from a static (EP=8, T*K, D) buffer
+  shuffling EP=8 source ranks of T=8192 tokens, softmax routing over E=256,
+           K=8; the rows for one rank's 32 local experts re-sorted and back
 """
 from __future__ import annotations
 
@@ -50,6 +53,7 @@ class Workload:
     mxfp8: bool = False
     sweep_T: tuple = field(default_factory=tuple)
     hc: int = 0                      # mHC residual streams (0: plain finalize)
+    ep: int = 1                      # expert-parallel ranks (padded combine, EP re-sort)
 
 
 WORKLOADS = {
@@ -62,6 +66,9 @@ WORKLOADS = {
                        sweep_T=(1, 8, 32, 128)),
     "prefill": Workload("prefill", 4, T=16384, D=5120, E=128, K=4, mxfp8=True),
     "mhc": Workload("mhc", 5, T=16384, D=5120, E=128, K=4, mxfp8=True, hc=4),
+    "padded": Workload("padded", 6, T=8192, D=7168, E=256, K=8, router="zipf_sigmoid",
+                       vtc=6000, ep=8),
+    "shuffling": Workload("shuffling", 7, T=8192, D=7168, E=256, K=8, ep=8),
 }
 
 
