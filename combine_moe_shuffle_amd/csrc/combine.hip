@@ -17,8 +17,10 @@
 //            invalid slots dropped and the rest sorted in-wave.
 //  general   only token_indices is known: a CSR of rows per token is built
 //            first (count with atomics on per-token counters, exclusive scan,
-//            fill); the order inside a token's list then depends on the
-//            atomics, so the reduce kernel sorts each list before adding.
+//            fill; one launch of per-token-range workgroups up to 131072
+//            rows, four launches beyond); the order inside a token's list then
+//            depends on the atomics, so the reduce kernel sorts each list
+//            before adding.
 //  padded    the general path over the static-shape expert-parallel layout
 //            [EP, T_K, D]: each row is read from the slab of the rank that
 //            owns its expert.
@@ -276,6 +278,119 @@ __global__ void csr_fill_kernel(const int* __restrict__ ti, int T, int a,
   if (static_cast<unsigned>(t) < static_cast<unsigned>(T)) list[start[t] + slot[r]] = r;
 }
 
+// The CSR in one launch: workgroup b owns tokens [b*kRangeT, (b+1)*kRangeT).
+// It reads every valid row's token index (from L2 after the first
+// workgroup), counts its own tokens' rows in LDS and the rows of all lower
+// tokens in registers -- the latter is its offset in the CSR, so no
+// workgroup waits for another -- scans its counters into start[], and fills
+// its tokens' lists by advancing them. With counts (the padded layout) each
+// workgroup takes the valid row count from the expert prefix, which
+// workgroup 0 also writes (prefix[0..E], prefix[E] = rows covered, clamped to
+// a). The order inside a token's list follows the LDS atomics; the reduce
+// kernels sort it. Used while every workgroup's two passes over the indices
+// stay short (a <= kRangeMaxRows).
+constexpr int kRangeT = 256;           // tokens per workgroup
+constexpr int kRangeMaxRows = 131072;  // rows read twice by every workgroup
+constexpr int kRangeUnroll = 8;        // index loads in flight per thread
+
+__device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* wave_tot,
+                                               int& total) {
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    const int wt = wave_tot[w];
+    if (w < wave) base += wt;
+    total += wt;
+  }
+  return base + incl - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
+    const int* __restrict__ ti, int T, int a, const int* __restrict__ vrows,
+    const int* __restrict__ counts, int E, int* __restrict__ prefix, int* __restrict__ start,
+    int* __restrict__ list) {
+  __shared__ int cnt[kRangeT];
+  __shared__ int wave_tot[3][kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int lo = blockIdx.x * kRangeT;
+  const int n = min(kRangeT, T - lo);
+  int V;
+  if (counts) {  // E <= kScanThreads, one expert per thread
+    const int v = tid < E ? max(counts[tid], 0) : 0;
+    int total;
+    const int excl = block_excl_scan(v, lane, wave, wave_tot[0], total);
+    if (blockIdx.x == 0) {
+      if (tid < E) prefix[tid] = min(excl, a);
+      if (tid == 0) prefix[E] = min(total, a);
+    }
+    V = min(total, a);
+  } else {
+    V = clamp_count(vrows, a);
+  }
+  if (tid < kRangeT) cnt[tid] = 0;
+  __syncthreads();
+
+  // pass 1: count this range's rows; rows of tokens below it in `below`.
+  // Every load of a batch issues before the first use (clamped index; rows
+  // past V are dropped by the select).
+  int below = 0;
+  for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
+    int tv[kRangeUnroll];
+#pragma unroll
+    for (int u = 0; u < kRangeUnroll; ++u) {
+      const int r = r0 + u * kScanThreads + tid;
+      const int t = ti[min(r, V - 1)];
+      tv[u] = r < V ? t : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kRangeUnroll; ++u) {
+      const int rel = tv[u] - lo;
+      if (static_cast<unsigned>(rel) < static_cast<unsigned>(n)) atomicAdd(&cnt[rel], 1);
+      else if (static_cast<unsigned>(tv[u]) < static_cast<unsigned>(lo)) ++below;
+    }
+  }
+  int below_total;
+  (void)block_excl_scan(below, lane, wave, wave_tot[1], below_total);  // syncs: cnt complete
+
+  // exclusive scan of the range's counters (one per thread), offset by below
+  const int c = tid < n ? cnt[tid] : 0;
+  int range_total;
+  const int pos = below_total + block_excl_scan(c, lane, wave, wave_tot[2], range_total);
+  if (tid < n) {
+    start[lo + tid] = pos;
+    cnt[tid] = pos;
+  }
+  if (lo + n == T && tid == 0) start[T] = below_total + range_total;
+  __syncthreads();
+
+  // pass 2: each of this range's rows takes the next free slot of its token
+  for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
+    int tv[kRangeUnroll];
+#pragma unroll
+    for (int u = 0; u < kRangeUnroll; ++u) {
+      const int r = r0 + u * kScanThreads + tid;
+      const int t = ti[min(r, V - 1)];
+      tv[u] = r < V ? t : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kRangeUnroll; ++u) {
+      const int rel = tv[u] - lo;
+      if (static_cast<unsigned>(rel) < static_cast<unsigned>(n))
+        list[atomicAdd(&cnt[rel], 1)] = r0 + u * kScanThreads + tid;
+    }
+  }
+}
+
 template <int CPL>
 __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
     uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
@@ -445,16 +560,22 @@ hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const 
   int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
   int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
                                      align256(static_cast<size_t>(T_K) * sizeof(int)));
-  hipLaunchKernelGGL(padded_prefix_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, E,
-                     T_K, prefix);
-  hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
-                     T + 1);
-  const dim3 rgrid((T_K + 255) / 256);
-  hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E,
-                     cnt, slot);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
-  hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E, cnt,
-                     slot, list);
+  if (T_K <= kRangeMaxRows) {
+    hipLaunchKernelGGL(csr_range_build_kernel, dim3((T + kRangeT - 1) / kRangeT),
+                       dim3(kScanThreads), 0, stream, ti, T, T_K, nullptr, counts, E, prefix,
+                       cnt, list);
+  } else {
+    hipLaunchKernelGGL(padded_prefix_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
+                       E, T_K, prefix);
+    hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
+                       T + 1);
+    const dim3 rgrid((T_K + 255) / 256);
+    hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E,
+                       cnt, slot);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
+    hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, T_K, prefix + E,
+                       cnt, slot, list);
+  }
   const SliceShape sh = combine_shape(D / kChunk);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
@@ -513,14 +634,20 @@ hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const in
   int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
   int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
                                      align256(static_cast<size_t>(a) * sizeof(int)));
-  hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
-                     T + 1);
-  const dim3 rgrid((a + 255) / 256);
-  hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows, cnt,
-                     slot);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
-  hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows, cnt,
-                     slot, list);
+  if (a <= kRangeMaxRows) {
+    hipLaunchKernelGGL(csr_range_build_kernel, dim3((T + kRangeT - 1) / kRangeT),
+                       dim3(kScanThreads), 0, stream, ti, T, a, valid_rows, nullptr, 0, nullptr,
+                       cnt, list);
+  } else {
+    hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
+                       T + 1);
+    const dim3 rgrid((a + 255) / 256);
+    hipLaunchKernelGGL(csr_count_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows,
+                       cnt, slot);
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
+    hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows,
+                       cnt, slot, list);
+  }
   const SliceShape sh = combine_shape(D / kChunk);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));

@@ -291,6 +291,27 @@ def test_scatter_add_padded_long_lists(dev):
     assert np.array_equal(bits_host(out), want)
 
 
+def test_scatter_add_csr_multi_launch(dev):
+    """More rows than the one-launch CSR build takes (131072): the general
+    and padded combines build the CSR in four launches."""
+    T, D, E, K, EP = 70000, 64, 8, 2, 2
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, None, seed=4)
+    V = int(counts[E])
+    say("csr multi-launch", T, D, E, K, EP, V)
+    y = W.to_bf16_bits(np.random.default_rng(8).standard_normal((T * K, D)).astype(np.float32))
+    want = orc.scatter_add(inp.out0.copy(), y, ti, V)
+    out = bf_dev(inp.out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    slabs = W.to_bf16_bits(np.random.default_rng(9).standard_normal(
+        (EP, T * K, D)).astype(np.float32))
+    want = orc.scatter_add_padded(inp.out0.copy(), slabs, counts[:E], ti)
+    out = bf_dev(inp.out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts[:E], dev), i32_dev(ti, dev),
+                               out)
+    assert np.array_equal(bits_host(out), want)
+
+
 # ---------------------------------------------------------------- EP re-sort
 SHUFFLING_CASES = [
     # (name, EP, C, c_lo, c_hi, packed, max count, D)
