@@ -19,12 +19,12 @@ resident in HBM:
             moe_combine_shuffling -> moe_split_shuffling
 W untimed steps, then exactly K timed steps between two device
 synchronisations (wall clock, and a HIP event pair around the region). Then
-the same K steps once more with HIP events around every stage on the stream
-the kernels run on (an event between two kernels costs the stream ~10 us, so
-the headline region carries none): each stage's average duration. The
-longest stage is the roofline kernel: its algorithmic bytes per launch
-(unique inputs read once, outputs written once, valid rows only) over that
-duration, against the 8 TB/s HBM peak.
+each stage alone, K launches back to back between one HIP event pair on the
+stream the kernels run on (an event between two kernels costs the stream
+~10 us, so neither region records one inside): each stage's average duration
+per launch. The longest stage is the roofline kernel: its algorithmic bytes
+per launch (unique inputs read once, outputs written once, valid rows only)
+over that duration, against the 8 TB/s HBM peak.
 
 One JSON line on stdout. value = valid tokens (routed rows for padded and
 shuffling) per second of the whole step. cpu_baseline = the CPU oracle
@@ -73,25 +73,18 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-class Timer:
-    """HIP events around named stages on the current stream."""
-
-    def __init__(self, torch, names, steps):
-        self.ev = {n: [(torch.cuda.Event(enable_timing=True),
-                        torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-                   for n in names}
-
-    def mark(self, name, i, k):
-        self.ev[name][i][k].record()
-
-    def mean_ms(self, name):
-        pairs = self.ev[name]
-        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-
-
-def _mark(tm, name, i, k):
-    if tm is not None:
-        tm.mark(name, i, k)
+def stage_ms(torch, fn, reps):
+    """Average duration of one launch of a stage: `reps` launches back to back
+    between one pair of HIP events on the current stream (the stream the
+    kernels run on; no event between two launches)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 # ------------------------------------------------------------------ workloads
@@ -121,20 +114,20 @@ def setup_dispatch(ctx, wl, with_cpu):
                 torch.empty(a, dtype=torch.int32, device=dev),
                 torch.empty((T, K), dtype=torch.int32, device=dev))
 
-    def step(tm=None, i=0):
-        _mark(tm, "shuffle", i, 0)
-        counts, ei, ti, rop = ops.moe_shuffle(scores, K, vtc_d, workspace=ws, out=shuf_out)
-        _mark(tm, "shuffle", i, 1)
-        vr = counts[E:]
-        _mark(tm, "gather", i, 0)
+    counts, ei, ti, rop = shuf_out
+    vr = counts[E:]
+
+    def shuffle():
+        ops.moe_shuffle(scores, K, vtc_d, workspace=ws, out=shuf_out)
+
+    def gather():
         if quant:
             ops.moe_gather_scale_quant(x, ti, ei, scores, ub, vr, rows, rscale)
         else:
             ops.moe_gather_scale_by_token(x, rop, ei, scores, vr, rows)
-        _mark(tm, "gather", i, 1)
-        _mark(tm, "scatter", i, 0)
+
+    def scatter():
         ops.moe_scatter_add_by_token(out, y, rop, vr)
-        _mark(tm, "scatter", i, 1)
 
     # algorithmic bytes per launch (unique data read once, written once)
     row_b = D * 2
@@ -145,7 +138,7 @@ def setup_dispatch(ctx, wl, with_cpu):
         gather_bytes = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
     scatter_bytes = V * row_b + 2 * vtc * row_b + T * K * 4
     return SimpleNamespace(
-        names=["shuffle", "gather", "scatter"], step=step,
+        stages={"shuffle": shuffle, "gather": gather, "scatter": scatter},
         stage_bytes={"shuffle": shuffle_bytes, "gather": gather_bytes,
                      "scatter": scatter_bytes},
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
@@ -179,11 +172,9 @@ def setup_finalize(ctx, wl, with_cpu, variant=False):
     codes = torch.empty((T, D), dtype=torch.uint8, device=dev) if mx else None
     scales = torch.empty(sbytes, dtype=torch.uint8, device=dev) if mx else None
 
-    def step(tm=None, i=0):
-        _mark(tm, "finalize", i, 0)
+    def finalize():
         ops.moe_finalize_rmsnorm(yd, wd, ropd, shd, gd, wl.eps, out=outd, mxfp8=mx,
                                  scale_layout=layout, mx_codes=codes, mx_scales=scales)
-        _mark(tm, "finalize", i, 1)
 
     row_b = D * 2
     fin_bytes = T * K * row_b + 2 * T * row_b + row_b + T * K * (6 if variant else 8)
@@ -191,7 +182,7 @@ def setup_finalize(ctx, wl, with_cpu, variant=False):
         fin_bytes += T * D + sbytes
     name = wl.name + ("-swizzled" if variant else "")
     return SimpleNamespace(
-        names=["finalize"], step=step, stage_bytes={"finalize": fin_bytes},
+        stages={"finalize": finalize}, stage_bytes={"finalize": fin_bytes},
         units_per_step=T, unit="tokens/s",
         metric="finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
         config={"workload": f"{name}: T={T} D={D} K={K}" + (" MXFP8" if mx else "") +
@@ -219,18 +210,16 @@ def setup_mhc(ctx, wl, with_cpu):
     codes = torch.empty((T, D), dtype=torch.uint8, device=dev)
     scales = torch.empty(sbytes, dtype=torch.uint8, device=dev)
 
-    def step(tm=None, i=0):
-        _mark(tm, "finalize_mhc", i, 0)
+    def finalize_mhc():
         ops.moe_finalize_mhc(yd, wd, ropd, shd, resd, postd, combd, pred, gd, wl.eps,
                              residual_out=res_out, out=outd, mxfp8=True,
                              scale_layout="swizzled", mx_codes=codes, mx_scales=scales)
-        _mark(tm, "finalize_mhc", i, 1)
 
     row_b = D * 2
     nbytes = (T * K * row_b + T * row_b + 2 * T * hc * row_b + T * row_b + row_b + T * K * 8 +
               T * hc * 8 + T * hc * hc * 4 + T * D + sbytes)
     return SimpleNamespace(
-        names=["finalize_mhc"], step=step, stage_bytes={"finalize_mhc": nbytes},
+        stages={"finalize_mhc": finalize_mhc}, stage_bytes={"finalize_mhc": nbytes},
         units_per_step=T, unit="tokens/s",
         metric="mHC finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
         config={"workload": f"{wl.name}: T={T} D={D} K={K} hc={hc} MXFP8 128x4-tiled scales",
@@ -267,15 +256,13 @@ def setup_padded(ctx, wl, with_cpu):
     ws = torch.empty(max(1, ctx.lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E)),
                      dtype=torch.uint8, device=dev)
 
-    def step(tm=None, i=0):
-        _mark(tm, "padded_scatter", i, 0)
+    def padded_scatter():
         ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
-        _mark(tm, "padded_scatter", i, 1)
 
     row_b = D * 2
     nbytes = V * row_b + 2 * vtc * row_b + V * 4 + E * 4
     return SimpleNamespace(
-        names=["padded_scatter"], step=step, stage_bytes={"padded_scatter": nbytes},
+        stages={"padded_scatter": padded_scatter}, stage_bytes={"padded_scatter": nbytes},
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
         config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} EP={EP} "
                             f"valid_token_count={vtc} static (EP, T*K, D) buffer",
@@ -304,18 +291,16 @@ def setup_shuffling(ctx, wl, with_cpu):
     ws_c = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_s = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-    def step(tm=None, i=0):
-        _mark(tm, "combine_shuffling", i, 0)
+    def combine_shuffling():
         ops.moe_combine_shuffling(tokens, counts, 0, EG, None, out=em, workspace=ws_c)
-        _mark(tm, "combine_shuffling", i, 1)
-        _mark(tm, "split_shuffling", i, 0)
+
+    def split_shuffling():
         ops.moe_split_shuffling(em, counts, 0, EG, None, out=back, workspace=ws_s)
-        _mark(tm, "split_shuffling", i, 1)
 
     row_b = D * 2
     nb = 2 * rows * row_b + EP * EG * 4 + (EG + 1) * 4
     return SimpleNamespace(
-        names=["combine_shuffling", "split_shuffling"], step=step,
+        stages={"combine_shuffling": combine_shuffling, "split_shuffling": split_shuffling},
         stage_bytes={"combine_shuffling": nb, "split_shuffling": nb},
         units_per_step=rows, unit="rows/s",
         metric="EP re-sort (combine_shuffling + split_shuffling) routed rows/s and achieved "
@@ -368,27 +353,30 @@ def main():
     else:
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
     steps, warm = args.steps, args.warmup
+    stages = list(s.stages.items())
+
+    def step():
+        for _, fn in stages:
+            fn()
 
     # ---- warmup, then exactly `steps` timed steps (no event inside a step:
     # each event record between kernels costs the stream ~10 us)
     for _ in range(warm):
-        s.step()
+        step()
     torch.cuda.synchronize()
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = time.perf_counter()
     region[0].record()
     for _ in range(steps):
-        s.step()
+        step()
     region[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     region_ms = region[0].elapsed_time(region[1])
-    # ---- the same steps again with HIP events around every stage: the
-    # per-kernel durations behind the roofline
-    tm = Timer(torch, s.names, steps)
-    for i in range(steps):
-        s.step(tm, i)
-    torch.cuda.synchronize()
+    # ---- each stage alone, `steps` launches back to back: its average
+    # duration per launch, the denominator of the roofline
+    names = [n for n, _ in stages]
+    st_ms = {n: stage_ms(torch, fn, steps) for n, fn in stages}
     if args.copy_bytes > 0:
         n = args.copy_bytes // 2
         src = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -398,10 +386,9 @@ def main():
         torch.cuda.synchronize()
 
     ms_step = elapsed * 1e3 / steps
-    stage_ms = {n: tm.mean_ms(n) for n in s.names}
     total_bytes = sum(s.stage_bytes.values())
-    dom = max(s.names, key=lambda n: stage_ms[n])
-    achieved = s.stage_bytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    dom = max(names, key=lambda n: st_ms[n])
+    achieved = s.stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom, s.kernel_src[dom], getattr(s, "traffic_key", name))
 
     line = {
@@ -421,9 +408,9 @@ def main():
         "config": s.config,
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "stage_us": {n: round(stage_ms[n] * 1e3, 2) for n in s.names},
-        "stage_gbps": {n: round(s.stage_bytes[n] / (stage_ms[n] * 1e-3) / 1e9, 1)
-                       for n in s.names},
+        "stage_us": {n: round(st_ms[n] * 1e3, 2) for n in names},
+        "stage_gbps": {n: round(s.stage_bytes[n] / (st_ms[n] * 1e-3) / 1e9, 1)
+                       for n in names},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic},
