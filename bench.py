@@ -17,12 +17,14 @@ resident in HBM:
             moe_scatter_add_padded
   shuffling rows from EP=8 source ranks for one rank's 32 local experts:
             moe_combine_shuffling -> moe_split_shuffling
-W untimed steps, then exactly K timed steps between two device
+A step launches its kernels from Python (--graph replays a HIP graph of the
+step instead; a graph launch costs more than a few kernel launches here). W
+untimed steps, then exactly K timed steps between two device
 synchronisations (wall clock, and a HIP event pair around the region). Then
-each stage alone, K launches back to back between one HIP event pair on the
-stream the kernels run on (an event between two kernels costs the stream
-~10 us, so neither region records one inside): each stage's average duration
-per launch. The longest stage is the roofline kernel: its algorithmic bytes
+each stage alone: K launches captured back to back in one HIP graph, replayed
+once between one HIP event pair on the stream the kernels run on (an event
+between two kernels costs the stream ~10 us, so neither region records one
+inside): each stage's average duration per launch, the kernels' own time. The longest stage is the roofline kernel: its algorithmic bytes
 per launch (unique inputs read once, outputs written once, valid rows only)
 over that duration, against the 8 TB/s HBM peak.
 
@@ -59,6 +61,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="zipf", choices=WORKLOAD_CHOICES)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay a HIP graph of the step instead of launching its kernels from "
+                        "Python (a graph launch costs more than a few kernel launches here)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many "
                         "bytes (the calibration kernel of the HBM counter runs)")
@@ -73,15 +78,37 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
+def capture(torch, fn):
+    """A HIP graph of fn(): one eager pass on a side stream, then the
+    capture (torch's capture stream is the current stream inside it, and the
+    bindings launch on the current stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 def stage_ms(torch, fn, reps):
-    """Average duration of one launch of a stage: `reps` launches back to back
-    between one pair of HIP events on the current stream (the stream the
-    kernels run on; no event between two launches)."""
+    """Average duration of one launch of a stage: `reps` launches captured back
+    to back in one HIP graph, replayed once between a pair of HIP events on
+    the stream the kernels run on. Without Python between launches and
+    without an event between kernels this is the kernels' own time (what the
+    rocprofv3 kernel trace shows), not the launch overhead."""
+    def many():
+        for _ in range(reps):
+            fn()
+    g = capture(torch, many)
+    g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(reps):
-        fn()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
@@ -354,21 +381,23 @@ def main():
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
     steps, warm = args.steps, args.warmup
     stages = list(s.stages.items())
+    graph = args.graph
 
     def step():
         for _, fn in stages:
             fn()
 
+    run_step = capture(torch, step).replay if graph else step
     # ---- warmup, then exactly `steps` timed steps (no event inside a step:
     # each event record between kernels costs the stream ~10 us)
     for _ in range(warm):
-        step()
+        run_step()
     torch.cuda.synchronize()
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = time.perf_counter()
     region[0].record()
     for _ in range(steps):
-        step()
+        run_step()
     region[1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -405,7 +434,8 @@ def main():
         "vs_baseline": None,
         "dtype": s.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": s.config,
+        "config": {**s.config, "launch": "one HIP graph per step" if graph else
+                   "eager (kernels launched from Python)"},
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stage_us": {n: round(st_ms[n] * 1e3, 2) for n in names},

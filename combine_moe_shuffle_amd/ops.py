@@ -16,8 +16,18 @@ import torch
 from . import _lib
 
 
-def _stream():
-    return torch.cuda.current_stream().cuda_stream
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device):
+    """The current stream of the current device, as a raw handle. The library
+    launches on the current HIP device, so the tensors must live there."""
+    cur = torch.cuda.current_device()
+    if device.index is not None and device.index != cur:
+        raise ValueError(f"the tensors are on {device} but the current device is cuda:{cur}")
+    if _raw_stream is not None:
+        return _raw_stream(cur)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _ptr(t):
@@ -92,7 +102,7 @@ def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspac
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     _lib.check(lib.moe_shuffle(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
                                _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace),
-                               workspace.numel(), _stream()))
+                               workspace.numel(), _stream(device)))
     return counts, ei, ti, rop
 
 
@@ -127,7 +137,7 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
         raise ValueError("out must be (a, D)")
     _lib.check(_lib.load().moe_gather_scale(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(vr), _ptr(out), _stream()))
+        scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
     return out
 
 
@@ -150,7 +160,7 @@ def moe_gather_scale_by_token(x, row_of_pair, expert_indices, scores, valid_rows
         raise ValueError("out must be (a, D)")
     _lib.check(_lib.load().moe_gather_scale_by_token(
         _ptr(x), T, D, _ptr(row_of_pair), K, _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(vr), _ptr(out), _stream()))
+        scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
     return out
 
 
@@ -175,7 +185,7 @@ def moe_gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=No
     _contig(out, "out")
     _lib.check(_lib.load().moe_gather_scale_quant(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream()))
+        scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream(device)))
     return out, out_scale
 
 
@@ -206,7 +216,7 @@ def moe_scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None, works
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     _lib.check(lib.moe_scatter_add(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
                                    a, D, _ptr(vr), _ptr(workspace), workspace.numel(),
-                                   _stream()))
+                                   _stream(device)))
     return out_tokens
 
 
@@ -220,7 +230,7 @@ def moe_scatter_add_by_token(out_tokens, in_tokens, row_of_pair, valid_rows=None
         raise ValueError("row_of_pair must be (T, K)")
     _lib.check(_lib.load().moe_scatter_add_by_token(
         _ptr(out_tokens), T, _ptr(in_tokens), _ptr(row_of_pair), row_of_pair.shape[1],
-        in_tokens.shape[0], D, _ptr(vr), _stream()))
+        in_tokens.shape[0], D, _ptr(vr), _stream(device)))
     return out_tokens
 
 
@@ -246,7 +256,7 @@ def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, w
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     _lib.check(lib.moe_scatter_add_padded(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
                                           _ptr(token_indices), _ptr(out_tokens), T, D,
-                                          _ptr(workspace), workspace.numel(), _stream()))
+                                          _ptr(workspace), workspace.numel(), _stream(device)))
     return out_tokens
 
 
@@ -275,7 +285,7 @@ def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, wit
     _lib.check(getattr(lib, name)(
         _ptr(tokens), tokens.shape[0], _ptr(out), out.shape[0], D, _ptr(counts), EP, C, c_lo,
         c_hi, -1 if rank_stride is None else int(rank_stride), _ptr(oc), _ptr(workspace),
-        workspace.numel(), _stream()))
+        workspace.numel(), _stream(device)))
     return out, oc
 
 
@@ -378,7 +388,7 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
     _lib.check(_lib.load().moe_finalize_rmsnorm(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
-        _stream()))
+        _stream(device)))
     return (out, codes, scales) if mxfp8 else out
 
 
@@ -428,7 +438,7 @@ def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, 
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),
         _ptr(gamma) if pre is not None else None, float(eps), T, K, D, hc, int(flags),
-        _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream()))
+        _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream(device)))
     return (residual_out, out, codes, scales) if mxfp8 else (residual_out, out)
 
 
@@ -440,7 +450,8 @@ def moe_convert_check(values):
     n = values.numel()
     bf = torch.empty(n, dtype=torch.int16, device=values.device)
     e4 = torch.empty(n, dtype=torch.uint8, device=values.device)
-    _lib.check(_lib.load().moe_convert_check(_ptr(values), n, _ptr(bf), _ptr(e4), _stream()))
+    _lib.check(_lib.load().moe_convert_check(_ptr(values), n, _ptr(bf), _ptr(e4),
+                                             _stream(values.device)))
     return bf, e4
 
 

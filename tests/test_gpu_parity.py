@@ -475,6 +475,91 @@ def test_finalize_mhc(dev, case):
         assert np.array_equal(res[3].cpu().numpy(), orc.mxfp8_swizzle(rm) if swz else rm)
 
 
+# ---------------------------------------------------------------- HIP graphs
+def test_graph_replay_matches_eager(dev):
+    """shuffle -> gather (by token) -> scatter (by token) -> finalize + MXFP8
+    (128x4-tiled scales) -> mHC finalize, captured in one HIP graph. Every
+    replay, with eager work (buffers overwritten) and synchronisations between
+    replays, equals the eager run bit for bit."""
+    wl = W.WORKLOADS["zipf"]
+    T, D, E, K, vtc, hc = 200, 1024, 16, 4, 150, 4
+    inp = W.dispatch_inputs(wl, T=T, D=D, E=E, K=K, vtc=vtc, out0="normal")
+    fi = W.finalize_inputs(W.WORKLOADS["mhc"], T=T, D=D, K=K, hole_frac=0.1)
+    m = W.mhc_inputs(W.WORKLOADS["mhc"], T=T, D=D, hc=hc)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    s, x, y, out0 = f32(inp.scores), bf_dev(inp.x, dev), bf_dev(inp.y, dev), bf_dev(inp.out0, dev)
+    vtc_d = scalar_dev(vtc, dev)
+    yf, wf, ropf = bf_dev(fi.y, dev), f32(fi.w), i32_dev(fi.row_of_pair, dev)
+    shf, gf = bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev)
+    res, post, comb, pre = bf_dev(m.residual, dev), f32(m.post), f32(m.comb), f32(m.pre)
+
+    def buffers():
+        i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device=dev)  # noqa: E731
+        u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=dev)  # noqa: E731
+        nsc = 256 * (D // 32)  # 128x4-tiled scales of T=200 rows, padded to 256
+        return dict(
+            ws=u8(ops._lib.load().moe_shuffle_workspace_bytes(T, E, K)),
+            shuf=(i32(E + 1), i32(T * K), i32(T * K), i32(T, K)),
+            rows=torch.empty((T * K, D), dtype=torch.bfloat16, device=dev),
+            out=out0.clone(), fin=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+            codes=u8(T, D), scales=u8(nsc), res_out=torch.empty_like(res),
+            mout=torch.empty((T, D), dtype=torch.bfloat16, device=dev), mcodes=u8(T, D),
+            mscales=u8(nsc))
+
+    def path(b):
+        counts, ei, ti, rop = ops.moe_shuffle(s, K, vtc_d, workspace=b["ws"], out=b["shuf"])
+        ops.moe_gather_scale_by_token(x, rop, ei, s, counts[E:], b["rows"])
+        ops.moe_scatter_add_by_token(b["out"], y, rop, counts[E:])
+        ops.moe_finalize_rmsnorm(yf, wf, ropf, shf, gf, fi.eps, out=b["fin"], mxfp8=True,
+                                 scale_layout="swizzled", mx_codes=b["codes"],
+                                 mx_scales=b["scales"])
+        ops.moe_finalize_mhc(yf, wf, ropf, shf, res, post, comb, pre, gf, fi.eps,
+                             residual_out=b["res_out"], out=b["mout"], mxfp8=True,
+                             scale_layout="swizzled", mx_codes=b["mcodes"],
+                             mx_scales=b["mscales"])
+
+    def snapshot(b):
+        V = int(b["shuf"][0][E].item())
+        snap = {k: b[k].cpu().clone() for k in ("out", "fin", "codes", "scales", "res_out",
+                                                 "mout", "mcodes", "mscales")}
+        snap["rows"] = b["rows"][:V].cpu().clone()
+        for i, t in enumerate(b["shuf"]):
+            snap[f"shuf{i}"] = t.cpu().clone()
+        return snap
+
+    say("graph replay", T, D, E, K, vtc, hc)
+    eager = buffers()
+    path(eager)
+    torch.cuda.synchronize()
+    want = snapshot(eager)
+
+    b = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager pass on the capture stream first
+        path(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path(b)
+    for rep in range(3):
+        # eager work between replays: reset the accumulated output, spoil the rest
+        b["out"].copy_(out0)
+        for k in ("fin", "res_out", "mout", "rows"):
+            b[k].view(torch.int16).fill_(0x7E00 + rep)
+        for k in ("codes", "scales", "mcodes", "mscales"):
+            b[k].fill_(0xA5)
+        for t in b["shuf"]:
+            t.fill_(-3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = snapshot(b)
+        for k, v in want.items():
+            assert torch.equal(got[k], v), (rep, k)
+
+
 # ---------------------------------------------------------------- full sizes
 @pytest.fixture(scope="module")
 def zipf_inputs():
