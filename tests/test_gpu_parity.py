@@ -109,6 +109,7 @@ SHUFFLE_CASES = [
     ("vtc-beyond", 100, 16, 2, 99999, "normal"),
     ("vtc-negative", 100, 16, 2, -5, "normal"),
     ("T0", 0, 16, 2, None, "normal"),
+    ("large-T", 70000, 64, 4, 65000, "normal"),
 ]
 
 
@@ -191,7 +192,8 @@ def test_gather_scale_bit_exact(dev, case, path):
 
 @pytest.mark.parametrize("ub", [None, 1200.0, 1e-3])
 @pytest.mark.parametrize("shape", [(96, 8 * (64 * 5 + 7), 6, 2, 90), (40, 5120, 16, 1, None),
-                                   (20, 8, 3, 2, None)], ids=["ragged", "D5120", "D8"])
+                                   (20, 8, 3, 2, None), (6, 65536, 4, 1, None)],
+                         ids=["ragged", "D5120", "D8", "Dmax"])
 def test_gather_scale_quant(dev, ub, shape):
     T, D, E, K, vtc = shape
     inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=3)
@@ -257,6 +259,7 @@ PADDED_CASES = [
     ("ep2-ragged-D", 77, 8 * (64 * 5 + 3), 10, 3, 2),
     ("ep4", 129, 1024, 16, 4, 4),
     ("ep8-wide", 64, 8 * 1000, 64, 8, 8),
+    ("E1024-ep64", 50, 64, 1024, 16, 64),   # the most experts and ranks
 ]
 
 
@@ -320,6 +323,7 @@ SHUFFLING_CASES = [
     ("static-ep8-local-range", 8, 64, 16, 24, False, 12, 1024),
     ("static-ep2-empty-range", 2, 8, 3, 3, False, 5, 64),
     ("static-ep64", 64, 32, 0, 32, False, 3, 512),
+    ("static-4096-segments", 64, 64, 0, 64, False, 2, 64),  # the most segments
 ]
 
 
@@ -370,6 +374,7 @@ FIN_CASES = [
     ("ragged-D", 33, 32 * 49, 3, 0.0, True, 0, True),   # partial last wave
     ("many-tokens", 2100, 640, 4, 0.05, True, 0, True),  # the many-token shape
     ("K1", 9, 256, 1, 0.0, False, 0, True),
+    ("Dmax", 3, 65536, 2, 0.0, True, 0, True),         # the widest row
 ]
 
 
@@ -439,6 +444,7 @@ MHC_CASES = [
     ("hc4-wide", 5, 16384 + 8192, 2, 0.0, 4, "norm", False, 0),  # four chunks per lane
     ("hc4-flags", 64, 2048, 8, 0.1, 4, "mx", True, 1 | 2),     # bf16 squares + weights
     ("hc4-T1", 1, 5120, 4, 0.0, 4, "mx", True, 0),
+    ("hc4-Dmax", 2, 32768, 2, 0.0, 4, "mx", True, 0),     # the widest row
 ]
 
 
@@ -473,6 +479,51 @@ def test_finalize_mhc(dev, case):
         oc, rm = orc.mxfp8_quantize(got)        # split check on the GPU's own output
         assert np.array_equal(res[2].cpu().numpy(), oc)
         assert np.array_equal(res[3].cpu().numpy(), orc.mxfp8_swizzle(rm) if swz else rm)
+
+
+# ---------------------------------------------------------------- empty inputs
+def test_empty_inputs_leave_outputs_alone(dev):
+    """Zero tokens, zero rows or zero counts: every entry point returns
+    without touching its outputs."""
+    say("empty inputs")
+    D, K, E = 64, 2, 4
+    bf = lambda *sh: torch.randn(sh, device=dev).to(torch.bfloat16)  # noqa: E731
+    i32 = lambda *sh: torch.zeros(sh, dtype=torch.int32, device=dev)  # noqa: E731
+    f32 = lambda *sh: torch.rand(sh, device=dev)  # noqa: E731
+    # zero tokens
+    ops.moe_gather_scale(bf(0, D), i32(0), i32(0), f32(0, E), out=bf(0, D))
+    ops.moe_gather_scale_by_token(bf(0, D), i32(0, K), i32(0), f32(0, E), out=bf(0, D))
+    ops.moe_gather_scale_quant(bf(0, D), i32(0), i32(0), f32(0, E))
+    out = bf(0, D)
+    ops.moe_scatter_add_by_token(out, bf(0, D), i32(0, K))
+    fin = ops.moe_finalize_rmsnorm(bf(0, D), f32(0, K), i32(0, K), None, bf(D), 1e-6,
+                                   mxfp8=True)
+    assert fin[0].shape == (0, D)
+    r = ops.moe_finalize_mhc(bf(0, D), f32(0, K), i32(0, K), None, bf(0, 4, D), f32(0, 4),
+                             f32(0, 4, 4), f32(0, 4), bf(D), 1e-6)
+    assert r[0].shape == (0, 4, D)
+    # rows present, none valid: outputs keep their bits
+    T = 5
+    out = bf(T, D)
+    keep = out.clone()
+    ops.moe_scatter_add(out, bf(T * K, D), i32(T * K), scalar_dev(0, dev))
+    ops.moe_scatter_add_by_token(out, bf(T * K, D), i32(T, K) - 1)
+    ops.moe_scatter_add_padded(bf(2, T * K, D), i32(E), i32(T * K), out)
+    assert torch.equal(out, keep)
+    rows = bf(T * K, D)
+    keep = rows.clone()
+    ops.moe_gather_scale(bf(T, D), i32(T * K), i32(T * K), f32(T, E), scalar_dev(0, dev), rows)
+    assert torch.equal(rows, keep)
+    # all counts zero: nothing moves, the column counts are zero
+    tok = bf(8, D)
+    em = bf(8, D)
+    keep = em.clone()
+    em2, oc = ops.moe_combine_shuffling(tok, i32(2, 4), 0, 4, None, out=em)
+    assert torch.equal(em2, keep) and int(oc.abs().sum()) == 0
+    back = bf(8, D)
+    keep = back.clone()
+    ops.moe_split_shuffling(em, i32(2, 4), 0, 4, 4, out=back)
+    assert torch.equal(back, keep)
 
 
 # ---------------------------------------------------------------- HIP graphs
