@@ -706,3 +706,48 @@ def test_mhc_finalize_full_size(dev):
     oc, rm = orc.mxfp8_quantize(got)
     assert np.array_equal(scales.cpu().numpy(), orc.mxfp8_swizzle(rm))
     assert_fp8_close(codes.cpu().numpy(), oc, "mhc mxfp8")
+
+
+def test_padded_combine_full_routing(dev):
+    """The padded workload's routing at full size (zipf scores, T=8192, E=256,
+    K=8, valid_token_count=6000, EP=8 static buffer), shuffled on the device
+    as the benchmark does; rows of D=256 keep the host copy of the eight
+    slabs small. Every element checked."""
+    wl = W.WORKLOADS["padded"]
+    D = 256
+    inp = W.dispatch_inputs(wl, D=D, with_y=False)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, wl.K, wl.vtc)
+    say("padded full routing", wl.T, D, wl.E, wl.K, wl.ep, int(counts[wl.E]))
+    s = torch.from_numpy(inp.scores).to(dev)
+    gc, gei, gti, grop = ops.moe_shuffle(s, wl.K, scalar_dev(wl.vtc, dev))
+    assert np.array_equal(gti.cpu().numpy(), ti)
+    slabs = W.to_bf16_bits(np.random.default_rng(6).standard_normal(
+        (wl.ep, wl.T * wl.K, D), dtype=np.float32))
+    want = orc.scatter_add_padded(np.zeros((wl.T, D), np.uint16), slabs, counts[:wl.E], ti)
+    out = torch.zeros((wl.T, D), dtype=torch.bfloat16, device=dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:wl.E].contiguous(), gti, out)
+    assert np.array_equal(bits_host(out), want)
+
+
+def test_shuffling_workload_full_size(dev):
+    """The EP re-sort as the benchmark runs it: eight source ranks of 8192
+    tokens routed over E=256 with K=8, rank 0's 32 local experts, packed
+    layout, D=7168; combine and split, every element checked."""
+    wl = W.WORKLOADS["shuffling"]
+    EG = wl.E // wl.ep
+    per_src = []
+    for r in range(wl.ep):
+        c, _, _, _ = orc.shuffle(W.router_scores(wl, seed=r), wl.K)
+        per_src.append(c[:EG])
+    cnt = np.stack(per_src).astype(np.int32)
+    rows = int(cnt.sum())
+    say("shuffling full size", wl.ep, EG, rows, wl.D)
+    tok = W.to_bf16_bits(np.random.default_rng(7).standard_normal((rows, wl.D),
+                                                                  dtype=np.float32))
+    want, woc = orc.combine_shuffling(tok, cnt, 0, EG, None)
+    cd = i32_dev(cnt, dev)
+    em, oc = ops.moe_combine_shuffling(bf_dev(tok, dev), cd, 0, EG)
+    assert np.array_equal(oc.cpu().numpy(), woc)
+    assert np.array_equal(bits_host(em), want)
+    back = ops.moe_split_shuffling(em, cd, 0, EG)
+    assert np.array_equal(bits_host(back), tok)
