@@ -596,12 +596,12 @@ hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const 
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream) {
-  // G rows in flight: the next power of two >= K, at most 8, with G * cpl <= 16
-  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 ? 4 : 8));
-  static const int allowed8[] = {2, 1};
-  static const int allowed4[] = {2, 4, 3, 1};
-  const SliceShape sh = G >= 8 ? pick_slices(D / kChunk, allowed8, 2, 1 << 20)
-                               : pick_slices(D / kChunk, allowed4, 4, 1 << 20);
+  // G rows in flight: the next power of two >= K, at most 4 (for K = 8 two
+  // groups of 4 measured 1.5 % faster than one of 8: fewer registers, more
+  // waves resident)
+  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : 4);
+  static const int allowed[] = {2, 4, 3, 1};
+  const SliceShape sh = pick_slices(D / kChunk, allowed, 4, 1 << 20);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);
@@ -612,8 +612,7 @@ hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
   do {                                \
     if (G == 1) L2(C, 1);             \
     else if (G == 2) L2(C, 2);        \
-    else if (G == 4) L2(C, 4);        \
-    else L2(C, ((C) <= 2 ? 8 : 4));   \
+    else L2(C, 4);                    \
   } while (0)
   switch (sh.cpl) {
     case 1: LG(1); break;

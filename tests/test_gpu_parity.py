@@ -158,6 +158,8 @@ GATHER_CASES = [
     ("short-row", 33, 8, 4, 2, None),                  # one chunk per row
     ("odd", 129, 8 * 1000, 13, 4, 100),
     ("vtc0", 16, 512, 4, 2, 0),
+    ("K16", 40, 8 * 70, 32, 16, 30),                   # four groups of rows in flight
+    ("K64", 10, 256, 64, 64, None),                    # a full wave of rows per token
 ]
 
 
