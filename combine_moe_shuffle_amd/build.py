@@ -19,6 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_shuffle.so")
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_abi_consumer.c")
+CONSUMER = os.path.join(ROOT, "tests", "c_abi_consumer")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 
 ARCH = "gfx950"
@@ -74,7 +76,23 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_consumer()
     return LIB
+
+
+def build_consumer() -> str:
+    """The plain C consumer of the ABI used by the tests: gcc, the header, the
+    HIP runtime API and this library (found through its rpath)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           f"-I{rocm}/include", f"-I{INCLUDE}", CONSUMER_SRC, "-o", CONSUMER + ".tmp",
+           f"-L{HERE}", "-lmoe_shuffle", f"-L{rocm}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../combine_moe_shuffle_amd", f"-Wl,-rpath,{rocm}/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building the C consumer failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(CONSUMER + ".tmp", CONSUMER)
+    return CONSUMER
 
 
 if __name__ == "__main__":

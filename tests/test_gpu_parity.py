@@ -15,6 +15,8 @@ Sizes: small shapes spanning several slices and a ragged tail, the edge cases
 scores, tokens with more than 64 rows), and the full workload sizes in the
 launch configuration the benchmark times.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -753,3 +755,36 @@ def test_shuffling_workload_full_size(dev):
     assert np.array_equal(bits_host(em), want)
     back = ops.moe_split_shuffling(em, cd, 0, EG)
     assert np.array_equal(bits_host(back), tok)
+
+
+def test_c_abi_consumer(dev, tmp_path):
+    """A plain C program (tests/c_abi_consumer.c: gcc, the header and the HIP
+    runtime only) runs shuffle -> gather by token -> scatter by token on the
+    tiny workload, as a child process; its outputs equal the oracle's."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_consumer")
+    assert os.path.exists(exe), "build the library first: it also builds the C consumer"
+    wl = W.WORKLOADS["tiny"]
+    T, D, E, K = wl.T, wl.D, wl.E, wl.K
+    inp = W.dispatch_inputs(wl, out0="normal")
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(fin, "wb") as f:
+        f.write(np.array([T, E, K, D], np.int32).tobytes())
+        for arr in (inp.scores, inp.x, inp.y, inp.out0):
+            f.write(np.ascontiguousarray(arr).tobytes())
+    say("c consumer", T, D, E, K)
+    r = subprocess.run([exe, str(fin), str(fout)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    buf = np.fromfile(fout, dtype=np.uint8)
+    a = T * K
+    sizes = [(E + 1) * 4, a * 4, a * 4, a * 4, a * D * 2, T * D * 2]
+    assert buf.size == sum(sizes)
+    parts = np.split(buf, np.cumsum(sizes)[:-1])
+    gc, gei, gti, grop = (p.view(np.int32) for p in parts[:4])
+    rows, out = parts[4].view(np.uint16).reshape(a, D), parts[5].view(np.uint16).reshape(T, D)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, K)
+    V = int(counts[E])
+    assert np.array_equal(gc, counts) and np.array_equal(gei, ei) and np.array_equal(gti, ti)
+    assert np.array_equal(grop, rop.ravel())
+    assert np.array_equal(rows[:V], orc.gather_scale(inp.x, ti, ei, inp.scores, V)[:V])
+    assert np.array_equal(out, orc.scatter_add(inp.out0.copy(), inp.y, ti, V))
