@@ -292,6 +292,8 @@ __global__ void csr_fill_kernel(const int* __restrict__ ti, int T, int a,
 constexpr int kRangeT = 256;           // tokens per workgroup
 constexpr int kRangeMaxRows = 131072;  // rows read twice by every workgroup
 constexpr int kRangeUnroll = 8;        // index loads in flight per thread
+constexpr int kRangeStage = 8192;      // a range's rows kept in LDS for the fill
+static_assert(kRangeT <= 256, "the staged fill packs the token offset in 8 bits");
 
 __device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* wave_tot,
                                                int& total) {
@@ -319,6 +321,9 @@ __global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
     int* __restrict__ list) {
   __shared__ int cnt[kRangeT];
   __shared__ int wave_tot[3][kScanThreads / kWave];
+  __shared__ int stage_row[kRangeStage];
+  __shared__ int stage_pos[kRangeStage];  // token offset | slot << 8
+  __shared__ int nstage;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
@@ -338,11 +343,14 @@ __global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
     V = clamp_count(vrows, a);
   }
   if (tid < kRangeT) cnt[tid] = 0;
+  if (tid == 0) nstage = 0;
   __syncthreads();
 
-  // pass 1: count this range's rows; rows of tokens below it in `below`.
-  // Every load of a batch issues before the first use (clamped index; rows
-  // past V are dropped by the select).
+  // pass 1: count this range's rows -- each takes its slot within its token
+  // and is staged in LDS (one position counter update per wave and batch) --
+  // and the rows of tokens below the range in `below`. Every load of a batch
+  // issues before the first use (clamped index; rows past V are dropped by
+  // the select).
   int below = 0;
   for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
     int tv[kRangeUnroll];
@@ -355,8 +363,23 @@ __global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
 #pragma unroll
     for (int u = 0; u < kRangeUnroll; ++u) {
       const int rel = tv[u] - lo;
-      if (static_cast<unsigned>(rel) < static_cast<unsigned>(n)) atomicAdd(&cnt[rel], 1);
-      else if (static_cast<unsigned>(tv[u]) < static_cast<unsigned>(lo)) ++below;
+      const bool in = static_cast<unsigned>(rel) < static_cast<unsigned>(n);
+      if (!in && static_cast<unsigned>(tv[u]) < static_cast<unsigned>(lo)) ++below;
+      const uint64_t m = __ballot(in);
+      if (m != 0) {  // wave-uniform
+        const int leader = __builtin_ctzll(m);
+        int wbase = 0;
+        if (lane == leader) wbase = atomicAdd(&nstage, __popcll(m));
+        wbase = __shfl(wbase, leader, kWave);
+        if (in) {
+          const int slot = atomicAdd(&cnt[rel], 1);
+          const int sp = wbase + __popcll(m & ((uint64_t{1} << lane) - 1u));
+          if (sp < kRangeStage) {
+            stage_row[sp] = r0 + u * kScanThreads + tid;
+            stage_pos[sp] = rel | (slot << 8);
+          }
+        }
+      }
     }
   }
   int below_total;
@@ -373,7 +396,17 @@ __global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
   if (lo + n == T && tid == 0) start[T] = below_total + range_total;
   __syncthreads();
 
-  // pass 2: each of this range's rows takes the next free slot of its token
+  // fill: staged rows go straight to start + slot; a range with more rows
+  // than the stage holds reads the indices again instead, each row taking the
+  // next free position of its token
+  const int ns = nstage;
+  if (ns <= kRangeStage) {
+    for (int i = tid; i < ns; i += kScanThreads) {
+      const int p = stage_pos[i];
+      list[cnt[p & 0xFF] + (p >> 8)] = stage_row[i];
+    }
+    return;
+  }
   for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
     int tv[kRangeUnroll];
 #pragma unroll

@@ -319,6 +319,28 @@ def test_scatter_add_csr_multi_launch(dev):
     assert np.array_equal(bits_host(out), want)
 
 
+def test_scatter_add_csr_stage_overflow(dev):
+    """One 256-token range owning more rows (10000) than the CSR build stages
+    in LDS (8192): the build falls back to a second pass over the indices."""
+    g = np.random.default_rng(13)
+    T, D, a = 100, 64, 10000
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("csr stage overflow", T, D, a)
+    want = orc.scatter_add(out0.copy(), y, ti, a)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev))
+    assert np.array_equal(bits_host(out), want)
+    # the padded layout: 4 experts over 2 ranks, all rows valid
+    counts = np.array([3000, 2500, 2500, 2000], np.int32)
+    slabs = W.to_bf16_bits(g.standard_normal((2, a, D)).astype(np.float32))
+    want = orc.scatter_add_padded(out0.copy(), slabs, counts, ti)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts, dev), i32_dev(ti, dev), out)
+    assert np.array_equal(bits_host(out), want)
+
+
 # ---------------------------------------------------------------- EP re-sort
 SHUFFLING_CASES = [
     # (name, EP, C, c_lo, c_hi, packed, max count, D)
