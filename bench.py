@@ -20,8 +20,12 @@ resident in HBM:
 A step launches its kernels from Python (--graph replays a HIP graph of the
 step instead; a graph launch costs more than a few kernel launches here). W
 untimed steps, then exactly K timed steps between two device
-synchronisations (wall clock, and a HIP event pair around the region). Then
-each stage alone: K launches captured back to back in one HIP graph, replayed
+synchronisations (wall clock, and a HIP event pair around the region): the
+warm steps behind `value`. Then K cold steps, each after a flush of L2 and the
+256 MB Infinity Cache -- a 1 GiB read (clean eviction) or a 1 GiB write (whose
+dirty lines the step then writes back) -- device time with the flushes' own
+time subtracted, reported under "cold" with each stage alone after a read
+flush. Then each stage alone: K launches captured back to back in one HIP graph, replayed
 once between one HIP event pair on the stream the kernels run on (an event
 between two kernels costs the stream ~10 us, so neither region records one
 inside): each stage's average duration per launch, the kernels' own time. The longest stage is the roofline kernel: its algorithmic bytes
@@ -402,6 +406,47 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     region_ms = region[0].elapsed_time(region[1])
+    # ---- cold steps: before each step a 1 GiB buffer is read (a sum), which
+    # evicts the step's data from L2 and the 256 MB Infinity Cache without
+    # leaving dirty lines behind; the same with a 1 GiB write, whose dirty
+    # lines the next step then writes back. Each flush alone is timed the same
+    # way and subtracted, so no event sits between a flush and its step.
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush_read():
+        torch.sum(flush_buf, dim=0, out=flush_sum)
+
+    def flush_write():
+        flush_buf.fill_(1.0)
+
+    def time_region(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    cold = {}
+    for kind, fl in (("read", flush_read), ("write", flush_write)):
+        def flush_step():
+            fl()
+            run_step()
+        flush_step()
+        cold[kind] = (time_region(flush_step) - time_region(fl)) / steps
+    # each stage alone after a read flush
+    t_flush = time_region(flush_read)
+    cold_stage = {}
+    for n, fn in stages:
+        def flush_stage():
+            flush_read()
+            fn()
+        flush_stage()
+        cold_stage[n] = (time_region(flush_stage) - t_flush) / steps
+    del flush_buf
     # ---- each stage alone, `steps` launches back to back: its average
     # duration per launch, the denominator of the roofline
     names = [n for n, _ in stages]
@@ -436,6 +481,12 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {**s.config, "launch": "one HIP graph per step" if graph else
                    "eager (kernels launched from Python)"},
+        "cold": {**{kind: {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
+                           "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                    for kind, ms in cold.items()},
+                 "stage_us_after_read": {n: round(cold_stage[n] * 1e3, 2) for n in names},
+                 "roofline_frac_after_read":
+                     s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stage_us": {n: round(st_ms[n] * 1e3, 2) for n in names},
