@@ -34,9 +34,9 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxQuantD = 65536;     // 16 waves * 64 lanes * 8 chunks * 8
-constexpr int kMaxFinalizeD = 65536;
-constexpr int kMaxMhcD = 32768;      // 16 waves x 64 lanes x 4 chunks x 8
-constexpr int kMaxMhcStreams = 4;  // same bound for the finalize workgroup
+constexpr int kMaxFinalizeD = 65536;  // same bound for the finalize workgroup
+constexpr int kMaxMhcD = 32768;       // 16 waves * 64 lanes * 4 chunks * 8
+constexpr int kMaxMhcStreams = 4;
 
 #define REQUIRE(cond, status, ...) \
   do {                             \
