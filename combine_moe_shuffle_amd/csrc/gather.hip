@@ -91,26 +91,18 @@ __global__ __launch_bounds__(kRowWaves* kWave) void gather_rows_kernel(
     scale_slice<CPL, false>(src, dst, s, slice0 + lane, nch);
 }
 
+// One token's slice, written to each of its valid rows scaled by that row's
+// score. Lane k holds slot k's row (my_r) and score (my_s); `valid` marks the
+// slots to write.
 template <int CPL, bool FULL>
-__device__ __forceinline__ void scatter_token_slice(const uint16_t* __restrict__ src,
-                                                    uint16_t* __restrict__ out, int D,
-                                                    const float* __restrict__ srow,
-                                                    int64_t se, const int* __restrict__ ei,
-                                                    int E, int my_r, uint64_t valid, int base,
+__device__ __forceinline__ void scatter_token_slice(const u32x4 (&v)[CPL],
+                                                    uint16_t* __restrict__ out, int D, int my_r,
+                                                    float my_s, uint64_t valid, int base,
                                                     int nch) {
-  // plain loads: measured faster here than non-temporal ones
-  u32x4 v[CPL];
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = base + j * kWave;
-    if (FULL || c < nch) v[j] = ld16(src + c * kChunk);
-  }
   for (uint64_t m = valid; m; m &= m - 1) {
     const int k = __builtin_ctzll(m);
     const int r = __builtin_amdgcn_readlane(my_r, k);
-    const int e = ei[r];
-    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;  // skipped
-    const float s = srow[static_cast<int64_t>(e) * se];
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
     uint16_t* dst = out + static_cast<int64_t>(r) * D;
     u32x4 o[CPL];
 #pragma unroll
@@ -127,6 +119,28 @@ __device__ __forceinline__ void scatter_token_slice(const uint16_t* __restrict__
       if (FULL || c < nch) st16_stream(dst + c * kChunk, o[j]);
     }
   }
+}
+
+// Dependent loads per wave: the token's slot rows; then, at once, the x slice
+// and every slot's expert id (lane k fetches slot k's); then every slot's
+// score; then the K row writes.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void gather_token(const uint16_t* __restrict__ src,
+                                             uint16_t* __restrict__ out, int D,
+                                             const float* __restrict__ srow, int64_t se,
+                                             const int* __restrict__ ei, int E, int my_r,
+                                             uint64_t valid, int base, int nch) {
+  // plain loads for x: measured faster here than non-temporal ones
+  u32x4 v[CPL];
+  const int my_e = my_r >= 0 ? ei[my_r] : -1;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = base + j * kWave;
+    if (FULL || c < nch) v[j] = ld16(src + c * kChunk);
+  }
+  const bool ok = static_cast<unsigned>(my_e) < static_cast<unsigned>(E);  // else skipped
+  const float my_s = ok ? srow[static_cast<int64_t>(my_e) * se] : 0.0f;
+  scatter_token_slice<CPL, FULL>(v, out, D, my_r, my_s, valid & __ballot(ok), base, nch);
 }
 
 template <int CPL>
@@ -152,11 +166,9 @@ __global__ __launch_bounds__(kRowWaves* kWave) void gather_tokens_kernel(
   const float* srow = scores + static_cast<int64_t>(t) * st;
   const int slice0 = sl * kWave * CPL;
   if (slice0 + kWave * CPL <= nch)
-    scatter_token_slice<CPL, true>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane,
-                                   nch);
+    gather_token<CPL, true>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
   else
-    scatter_token_slice<CPL, false>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane,
-                                    nch);
+    gather_token<CPL, false>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
 }
 
 constexpr float kRowwiseEps = 1e-12f;
