@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="zipf", choices=WORKLOAD_CHOICES)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold-cache steps (profiling runs: every launch then warm)")
     p.add_argument("--graph", action="store_true",
                    help="replay a HIP graph of the step instead of launching its kernels from "
                         "Python (a graph launch costs more than a few kernel launches here)")
@@ -431,16 +433,17 @@ def main():
         return e0.elapsed_time(e1)
 
     cold = {}
-    for kind, fl in (("read", flush_read), ("write", flush_write)):
+    cold_stage = {}
+    kinds = () if args.no_cold else (("read", flush_read), ("write", flush_write))
+    for kind, fl in kinds:
         def flush_step():
             fl()
             run_step()
         flush_step()
         cold[kind] = (time_region(flush_step) - time_region(fl)) / steps
     # each stage alone after a read flush
-    t_flush = time_region(flush_read)
-    cold_stage = {}
-    for n, fn in stages:
+    t_flush = 0.0 if args.no_cold else time_region(flush_read)
+    for n, fn in ([] if args.no_cold else stages):
         def flush_stage():
             flush_read()
             fn()
@@ -481,12 +484,13 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {**s.config, "launch": "one HIP graph per step" if graph else
                    "eager (kernels launched from Python)"},
-        "cold": {**{kind: {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
-                           "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-                    for kind, ms in cold.items()},
-                 "stage_us_after_read": {n: round(cold_stage[n] * 1e3, 2) for n in names},
-                 "roofline_frac_after_read":
-                     s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "cold": None if args.no_cold else {
+            **{kind: {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
+                      "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+               for kind, ms in cold.items()},
+            "stage_us_after_read": {n: round(cold_stage[n] * 1e3, 2) for n in names},
+            "roofline_frac_after_read":
+                s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stage_us": {n: round(st_ms[n] * 1e3, 2) for n in names},
