@@ -18,17 +18,22 @@ resident in HBM:
   shuffling rows from EP=8 source ranks for one rank's 32 local experts:
             moe_combine_shuffling -> moe_split_shuffling
 A step launches its kernels from Python (--graph replays a HIP graph of the
-step instead; a graph launch costs more than a few kernel launches here). W
-untimed steps, then exactly K timed steps between two device
-synchronisations (wall clock, and a HIP event pair around the region): the
-warm steps behind `value`. Then K cold steps, each after a flush of L2 and the
-256 MB Infinity Cache -- a 1 GiB read (clean eviction) or a 1 GiB write (whose
-dirty lines the step then writes back) -- device time with the flushes' own
-time subtracted, reported under "cold" with each stage alone after a read
-flush. Then each stage alone: K launches captured back to back in one HIP graph, replayed
-once between one HIP event pair on the stream the kernels run on (an event
-between two kernels costs the stream ~10 us, so neither region records one
-inside): each stage's average duration per launch, the kernels' own time. The longest stage is the roofline kernel: its algorithmic bytes
+step instead; a graph launch costs more than a few kernel launches here).
+
+1. W untimed steps, then exactly K timed steps between two device
+   synchronisations (wall clock, and a HIP event pair around the region): the
+   warm steps behind `value`.
+2. K cold steps, each after a flush of L2 and the 256 MB Infinity Cache -- a
+   1 GiB read (clean eviction) or a 1 GiB write (whose dirty lines the step
+   then writes back) -- device time with the flushes' own time subtracted,
+   reported under "cold" with each stage alone after a read flush
+   (--no-cold skips them, for profiling runs).
+3. Each stage alone: K launches captured back to back in one HIP graph,
+   replayed once between one HIP event pair on the stream the kernels run on:
+   each stage's average duration per launch, the kernels' own time.
+
+An event between two kernels costs the stream ~10 us, so no region records
+one inside. The longest stage is the roofline kernel: its algorithmic bytes
 per launch (unique inputs read once, outputs written once, valid rows only)
 over that duration, against the 8 TB/s HBM peak.
 

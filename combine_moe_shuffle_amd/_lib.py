@@ -1,7 +1,11 @@
 """Loads libmoe_shuffle.so (built in-tree by combine_moe_shuffle_amd.build)
 and declares the C ABI of include/moe_shuffle.h for ctypes.
 
-There is no fallback: if the library is missing, every op raises.
+The launching entry points are called through the _moe_fastcall extension
+when it is built (one compiled call that parses plain ints and floats, no
+per-argument ctypes conversion), else through ctypes; both call the same
+library. There is no fallback beyond that: if the library is missing, every
+op raises.
 """
 from __future__ import annotations
 
@@ -63,6 +67,36 @@ class MoeError(RuntimeError):
 
 
 _lib = None
+_fast = None
+_fast_tried = False
+
+
+def fast():
+    """The compiled fast-call module, or None when it is not built."""
+    global _fast, _fast_tried
+    if not _fast_tried:
+        _fast_tried = True
+        try:
+            from . import _moe_fastcall
+            _fast = _moe_fastcall
+        except ImportError:
+            _fast = None
+    return _fast
+
+
+_fns = {}
+
+
+def fn(name: str):
+    """The callable for a status-returning entry point: pointers as ints
+    (0 for NULL), sizes as ints, floats as floats, the stream handle as an
+    int."""
+    f = _fns.get(name)
+    if f is None:
+        mod = fast()
+        f = getattr(mod, name) if mod is not None else getattr(load(), name)
+        _fns[name] = f
+    return f
 
 
 def load() -> ctypes.CDLL:
@@ -84,5 +118,7 @@ def load() -> ctypes.CDLL:
 
 def check(status: int) -> None:
     if status != 0:
-        msg = load().moe_last_error().decode(errors="replace")
+        mod = fast()
+        msg = (mod.last_error() if mod is not None
+               else load().moe_last_error().decode(errors="replace"))
         raise MoeError(status, msg)

@@ -31,7 +31,7 @@ def _stream(device):
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    return 0 if t is None else t.data_ptr()
 
 
 def _need(t, name, dtype, ndim=None, device=None):
@@ -100,7 +100,7 @@ def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspac
     need = lib.moe_shuffle_workspace_bytes(T, E, K)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    _lib.check(lib.moe_shuffle(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
+    _lib.check(_lib.fn("moe_shuffle")(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
                                _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace),
                                workspace.numel(), _stream(device)))
     return counts, ei, ti, rop
@@ -135,7 +135,7 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
     _contig(out, "out")
     if tuple(out.shape) != (a, D):
         raise ValueError("out must be (a, D)")
-    _lib.check(_lib.load().moe_gather_scale(
+    _lib.check(_lib.fn("moe_gather_scale")(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
         scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
     return out
@@ -158,7 +158,7 @@ def moe_gather_scale_by_token(x, row_of_pair, expert_indices, scores, valid_rows
     _contig(out, "out")
     if tuple(out.shape) != (a, D):
         raise ValueError("out must be (a, D)")
-    _lib.check(_lib.load().moe_gather_scale_by_token(
+    _lib.check(_lib.fn("moe_gather_scale_by_token")(
         _ptr(x), T, D, _ptr(row_of_pair), K, _ptr(expert_indices), a, _ptr(scores), st, se,
         scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
     return out
@@ -183,7 +183,7 @@ def moe_gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=No
     _need(out, "out", torch.uint8, 2, device)
     _need(out_scale, "out_scale", torch.float32, 1, device)
     _contig(out, "out")
-    _lib.check(_lib.load().moe_gather_scale_quant(
+    _lib.check(_lib.fn("moe_gather_scale_quant")(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
         scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream(device)))
     return out, out_scale
@@ -214,7 +214,7 @@ def moe_scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None, works
     need = lib.moe_scatter_add_workspace_bytes(T, a)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    _lib.check(lib.moe_scatter_add(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
+    _lib.check(_lib.fn("moe_scatter_add")(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
                                    a, D, _ptr(vr), _ptr(workspace), workspace.numel(),
                                    _stream(device)))
     return out_tokens
@@ -228,7 +228,7 @@ def moe_scatter_add_by_token(out_tokens, in_tokens, row_of_pair, valid_rows=None
     T, D = out_tokens.shape
     if row_of_pair.shape[0] != T:
         raise ValueError("row_of_pair must be (T, K)")
-    _lib.check(_lib.load().moe_scatter_add_by_token(
+    _lib.check(_lib.fn("moe_scatter_add_by_token")(
         _ptr(out_tokens), T, _ptr(in_tokens), _ptr(row_of_pair), row_of_pair.shape[1],
         in_tokens.shape[0], D, _ptr(vr), _stream(device)))
     return out_tokens
@@ -254,7 +254,7 @@ def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, w
     need = lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    _lib.check(lib.moe_scatter_add_padded(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
+    _lib.check(_lib.fn("moe_scatter_add_padded")(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
                                           _ptr(token_indices), _ptr(out_tokens), T, D,
                                           _ptr(workspace), workspace.numel(), _stream(device)))
     return out_tokens
@@ -282,7 +282,7 @@ def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, wit
     need = lib.moe_shuffling_workspace_bytes(EP, c_hi - c_lo, em_rows)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-    _lib.check(getattr(lib, name)(
+    _lib.check(_lib.fn(name)(
         _ptr(tokens), tokens.shape[0], _ptr(out), out.shape[0], D, _ptr(counts), EP, C, c_lo,
         c_hi, -1 if rank_stride is None else int(rank_stride), _ptr(oc), _ptr(workspace),
         workspace.numel(), _stream(device)))
@@ -385,7 +385,7 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
         out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
-    _lib.check(_lib.load().moe_finalize_rmsnorm(
+    _lib.check(_lib.fn("moe_finalize_rmsnorm")(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
         _stream(device)))
@@ -434,10 +434,10 @@ def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, 
         out = None
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
-    _lib.check(_lib.load().moe_finalize_mhc(
+    _lib.check(_lib.fn("moe_finalize_mhc")(
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),
-        _ptr(gamma) if pre is not None else None, float(eps), T, K, D, hc, int(flags),
+        _ptr(gamma) if pre is not None else 0, float(eps), T, K, D, hc, int(flags),
         _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream(device)))
     return (residual_out, out, codes, scales) if mxfp8 else (residual_out, out)
 
@@ -450,7 +450,7 @@ def moe_convert_check(values):
     n = values.numel()
     bf = torch.empty(n, dtype=torch.int16, device=values.device)
     e4 = torch.empty(n, dtype=torch.uint8, device=values.device)
-    _lib.check(_lib.load().moe_convert_check(_ptr(values), n, _ptr(bf), _ptr(e4),
+    _lib.check(_lib.fn("moe_convert_check")(_ptr(values), n, _ptr(bf), _ptr(e4),
                                              _stream(values.device)))
     return bf, e4
 

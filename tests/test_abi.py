@@ -267,3 +267,35 @@ def test_ops_raise_without_gpu_tensors():
         ops.moe_gather_scale(torch.zeros(4, 16, dtype=torch.bfloat16),
                              torch.zeros(8, dtype=torch.int32),
                              torch.zeros(8, dtype=torch.int32), torch.zeros(4, 2))
+
+
+def test_fast_call_module_covers_every_launching_entry_point(lib):
+    """The compiled fast-call extension wraps every status-returning entry
+    point of the signature table, with the same arity."""
+    fast = _lib.fast()
+    assert fast is not None, "the fast-call extension is built with the library"
+    for name, (res, args) in _lib.SIGNATURES.items():
+        if res is not ctypes.c_int or not args:
+            continue
+        f = getattr(fast, name)
+        with pytest.raises(TypeError):
+            f(*([0] * (len(args) - 1)))  # one argument short
+
+
+@host_only
+def test_fast_call_rejects_like_ctypes(lib):
+    """Host-side rejections give the same status and message through the
+    extension as through ctypes."""
+    fast = _lib.fast()
+    calls = [
+        ("moe_finalize_rmsnorm",
+         (FAKE, 64, FAKE, FAKE, 0, FAKE, 1e-6, 8, 65, 256, 0, FAKE, 0, 0, 0)),
+        ("moe_shuffle", (FAKE, 8, 1, 4, 8, 9, 0, FAKE, FAKE, FAKE, 0, FAKE, 1 << 20, 0)),
+        ("moe_scatter_add", (FAKE, 8, FAKE, FAKE, 16, 64, 0, FAKE, 16, 0)),
+    ]
+    for name, args in calls:
+        s_fast = getattr(fast, name)(*args)
+        m_fast = fast.last_error()
+        s_ct = getattr(lib, name)(*args)
+        m_ct = lib.moe_last_error().decode()
+        assert s_fast == s_ct != OK and m_fast == m_ct, name
