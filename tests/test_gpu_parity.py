@@ -810,3 +810,86 @@ def test_c_abi_consumer(dev, tmp_path):
     assert np.array_equal(grop, rop.ravel())
     assert np.array_equal(rows[:V], orc.gather_scale(inp.x, ti, ei, inp.scores, V)[:V])
     assert np.array_equal(out, orc.scatter_add(inp.out0.copy(), inp.y, ti, V))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_randomized_shapes_against_oracle(dev, seed):
+    """Seeded random shapes through every entry point: T, D, E, K, the valid
+    count, score strides and EP drawn per seed; every output checked."""
+    g = np.random.default_rng(1000 + seed)
+    T = int(g.integers(1, 300))
+    E = int(g.integers(1, 300))
+    K = int(g.integers(1, min(E, 16) + 1))
+    D = 8 * int(g.integers(1, 260))
+    vtc = None if g.random() < 0.3 else int(g.integers(0, T + 1))
+    say("random", seed, T, D, E, K, vtc)
+    s = g.standard_normal((T, E)).astype(np.float32)
+    if g.random() < 0.3:
+        s = np.round(s * 2) / 2                        # ties
+    x = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    y = W.to_bf16_bits(g.standard_normal((T * K, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    counts, ei, ti, rop = orc.shuffle(s, K, vtc)
+    V = int(counts[E])
+    if g.random() < 0.5:
+        sd = torch.from_numpy(np.ascontiguousarray(s.T)).to(dev).t()
+    else:
+        sd = torch.from_numpy(s).to(dev)
+    gc, gei, gti, grop = ops.moe_shuffle(sd, K, scalar_dev(vtc, dev))
+    assert np.array_equal(gc.cpu().numpy(), counts)
+    assert np.array_equal(gti.cpu().numpy(), ti) and np.array_equal(gei.cpu().numpy(), ei)
+    assert np.array_equal(grop.cpu().numpy(), rop)
+    vr = gc[E:]
+    want_rows = orc.gather_scale(x, ti, ei, s, V)
+    for path in ("rows", "by_token"):
+        rows = torch.zeros((T * K, D), dtype=torch.bfloat16, device=dev)
+        if path == "rows":
+            ops.moe_gather_scale(bf_dev(x, dev), gti, gei, sd, vr, rows)
+        else:
+            ops.moe_gather_scale_by_token(bf_dev(x, dev), grop, gei, sd, vr, rows)
+        assert np.array_equal(bits_host(rows)[:V], want_rows[:V]), path
+    wq, wsc = orc.gather_scale_quant(x, ti, ei, s, None, V)
+    q, qs = ops.moe_gather_scale_quant(bf_dev(x, dev), gti, gei, sd, None, vr)
+    assert np.array_equal(q.cpu().numpy()[:V], wq[:V])
+    assert np.array_equal(qs.cpu().numpy()[:V].view(np.uint32), wsc[:V].view(np.uint32))
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    for path in ("general", "by_token"):
+        out = bf_dev(out0, dev)
+        if path == "general":
+            ops.moe_scatter_add(out, bf_dev(y, dev), gti, vr)
+        else:
+            ops.moe_scatter_add_by_token(out, bf_dev(y, dev), grop, vr)
+        assert np.array_equal(bits_host(out), want), path
+    # padded combine over a divisor of E
+    EP = int(g.choice([d for d in range(1, min(E, 8) + 1) if E % d == 0]))
+    slabs = W.to_bf16_bits(g.standard_normal((EP, T * K, D)).astype(np.float32))
+    want = orc.scatter_add_padded(out0.copy(), slabs, counts[:E], ti)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:E].contiguous(), gti, out)
+    assert np.array_equal(bits_host(out), want)
+    # finalize and mHC on the shuffle's rows (D a multiple of 32 for MXFP8)
+    Df = 32 * max(1, D // 32)
+    yf = W.to_bf16_bits(g.standard_normal((T * K, Df)).astype(np.float32))
+    w = g.random((T, K)).astype(np.float32)
+    shared = W.to_bf16_bits(g.standard_normal((T, Df)).astype(np.float32))
+    gamma = W.to_bf16_bits(g.uniform(0.5, 1.5, Df).astype(np.float32))
+    want_o = orc.finalize_rmsnorm(yf, w, rop, shared, gamma, 1e-6)
+    o, mc, ms = ops.moe_finalize_rmsnorm(bf_dev(yf, dev), torch.from_numpy(w).to(dev), grop,
+                                         bf_dev(shared, dev), bf_dev(gamma, dev), 1e-6,
+                                         mxfp8=True)
+    got = bits_host(o)
+    _close(got, want_o, "finalize")
+    oc, os_ = orc.mxfp8_quantize(got)
+    assert np.array_equal(mc.cpu().numpy(), oc) and np.array_equal(ms.cpu().numpy(), os_)
+    hc = int(g.integers(1, 5))
+    res = W.to_bf16_bits(g.standard_normal((T, hc, Df)).astype(np.float32))
+    post = g.uniform(0, 2, (T, hc)).astype(np.float32)
+    comb = g.random((T, hc, hc)).astype(np.float32)
+    pre = g.random((T, hc)).astype(np.float32)
+    wres, wout, _, _ = orc.finalize_mhc(yf, w, rop, shared, res, post, comb, pre, gamma, 1e-6)
+    f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+    r_out, m_out = ops.moe_finalize_mhc(bf_dev(yf, dev), f32(w), grop, bf_dev(shared, dev),
+                                        bf_dev(res, dev), f32(post), f32(comb), f32(pre),
+                                        bf_dev(gamma, dev), 1e-6)
+    _close(bits_host(r_out), wres, "mhc residual")
+    _close(bits_host(m_out), wout, "mhc out")
