@@ -893,3 +893,70 @@ def test_randomized_shapes_against_oracle(dev, seed):
                                         bf_dev(gamma, dev), 1e-6)
     _close(bits_host(r_out), wres, "mhc residual")
     _close(bits_host(m_out), wout, "mhc out")
+
+
+def test_every_op_is_deterministic(dev):
+    """Each entry point run three times on the same inputs gives the same
+    bits, including the combines whose row lists are built with atomics
+    (here with up to 40 rows on one token)."""
+    g = np.random.default_rng(77)
+    T, D, E, K = 300, 640, 32, 8
+    s = torch.from_numpy(g.standard_normal((T, E)).astype(np.float32)).to(dev)
+    x = bf_dev(W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32)), dev)
+    y = bf_dev(W.to_bf16_bits(g.standard_normal((T * K, D)).astype(np.float32)), dev)
+    out0 = bf_dev(W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32)), dev)
+    ti_hot = np.where(g.random(T * K) < 0.02, 7, g.integers(0, T, T * K)).astype(np.int32)
+    ti_hot = i32_dev(ti_hot, dev)
+    say("determinism", T, D, E, K)
+
+    def run_once():
+        counts, ei, ti, rop = ops.moe_shuffle(s, K, scalar_dev(250, dev))
+        vr = counts[E:]
+        rows = ops.moe_gather_scale_by_token(x, rop, ei, s, vr,
+                                             torch.zeros((T * K, D), dtype=torch.bfloat16,
+                                                         device=dev))
+        q, qs = ops.moe_gather_scale_quant(x, ti, ei, s, None, vr)
+        a = out0.clone()
+        ops.moe_scatter_add(a, y, ti_hot)
+        b = out0.clone()
+        ops.moe_scatter_add_padded(y.view(2, T * K // 2, D).repeat(1, 2, 1).contiguous(),
+                                   torch.full((E,), T * K // E, dtype=torch.int32, device=dev),
+                                   ti_hot, b)
+        c = out0.clone()
+        ops.moe_scatter_add_by_token(c, y, rop, vr)
+        w = torch.rand((T, K), device=dev)
+        o, mc, ms = ops.moe_finalize_rmsnorm(y, w, rop, out0, x[0].contiguous(), 1e-6,
+                                             mxfp8=True)
+        torch.cuda.synchronize()
+        V = int(counts[E].item())  # rows past V of the FP8 outputs are not written
+        return [t.cpu() for t in (counts, ei, ti, rop, rows, q[:V], qs[:V], a, b, c,
+                                  o, mc, ms)], w
+
+    first, w0 = run_once()
+    for _ in range(2):
+        again, w = run_once()
+        for i, (u, v) in enumerate(zip(first[:10], again[:10])):
+            assert torch.equal(u, v), i
+    # the finalize with the same weights both times
+    counts, ei, ti, rop = ops.moe_shuffle(s, K, scalar_dev(250, dev))
+    outs = [ops.moe_finalize_rmsnorm(y, w0, rop, out0, x[0].contiguous(), 1e-6,
+                                     mxfp8=True) for _ in range(3)]
+    for o, mc, ms in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(mc, outs[0][1])
+        assert torch.equal(ms, outs[0][2])
+
+
+def test_zero_width_rows_are_no_ops(dev):
+    """D = 0: every row entry point returns without touching anything."""
+    say("zero-width rows")
+    T, E, K = 6, 4, 2
+    z = torch.empty((T, 0), dtype=torch.bfloat16, device=dev)
+    zi = torch.zeros(T * K, dtype=torch.int32, device=dev)
+    s = torch.rand((T, E), device=dev)
+    ops.moe_gather_scale(z, zi, zi, s, out=torch.empty((T * K, 0), dtype=torch.bfloat16,
+                                                      device=dev))
+    ops.moe_gather_scale_quant(z, zi, zi, s)
+    ops.moe_scatter_add(z.clone(), torch.empty((T * K, 0), dtype=torch.bfloat16, device=dev), zi)
+    ops.moe_scatter_add_by_token(z.clone(), torch.empty((T * K, 0), dtype=torch.bfloat16,
+                                                        device=dev), zi.view(T, K))
+    torch.cuda.synchronize()
