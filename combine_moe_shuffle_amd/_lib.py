@@ -31,8 +31,9 @@ SIGNATURES = {
     "moe_shuffle_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_shuffle": (_status, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
                               _sz, _p]),
+    "moe_gather_scale_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_gather_scale": (_status, [_p, _i32, _i32, _p, _p, _i32, _p, _i64, _i64, _i32, _p,
-                                   _p, _p]),
+                                   _p, _p, _sz, _p]),
     "moe_gather_scale_by_token": (_status, [_p, _i32, _i32, _p, _i32, _p, _i32, _p, _i64,
                                             _i64, _i32, _p, _p, _p]),
     "moe_gather_scale_quant": (_status, [_p, _i32, _i32, _p, _p, _i32, _p, _i64, _i64, _i32,

@@ -128,17 +128,30 @@ static moe_status_t check_gather(const moe_bf16_t* x, int32_t T, int32_t D, int3
   return MOE_OK;
 }
 
+size_t moe_gather_scale_workspace_bytes(int32_t T, int32_t a) {
+  if (T < 0 || a < 0) return 0;
+  return moe::scatter_add_workspace_bytes(T, a);
+}
+
 moe_status_t moe_gather_scale(const moe_bf16_t* x, int32_t T, int32_t D,
                               const int32_t* token_indices, const int32_t* expert_indices,
                               int32_t a, const float* scores, int64_t stride_t,
                               int64_t stride_e, int32_t E, const int32_t* valid_rows,
-                              moe_bf16_t* out, void* stream) {
+                              moe_bf16_t* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   moe_status_t s = check_gather(x, T, D, a, scores, stride_t, stride_e, E, out, 16);
   if (s != MOE_OK) return s;
   if (a == 0 || D == 0) return ok();
   REQUIRE(token_indices && expert_indices, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  if (workspace != nullptr) {
+    const size_t need = moe::scatter_add_workspace_bytes(T, a);
+    REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE,
+            "gather_scale workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    REQUIRE(aligned(workspace, 256), MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  if (T == 0) return ok();  // no token row exists, so no row is written
   return hip_status(moe::launch_gather_scale(x, T, D, token_indices, expert_indices, a, scores,
-                                             stride_t, stride_e, E, valid_rows, out,
+                                             stride_t, stride_e, E, valid_rows, out, workspace,
                                              static_cast<hipStream_t>(stream)),
                     "moe_gather_scale");
 }

@@ -658,18 +658,20 @@ hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
-                              int a, int D, const int* valid_rows, void* workspace,
+hipError_t launch_token_lists(const int* ti, int T, int a, const int* valid_rows,
+                              void* workspace, const int** start, const int** list,
                               hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int* cnt = reinterpret_cast<int*>(ws);  // [T+1]: counts, then starts
   int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
-  int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
-                                     align256(static_cast<size_t>(a) * sizeof(int)));
+  int* lst = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
+                                    align256(static_cast<size_t>(a) * sizeof(int)));
+  *start = cnt;
+  *list = lst;
   if (a <= kRangeMaxRows) {
     hipLaunchKernelGGL(csr_range_build_kernel, dim3((T + kRangeT - 1) / kRangeT),
                        dim3(kScanThreads), 0, stream, ti, T, a, valid_rows, nullptr, 0, nullptr,
-                       cnt, list);
+                       cnt, lst);
   } else {
     hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
                        T + 1);
@@ -678,8 +680,18 @@ hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const in
                        cnt, slot);
     hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, cnt, T);
     hipLaunchKernelGGL(csr_fill_kernel, rgrid, dim3(256), 0, stream, ti, T, a, valid_rows,
-                       cnt, slot, list);
+                       cnt, slot, lst);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
+                              int a, int D, const int* valid_rows, void* workspace,
+                              hipStream_t stream) {
+  const int* cnt;
+  const int* list;
+  const hipError_t e = launch_token_lists(ti, T, a, valid_rows, workspace, &cnt, &list, stream);
+  if (e != hipSuccess) return e;
   const SliceShape sh = combine_shape(D / kChunk);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));

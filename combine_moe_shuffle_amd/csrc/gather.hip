@@ -171,6 +171,37 @@ __global__ __launch_bounds__(kRowWaves* kWave) void gather_tokens_kernel(
     gather_token<CPL, false>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
 }
 
+// The same as gather_tokens_kernel with each token's rows taken from a CSR
+// of token_indices (launch_token_lists) instead of row_of_pair: up to 64 rows
+// per pass, in any order (rows are written, not accumulated).
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void gather_lists_kernel(
+    const uint16_t* __restrict__ x, int T, int E, int D, const int* __restrict__ start,
+    const int* __restrict__ list, const int* __restrict__ ei, const float* __restrict__ scores,
+    int64_t st, int64_t se, uint16_t* __restrict__ out, int nsl) {
+  const int lane = lane_id();
+  const int64_t unit =
+      static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int beg = start[t];
+  const int n = start[t + 1] - beg;
+  const int nch = D >> 3;
+  const uint16_t* src = x + static_cast<int64_t>(t) * D;
+  const float* srow = scores + static_cast<int64_t>(t) * st;
+  const int slice0 = sl * kWave * CPL;
+  const bool full = slice0 + kWave * CPL <= nch;
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int my_r = lane < n - c0 ? list[beg + c0 + lane] : -1;
+    const uint64_t valid = __ballot(my_r >= 0);
+    if (full)
+      gather_token<CPL, true>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
+    else
+      gather_token<CPL, false>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
+  }
+}
+
 constexpr float kRowwiseEps = 1e-12f;
 
 template <int CPL>
@@ -282,8 +313,26 @@ SliceShape pick_slices(int nch, const int* allowed, int n_allowed, int max_slice
 hipError_t launch_gather_scale(const uint16_t* x, int T, int D, const int* ti,
                                const int* ei, int a, const float* scores, int64_t st,
                                int64_t se, int E, const int* valid_rows, uint16_t* out,
-                               hipStream_t stream) {
+                               void* workspace, hipStream_t stream) {
   const SliceShape sh = stream_shape(D / kChunk);
+  if (workspace) {
+    // token order: each x row read once, written to its rows through a CSR
+    // of token_indices built in the workspace
+    const int* start;
+    const int* list;
+    const hipError_t e = launch_token_lists(ti, T, a, valid_rows, workspace, &start, &list,
+                                            stream);
+    if (e != hipSuccess) return e;
+    const int64_t tunits = static_cast<int64_t>(T) * sh.nsl;
+    const dim3 tgrid(static_cast<unsigned>((tunits + kRowWaves - 1) / kRowWaves));
+#define LT(C)                                                                              \
+  hipLaunchKernelGGL(gather_lists_kernel<C>, tgrid, dim3(kRowWaves * kWave), 0, stream, x, T, \
+                     E, D, start, list, ei, scores, st, se, out, sh.nsl)
+    MOE_DISPATCH_CPL(sh.cpl, LT)
+#undef LT
+    return hipGetLastError();
+  }
+  // row order: one wave per (row, slice), x re-read once per route
   const int64_t units = static_cast<int64_t>(a) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);

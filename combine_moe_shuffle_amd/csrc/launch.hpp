@@ -17,10 +17,17 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
                           hipStream_t stream);
 
 // gather.hip
+// The rows of each token in token_indices' valid rows [0, V), as a CSR in a
+// workspace of scatter_add_workspace_bytes(T, a): start[0..T], list[0..V)
+// (the order inside a token's list is not fixed). Tokens outside [0, T) are
+// left out.
+hipError_t launch_token_lists(const int* ti, int T, int a, const int* valid_rows,
+                              void* workspace, const int** start, const int** list,
+                              hipStream_t stream);
 hipError_t launch_gather_scale(const uint16_t* x, int T, int D, const int* ti,
                                const int* ei, int a, const float* scores, int64_t st,
                                int64_t se, int E, const int* valid_rows, uint16_t* out,
-                               hipStream_t stream);
+                               void* workspace, hipStream_t stream);
 hipError_t launch_gather_scale_by_token(const uint16_t* x, int T, int D,
                                         const int* row_of_pair, int K, const int* ei,
                                         int a, const float* scores, int64_t st,

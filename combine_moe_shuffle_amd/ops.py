@@ -119,9 +119,15 @@ def _gather_common(x, expert_indices, scores, valid_rows):
     return device, st, se, _scalar_i32(valid_rows, "valid_rows", device)
 
 
-def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, out=None):
+def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, out=None,
+                     workspace=None, row_order=False):
     """out[i] = bf16(x[token_indices[i]] * scores[t, expert_indices[i]]) for
-    i < valid_rows; other rows of ``out`` are left as they are."""
+    i < valid_rows; other rows of ``out`` are left as they are.
+
+    By default the rows are visited token by token through a list of each
+    token's rows built in ``workspace`` (allocated when None), reading each x
+    row once; ``row_order=True`` visits them row by row with no workspace.
+    Both give the same bits."""
     device, st, se, vr = _gather_common(x, expert_indices, scores, valid_rows)
     _need(token_indices, "token_indices", torch.int32, 1, device)
     _contig(token_indices, "token_indices")
@@ -135,9 +141,17 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
     _contig(out, "out")
     if tuple(out.shape) != (a, D):
         raise ValueError("out must be (a, D)")
+    nbytes = 0
+    if not row_order:
+        need = _lib.load().moe_gather_scale_workspace_bytes(T, a)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        nbytes = workspace.numel()
+    else:
+        workspace = None
     _lib.check(_lib.fn("moe_gather_scale")(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
+        scores.shape[1], _ptr(vr), _ptr(out), _ptr(workspace), nbytes, _stream(device)))
     return out
 
 

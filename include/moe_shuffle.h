@@ -136,18 +136,27 @@ MOE_API moe_status_t moe_shuffle(const float *scores, int64_t stride_t, int64_t 
  * clamped to [0, a], or a when NULL; the pages call it valid_token_count),
  *   t = token_indices[i], e = expert_indices[i],
  *   out[i, :] = bf16_rne( f32(x[t, :]) * scores[t*stride_t + e*stride_e] )
- * (one fp32 multiply per element). Rows i >= V are not written.
+ * (one fp32 multiply per element). Rows i >= V are not written, nor rows
+ * whose t or e is out of range.
+ *
+ * With a workspace (>= moe_gather_scale_workspace_bytes(T, a) bytes,
+ * 256-byte aligned) the rows are visited token by token through a list of
+ * each token's rows built there (one extra launch; four when a > 131072), so
+ * each row of x is read from memory once; with workspace == NULL, row by row
+ * (x re-read once per row that uses it). The output is the same bit for bit.
+ * The workspace is scratch: its contents on entry do not matter.
  *
  * x     [T, D] bf16;  out [a, D] bf16;  token_indices, expert_indices [a] int32
  * D % 8 == 0.
  * ---------------------------------------------------------------------- */
+MOE_API size_t moe_gather_scale_workspace_bytes(int32_t T, int32_t a);
 MOE_API moe_status_t moe_gather_scale(const moe_bf16_t *x, int32_t T, int32_t D,
                               const int32_t *token_indices,
                               const int32_t *expert_indices, int32_t a,
                               const float *scores, int64_t stride_t,
                               int64_t stride_e, int32_t E,
                               const int32_t *valid_rows, moe_bf16_t *out,
-                              void *stream);
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_gather_scale_by_token -- the same output as moe_gather_scale, visiting
  * the rows token by token through the inverse map row_of_pair ([T, K] int32,

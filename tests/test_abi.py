@@ -114,15 +114,23 @@ def test_shuffle_rejects(lib):
 @host_only
 def test_gather_rejects(lib):
     g = lib.moe_gather_scale
-    assert g(FAKE, 4, 12, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID  # D % 8
+    # D % 8
+    assert g(FAKE, 4, 12, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 0, None) == INVALID
     assert "multiple of 8" in _err(lib)
-    assert g(FAKE + 8, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
-    assert g(FAKE, 4, 16, None, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
-    assert g(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 0, None, FAKE, None) == INVALID  # E
-    assert g(FAKE, 4, 16, FAKE, FAKE, -1, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
+    assert g(FAKE + 8, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 0, None) == INVALID
+    assert g(FAKE, 4, 16, None, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None, 0, None) == INVALID
+    # E
+    assert g(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 0, None, FAKE, None, 0, None) == INVALID
+    assert g(FAKE, 4, 16, FAKE, FAKE, -1, FAKE, 4, 1, 4, None, FAKE, None, 0, None) == INVALID
     # nothing to do: OK without touching anything
-    assert g(None, 0, 16, None, None, 0, None, 4, 1, 4, None, None, None) == OK
-    assert g(None, 4, 0, None, None, 8, None, 4, 1, 4, None, None, None) == OK
+    assert g(None, 0, 16, None, None, 0, None, 4, 1, 4, None, None, None, 0, None) == OK
+    assert g(None, 4, 0, None, None, 8, None, 4, 1, 4, None, None, None, 0, None) == OK
+    need = lib.moe_gather_scale_workspace_bytes(4, 8)
+    assert need == lib.moe_scatter_add_workspace_bytes(4, 8)
+    assert g(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, FAKE, need - 1,
+             None) == WORKSPACE
+    assert g(FAKE, 4, 16, FAKE, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, FAKE + 4, need,
+             None) == INVALID  # workspace alignment
     bt = lib.moe_gather_scale_by_token
     assert bt(FAKE, 4, 16, FAKE, 0, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID
     assert bt(FAKE, 4, 16, FAKE, 65, FAKE, 8, FAKE, 4, 1, 4, None, FAKE, None) == INVALID

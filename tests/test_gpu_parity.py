@@ -174,7 +174,7 @@ def _dispatch_case(T, D, E, K, vtc, seed=0):
 
 
 @pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
-@pytest.mark.parametrize("path", ["rows", "by_token"])
+@pytest.mark.parametrize("path", ["lists", "rows", "by_token"])
 def test_gather_scale_bit_exact(dev, case, path):
     name, T, D, E, K, vtc = case
     inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc)
@@ -187,8 +187,9 @@ def test_gather_scale_bit_exact(dev, case, path):
     x = bf_dev(inp.x, dev)
     s = torch.from_numpy(inp.scores).to(dev)
     vr = scalar_dev(V, dev)
-    if path == "rows":
-        ops.moe_gather_scale(x, i32_dev(ti, dev), i32_dev(ei, dev), s, vr, out)
+    if path != "by_token":
+        ops.moe_gather_scale(x, i32_dev(ti, dev), i32_dev(ei, dev), s, vr, out,
+                             row_order=path == "rows")
     else:
         ops.moe_gather_scale_by_token(x, i32_dev(rop, dev), i32_dev(ei, dev), s, vr, out)
     assert np.array_equal(bits_host(out), want)
@@ -253,6 +254,41 @@ def test_scatter_add_general_long_lists(dev):
     want = orc.scatter_add(out0.copy(), y, ti, V)
     out = bf_dev(out0, dev)
     ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+
+
+@pytest.mark.parametrize("row_order", [False, True], ids=["lists", "rows"])
+def test_gather_scale_general_long_lists(dev, row_order):
+    """Arbitrary token_indices: a token owning 100 rows (more than one pass of
+    the token-order gather), unsorted rows, a valid bound below a; and a > 131072
+    rows, where the token lists are built in four launches."""
+    g = np.random.default_rng(10)
+    T, D, E, a, V = 12, 8 * 70, 6, 400, 350
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    ti[g.permutation(a)[:100]] = 5
+    ei = g.integers(0, E, size=a).astype(np.int32)
+    x = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    sc = g.random((T, E)).astype(np.float32)
+    say("gather long lists", row_order, T, D, E, a, V)
+    want = np.full((a, D), SENTINEL, np.uint16)
+    orc.gather_scale(x, ti, ei, sc, V, want)
+    out = torch.full((a, D), SENTINEL - 65536, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    ops.moe_gather_scale(bf_dev(x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                         torch.from_numpy(sc).to(dev), scalar_dev(V, dev), out,
+                         row_order=row_order)
+    assert np.array_equal(bits_host(out), want)
+
+    T, D, E, K = 70000, 64, 8, 2
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, None, seed=4)
+    V = int(counts[E])
+    say("gather multi-launch lists", row_order, T, D, E, K, V)
+    want = np.full((T * K, D), SENTINEL, np.uint16)
+    orc.gather_scale(inp.x, ti, ei, inp.scores, V, want)
+    out = torch.full((T * K, D), SENTINEL - 65536, dtype=torch.int16,
+                     device=dev).view(torch.bfloat16)
+    ops.moe_gather_scale(bf_dev(inp.x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                         torch.from_numpy(inp.scores).to(dev), scalar_dev(V, dev), out,
+                         row_order=row_order)
     assert np.array_equal(bits_host(out), want)
 
 
@@ -670,13 +706,15 @@ def test_zipf_pipeline_full_size(dev, zipf_inputs):
     ops.moe_scatter_add_by_token(out, y, grop, vr)
     want = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
     assert np.array_equal(bits_host(out), want)
-    # the general combine and the row-order gather agree with the same oracle
+    # the general combine and both visit orders of the general gather agree
+    # with the same oracle
     out2 = torch.zeros_like(out)
     ops.moe_scatter_add(out2, y, gti, vr)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
-    rows2 = torch.empty_like(rows)
-    ops.moe_gather_scale(x, gti, gei, s, vr, rows2)
-    assert torch.equal(rows2[:V].view(torch.int16), rows[:V].view(torch.int16))
+    for row_order in (False, True):
+        rows2 = torch.empty_like(rows)
+        ops.moe_gather_scale(x, gti, gei, s, vr, rows2, row_order=row_order)
+        assert torch.equal(rows2[:V].view(torch.int16), rows[:V].view(torch.int16))
 
 
 def test_quant_workload_full_size(dev):
@@ -841,10 +879,11 @@ def test_randomized_shapes_against_oracle(dev, seed):
     assert np.array_equal(grop.cpu().numpy(), rop)
     vr = gc[E:]
     want_rows = orc.gather_scale(x, ti, ei, s, V)
-    for path in ("rows", "by_token"):
+    for path in ("lists", "rows", "by_token"):
         rows = torch.zeros((T * K, D), dtype=torch.bfloat16, device=dev)
-        if path == "rows":
-            ops.moe_gather_scale(bf_dev(x, dev), gti, gei, sd, vr, rows)
+        if path != "by_token":
+            ops.moe_gather_scale(bf_dev(x, dev), gti, gei, sd, vr, rows,
+                                 row_order=path == "rows")
         else:
             ops.moe_gather_scale_by_token(bf_dev(x, dev), grop, gei, sd, vr, rows)
         assert np.array_equal(bits_host(rows)[:V], want_rows[:V]), path
