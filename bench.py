@@ -359,7 +359,7 @@ def setup_shuffling(ctx, wl, with_cpu):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build's path runs on a single MI355X and "
+        print(f"bench.py measures one GPU: the path runs on a single MI355X and "
               f"has no multi-GPU mode (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
