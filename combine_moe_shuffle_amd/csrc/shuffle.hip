@@ -1,5 +1,7 @@
 // moe_shuffle: top-k routing and the stable counting sort of the
-// (token, expert) pairs by expert, as three launches with no global atomics:
+// (token, expert) pairs by expert, as three launches with no global atomics
+// (two when the histogram of step 1 fits in LDS: scan_place_kernel does
+// steps 2 and 3 in one launch):
 //
 //  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
 //     the top-k of two tokens at once, the expert axis spread over its 64
@@ -299,6 +301,96 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(
   }
 }
 
+// The expert scan and the placement in one launch, for histograms that fit
+// in LDS (E * nblk <= kFuseHist ints). In expert-major order the exclusive
+// scan of the flattened [E][nblk] histogram is, at (e, b), every row of the
+// experts below e plus expert e's rows in blocks below b: exactly
+// first[e] + offset[e][b]. Every workgroup runs that one scan (thread i owns
+// entries 32i .. 32i+31: one local pass, a workgroup scan of the thread
+// sums, the prefixes written to LDS with one pad word per 32 so the writes
+// do not collide in a bank), then places its pairs. Workgroup 0 writes
+// counts as differences of the prefixes at row starts.
+constexpr int kFusePer = 32;
+constexpr int kFuseHist = kPlaceThreads * kFusePer;  // 8192
+__device__ __forceinline__ int fuse_pad(int i) { return i + (i >> 5); }
+
+__global__ __launch_bounds__(kPlaceThreads) void scan_place_kernel(
+    const int* __restrict__ pair, const int* __restrict__ hist, int nblk, int T, int E, int K,
+    const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
+    int* __restrict__ ei, int* __restrict__ rop) {
+  __shared__ int pre[kFuseHist + kFuseHist / 32 + 1];
+  __shared__ int wave_tot[kPlaceThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * kPlaceThreads + tid;
+  const int64_t npairs = static_cast<int64_t>(T) * K;
+  const bool have = p < npairs;
+  const int t = have ? static_cast<int>(p / K) : 0;
+  const int vtc = clamp_count(vtc_ptr, T);
+  const int v = (have && t < vtc) ? pair[p] : 0;
+  const int e = v & 0xFFFF;
+  const int rank = v >> 16;
+
+  // this thread's entries, as 16-byte loads: hist is 256-byte aligned and
+  // its workspace region is padded to 256 bytes, so a load that starts
+  // below n stays inside it; entries >= n are taken as 0
+  const int n = E * nblk;
+  const int i0 = tid * kFusePer;
+  int val[kFusePer];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < kFusePer / 4; ++j) {
+    const int i = i0 + 4 * j;
+    const u32x4 q = i < n ? *reinterpret_cast<const u32x4*>(hist + i) : u32x4{0u, 0u, 0u, 0u};
+    val[4 * j + 0] = i + 0 < n ? static_cast<int>(q.x) : 0;
+    val[4 * j + 1] = i + 1 < n ? static_cast<int>(q.y) : 0;
+    val[4 * j + 2] = i + 2 < n ? static_cast<int>(q.z) : 0;
+    val[4 * j + 3] = i + 3 < n ? static_cast<int>(q.w) : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kFusePer; ++j) mine += val[j];
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  int all = 0;
+#pragma unroll
+  for (int w = 0; w < kPlaceThreads / kWave; ++w) {
+    run += w < wave ? wave_tot[w] : 0;
+    all += wave_tot[w];
+  }
+#pragma unroll
+  for (int j = 0; j < kFusePer; ++j) {
+    if (i0 + j < n) pre[fuse_pad(i0 + j)] = run;
+    run += val[j];
+  }
+  if (tid == 0) pre[fuse_pad(n)] = all;
+  __syncthreads();
+
+  if (blockIdx.x == 0) {
+    for (int x = tid; x < E; x += kPlaceThreads)
+      counts[x] = pre[fuse_pad((x + 1) * nblk)] - pre[fuse_pad(x * nblk)];
+    if (tid == 0) counts[E] = vtc * K;
+  }
+  if (!have) return;
+  if (t < vtc) {
+    const int r = pre[fuse_pad(e * nblk + t / kTokPerBlock)] + rank;
+    ti[r] = t;
+    ei[r] = e;
+    if (rop) rop[p] = r;
+  } else {
+    ti[p] = t;
+    ei[p] = -1;
+    if (rop) rop[p] = -1;
+  }
+}
+
 // counts[0..E] = 0 (no pairs at all)
 __global__ void zero_counts_kernel(int* __restrict__ counts, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -339,10 +431,16 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
   else if (pl <= 8) MOE_SEL(8);
   else MOE_SEL(16);
 #undef MOE_SEL
-  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
-                     dim3(kScanWaves * kWave), 0, stream, hist, E, nblk, counts);
   const int64_t npairs = static_cast<int64_t>(T) * K;
   const int pblocks = static_cast<int>((npairs + kPlaceThreads - 1) / kPlaceThreads);
+  if (static_cast<int64_t>(E) * nblk <= kFuseHist) {
+    hipLaunchKernelGGL(scan_place_kernel, dim3(pblocks), dim3(kPlaceThreads), 0, stream, pair,
+                       hist, nblk, T, E, K, vtc, counts, token_indices, expert_indices,
+                       row_of_pair);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
+                     dim3(kScanWaves * kWave), 0, stream, hist, E, nblk, counts);
   hipLaunchKernelGGL(place_kernel, dim3(pblocks), dim3(kPlaceThreads), 0, stream, pair, hist,
                      nblk, T, E, K, vtc, counts, token_indices, expert_indices, row_of_pair);
   return hipGetLastError();

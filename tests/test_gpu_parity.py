@@ -112,6 +112,9 @@ SHUFFLE_CASES = [
     ("vtc-negative", 100, 16, 2, -5, "normal"),
     ("T0", 0, 16, 2, None, "normal"),
     ("large-T", 70000, 64, 4, 65000, "normal"),
+    # histogram sizes E * ceil(T/32) around the one-launch scan-and-place limit
+    ("hist-8192", 1024, 256, 8, 1000, "normal"),
+    ("hist-8448", 1056, 256, 8, 1000, "normal"),
 ]
 
 
