@@ -14,6 +14,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_shuffle.so")
+# MOE_ABI_VERSION of include/moe_shuffle.h that SIGNATURES describes
+ABI_VERSION = 2
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -94,8 +96,9 @@ def fn(name: str):
     int."""
     f = _fns.get(name)
     if f is None:
+        lib = load()  # also checks the library's ABI version
         mod = fast()
-        f = getattr(mod, name) if mod is not None else getattr(load(), name)
+        f = getattr(mod, name) if mod is not None else getattr(lib, name)
         _fns[name] = f
     return f
 
@@ -113,6 +116,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(
+            f"{LIB_PATH} implements ABI {lib.moe_abi_version()}, the binding expects "
+            f"{ABI_VERSION}: rebuild it with `python -m combine_moe_shuffle_amd.build`")
     _lib = lib
     return lib
 

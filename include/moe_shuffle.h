@@ -74,7 +74,7 @@ typedef enum {
 } moe_status_t;
 
 /* Version of this ABI (bumped on any signature change). */
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 MOE_API int moe_abi_version(void);
 
 /* Static name of a status code. */

@@ -66,7 +66,7 @@ def test_signature_table_arity_matches_header(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(3) == b"MOE_ERR_WORKSPACE"
 
