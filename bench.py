@@ -22,7 +22,9 @@ step instead; a graph launch costs more than a few kernel launches here).
 
 1. W untimed steps, then exactly K timed steps between two device
    synchronisations (wall clock, and a HIP event pair around the region): the
-   warm steps behind `value`.
+   warm steps behind `value`. Then K steps one at a time, each between an
+   event pair with the host waiting for it: p10 / p50 / p90 of an isolated
+   step's latency, launch included ("step_us_isolated").
 2. K cold steps, each after a flush of L2 and the 256 MB Infinity Cache -- a
    1 GiB read (clean eviction) or a 1 GiB write (whose dirty lines the step
    then writes back) -- device time with the flushes' own time subtracted,
@@ -413,6 +415,18 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     region_ms = region[0].elapsed_time(region[1])
+    # ---- the spread over steps: each step alone between an event pair, the
+    # host waiting for it before the next (the latency of one isolated step,
+    # launch included)
+    isolated = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run_step()
+        e1.record()
+        torch.cuda.synchronize()
+        isolated.append(e0.elapsed_time(e1) * 1e3)
+    p10, p50, p90 = (float(v) for v in np.percentile(isolated, [10, 50, 90]))
     # ---- cold steps: before each step a 1 GiB buffer is read (a sum), which
     # evicts the step's data from L2 and the 256 MB Infinity Cache without
     # leaving dirty lines behind; the same with a 1 GiB write, whose dirty
@@ -482,6 +496,7 @@ def main():
         "warmup": warm,
         "ms_per_step": ms_step,
         "ms_per_step_device": region_ms / steps,
+        "step_us_isolated": {"p10": round(p10, 2), "p50": round(p50, 2), "p90": round(p90, 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
