@@ -41,7 +41,9 @@ over that duration, against the 8 TB/s HBM peak.
 
 One JSON line on stdout. value = valid tokens (routed rows for padded and
 shuffling) per second of the whole step. cpu_baseline = the CPU oracle
-(single-threaded C) timed on a bounded sample of the same step.
+(single-threaded C) timed on a bounded sample of the same step, pinned to one
+core; "host" names the CPU model and core counts, "stage_s" the dispatch
+workloads' per-stage times.
 """
 from __future__ import annotations
 
@@ -392,6 +394,8 @@ def main():
         s = setup_padded(ctx, W.WORKLOADS["padded"], with_cpu)
     else:
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
+    if s.cpu:
+        s.cpu["host"] = _host()
     steps, warm = args.steps, args.warmup
     stages = list(s.stages.items())
     graph = args.graph
@@ -540,34 +544,64 @@ def load_traffic(kernel, srcs, workload):
 
 # ------------------------------------------------------------------ CPU oracle
 def _median_time(fn, reps):
-    ts = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        fn()
-        ts.append(time.perf_counter() - t0)
+    """Median wall time of `reps` runs of fn, the process pinned to one core
+    meanwhile (the oracle is single-threaded)."""
+    old = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old)})
+    try:
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, old)
     return float(np.median(ts))
+
+
+def _host():
+    """The host the CPU baseline ran on: its CPU model, the logical CPUs the
+    system has and those this process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "nproc": os.cpu_count(), "usable": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline_dispatch(orc, inp, wl, vtc):
     """The oracle on the same step (shuffle, gather, scatter-add), single
     thread; median of 3 runs."""
     K = wl.K
+    stage_t = {"shuffle": [], "gather": [], "scatter": []}
+    rows = np.empty((wl.T * K, wl.D), np.uint16)
 
     def run():
+        t0 = time.perf_counter()
         counts, ei, ti, rop = orc.shuffle(inp.scores, K, wl.vtc)
         V = int(counts[wl.E])
-        rows = np.empty((wl.T * K, wl.D), np.uint16)
+        t1 = time.perf_counter()
         if wl.quant:
             orc.gather_scale_quant(inp.x, ti, ei, inp.scores, wl.scale_ub, V)
         else:
             orc.gather_scale(inp.x, ti, ei, inp.scores, V, rows)
+        t2 = time.perf_counter()
         orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+        t3 = time.perf_counter()
+        for k, d in zip(stage_t, (t1 - t0, t2 - t1, t3 - t2)):
+            stage_t[k].append(d)
 
     t = _median_time(run, 3)
     return {"value": vtc / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole step (shuffle, gather, scatter-add) of the {wl.name} "
                       f"workload, {vtc} valid tokens; median of 3 runs, "
-                      f"{t:.2f} s each"}
+                      f"{t:.2f} s each",
+            "stage_s": {k: round(float(np.median(v)), 4) for k, v in stage_t.items()}}
 
 
 def cpu_baseline_finalize(orc, fi, wl, w, flags, name):
