@@ -753,6 +753,25 @@ def test_prefill_finalize_full_size(dev):
     assert_fp8_close(codes.cpu().numpy(), oc, "prefill mxfp8")
 
 
+def test_prefill_swizzled_finalize_full_size(dev):
+    """The prefill finalize with bf16 routing weights and 128x4-tiled MXFP8
+    scales at T=16384, D=5120, K=4, as the benchmark launches it."""
+    wl = W.WORKLOADS["prefill"]
+    fi = W.finalize_inputs(wl)
+    wb = W.to_bf16_bits(fi.w)
+    say("prefill-swizzled finalize", wl.T, wl.D, wl.K)
+    out, codes, scales = ops.moe_finalize_rmsnorm(
+        bf_dev(fi.y, dev), bf_dev(wb, dev), i32_dev(fi.row_of_pair, dev),
+        bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev), fi.eps, mxfp8=True,
+        scale_layout="swizzled")
+    got = bits_host(out)
+    want = orc.finalize_rmsnorm(fi.y, wb, fi.row_of_pair, fi.shared, fi.gamma, fi.eps, flags=2)
+    _close(got, want, "prefill-swizzled")
+    oc, os_ = orc.mxfp8_quantize(got)
+    assert np.array_equal(scales.cpu().numpy(), orc.mxfp8_swizzle(os_))
+    assert_fp8_close(codes.cpu().numpy(), oc, "prefill-swizzled mxfp8")
+
+
 def test_mhc_finalize_full_size(dev):
     """The hc = 4 mHC finalize at T=16384, D=5120, K=4 with MXFP8 and swizzled
     scales, as the benchmark launches it."""
@@ -794,6 +813,35 @@ def test_padded_combine_full_routing(dev):
     out = torch.zeros((wl.T, D), dtype=torch.bfloat16, device=dev)
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:wl.E].contiguous(), gti, out)
     assert np.array_equal(bits_host(out), want)
+
+
+def test_padded_combine_full_size(dev):
+    """The padded workload exactly as the benchmark launches it: T=8192,
+    D=7168, E=256, K=8, valid_token_count=6000, eight (T*K, D) slabs drawn
+    on the device. Every 7th 16-byte chunk of each output row -- every slice
+    of the launch, lanes at every offset -- is checked against the oracle run
+    on those columns (the combine is independent per column)."""
+    wl = W.WORKLOADS["padded"]
+    T, D, E, K, EP = wl.T, wl.D, wl.E, wl.K, wl.ep
+    inp = W.dispatch_inputs(wl, with_y=False)
+    counts, ei, ti, rop = orc.shuffle(inp.scores, K, wl.vtc)
+    say("padded full size", T, D, E, K, EP, int(counts[E]))
+    gc, gei, gti, grop = ops.moe_shuffle(torch.from_numpy(inp.scores).to(dev), K,
+                                         scalar_dev(wl.vtc, dev))
+    assert np.array_equal(gti.cpu().numpy(), ti)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6006)
+    slabs = torch.empty((EP, T * K, D), dtype=torch.bfloat16, device=dev)
+    for r in range(EP):
+        slabs[r] = torch.randn((T * K, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    ops.moe_scatter_add_padded(slabs, gc[:E].contiguous(), gti, out)
+    chunks = torch.arange(0, D // 8, 7, device=dev)
+    cols = (chunks[:, None] * 8 + torch.arange(8, device=dev)).reshape(-1)
+    sub = bits_host(slabs.index_select(2, cols))
+    del slabs
+    want = orc.scatter_add_padded(np.zeros((T, cols.numel()), np.uint16), sub, counts[:E], ti)
+    assert np.array_equal(bits_host(out.index_select(1, cols)), want)
 
 
 def test_shuffling_workload_full_size(dev):
