@@ -61,6 +61,21 @@ def _scalar_i32(t, name, device):
     return t
 
 
+def _workspace(workspace, need, device):
+    """The workspace tensor (allocated when None) and its size in bytes. A
+    caller's workspace must be a contiguous tensor on the same GPU; the
+    library checks its size and alignment."""
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    elif not isinstance(workspace, torch.Tensor):
+        raise ValueError("workspace must be a tensor")
+    else:
+        if not workspace.is_cuda or workspace.device != device:
+            raise ValueError(f"workspace must be on {device}")
+        _contig(workspace, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _scores(scores, device):
     _need(scores, "scores", torch.float32, 2, device)
     return scores.stride(0), scores.stride(1)
@@ -97,12 +112,10 @@ def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspac
         ei = torch.empty(T * K, dtype=torch.int32, device=device)
         ti = torch.empty(T * K, dtype=torch.int32, device=device)
         rop = torch.empty((T, K), dtype=torch.int32, device=device) if row_of_pair else None
-    need = lib.moe_shuffle_workspace_bytes(T, E, K)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    workspace, nbytes = _workspace(workspace, lib.moe_shuffle_workspace_bytes(T, E, K), device)
     _lib.check(_lib.fn("moe_shuffle")(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
-                               _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace),
-                               workspace.numel(), _stream(device)))
+                               _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace), nbytes,
+                               _stream(device)))
     return counts, ei, ti, rop
 
 
@@ -143,10 +156,8 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
         raise ValueError("out must be (a, D)")
     nbytes = 0
     if not row_order:
-        need = _lib.load().moe_gather_scale_workspace_bytes(T, a)
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-        nbytes = workspace.numel()
+        workspace, nbytes = _workspace(
+            workspace, _lib.load().moe_gather_scale_workspace_bytes(T, a), device)
     else:
         workspace = None
     _lib.check(_lib.fn("moe_gather_scale")(
@@ -225,12 +236,9 @@ def moe_scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None, works
     if token_indices.numel() != a:
         raise ValueError("token_indices must have in_tokens.shape[0] entries")
     lib = _lib.load()
-    need = lib.moe_scatter_add_workspace_bytes(T, a)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    workspace, nbytes = _workspace(workspace, lib.moe_scatter_add_workspace_bytes(T, a), device)
     _lib.check(_lib.fn("moe_scatter_add")(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
-                                   a, D, _ptr(vr), _ptr(workspace), workspace.numel(),
-                                   _stream(device)))
+                                   a, D, _ptr(vr), _ptr(workspace), nbytes, _stream(device)))
     return out_tokens
 
 
@@ -265,12 +273,11 @@ def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, w
     if out_tokens.shape[1] != D or token_indices.numel() != T_K:
         raise ValueError("shapes must be in (EP, T_K, D), token_indices (T_K,), out (T, D)")
     lib = _lib.load()
-    need = lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    workspace, nbytes = _workspace(
+        workspace, lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E), device)
     _lib.check(_lib.fn("moe_scatter_add_padded")(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
                                           _ptr(token_indices), _ptr(out_tokens), T, D,
-                                          _ptr(workspace), workspace.numel(), _stream(device)))
+                                          _ptr(workspace), nbytes, _stream(device)))
     return out_tokens
 
 
@@ -293,13 +300,12 @@ def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, wit
     oc = torch.empty(c_hi - c_lo + 1, dtype=torch.int32, device=device) if with_counts else None
     lib = _lib.load()
     em_rows = out.shape[0] if name == "moe_combine_shuffling" else tokens.shape[0]
-    need = lib.moe_shuffling_workspace_bytes(EP, c_hi - c_lo, em_rows)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    workspace, nbytes = _workspace(
+        workspace, lib.moe_shuffling_workspace_bytes(EP, c_hi - c_lo, em_rows), device)
     _lib.check(_lib.fn(name)(
         _ptr(tokens), tokens.shape[0], _ptr(out), out.shape[0], D, _ptr(counts), EP, C, c_lo,
         c_hi, -1 if rank_stride is None else int(rank_stride), _ptr(oc), _ptr(workspace),
-        workspace.numel(), _stream(device)))
+        nbytes, _stream(device)))
     return out, oc
 
 

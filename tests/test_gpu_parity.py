@@ -1044,6 +1044,40 @@ def test_every_op_is_deterministic(dev):
         assert torch.equal(ms, outs[0][2])
 
 
+def test_binding_checks_caller_workspaces(dev):
+    """A workspace the caller passes must be a contiguous tensor on the same
+    GPU (else ValueError before any launch); any dtype works, its size counted
+    in bytes."""
+    say("binding workspaces")
+    T, E, K, D = 40, 8, 2, 64
+    s = torch.rand((T, E), device=dev)
+    counts, ei, ti, rop = ops.moe_shuffle(s, K)
+    x = torch.randn((T, D), device=dev).to(torch.bfloat16)
+    y = torch.randn((T * K, D), device=dev).to(torch.bfloat16)
+    lib = ops._lib.load()
+    calls = {
+        "shuffle": (lib.moe_shuffle_workspace_bytes(T, E, K),
+                    lambda ws: ops.moe_shuffle(s, K, workspace=ws)),
+        "gather": (lib.moe_gather_scale_workspace_bytes(T, T * K),
+                   lambda ws: ops.moe_gather_scale(x, ti, ei, s, counts[E:], workspace=ws)),
+        "scatter": (lib.moe_scatter_add_workspace_bytes(T, T * K),
+                    lambda ws: ops.moe_scatter_add(x.clone(), y, ti, counts[E:], workspace=ws)),
+        "padded": (lib.moe_scatter_add_padded_workspace_bytes(T, T * K, E),
+                   lambda ws: ops.moe_scatter_add_padded(y.view(1, T * K, D), counts[:E].clone(),
+                                                         ti, x.clone(), workspace=ws)),
+        "combine_shuffling": (lib.moe_shuffling_workspace_bytes(2, 4, T * K),
+                              lambda ws: ops.moe_combine_shuffling(
+                                  y, counts[:E].view(2, 4).contiguous(), workspace=ws)),
+    }
+    for name, (need, call) in calls.items():
+        with pytest.raises(ValueError):
+            call(torch.empty(need + 256, dtype=torch.uint8))                  # host memory
+        with pytest.raises(ValueError):
+            call(torch.empty((need + 256) * 2, dtype=torch.uint8, device=dev)[::2])  # strided
+        call(torch.empty((need + 3) // 4 + 64, dtype=torch.float32, device=dev))   # bytes
+    torch.cuda.synchronize()
+
+
 def test_zero_width_rows_are_no_ops(dev):
     """D = 0: every row entry point returns without touching anything."""
     say("zero-width rows")
