@@ -61,6 +61,18 @@ def _scalar_i32(t, name, device):
     return t
 
 
+def _out(t, name, dtype, shape, device):
+    """An output tensor: the caller's, checked (dtype, device, contiguity and
+    exact shape, so no kernel writes past its end), or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, name, dtype, len(shape), device)
+    _contig(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
 def _workspace(workspace, need, device):
     """The workspace tensor (allocated when None) and its size in bytes. A
     caller's workspace must be a contiguous tensor on the same GPU; the
@@ -148,12 +160,7 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
     if expert_indices.numel() != a:
         raise ValueError("token_indices and expert_indices must have the same length")
     T, D = x.shape
-    if out is None:
-        out = torch.empty((a, D), dtype=torch.bfloat16, device=device)
-    _need(out, "out", torch.bfloat16, 2, device)
-    _contig(out, "out")
-    if tuple(out.shape) != (a, D):
-        raise ValueError("out must be (a, D)")
+    out = _out(out, "out", torch.bfloat16, (a, D), device)
     nbytes = 0
     if not row_order:
         workspace, nbytes = _workspace(
@@ -177,12 +184,7 @@ def moe_gather_scale_by_token(x, row_of_pair, expert_indices, scores, valid_rows
         raise ValueError("row_of_pair must be (T, K)")
     K = row_of_pair.shape[1]
     a = expert_indices.numel()
-    if out is None:
-        out = torch.empty((a, D), dtype=torch.bfloat16, device=device)
-    _need(out, "out", torch.bfloat16, 2, device)
-    _contig(out, "out")
-    if tuple(out.shape) != (a, D):
-        raise ValueError("out must be (a, D)")
+    out = _out(out, "out", torch.bfloat16, (a, D), device)
     _lib.check(_lib.fn("moe_gather_scale_by_token")(
         _ptr(x), T, D, _ptr(row_of_pair), K, _ptr(expert_indices), a, _ptr(scores), st, se,
         scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
@@ -201,13 +203,8 @@ def moe_gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=No
         _need(scale_ub, "scale_ub", torch.float32, device=device)
         if scale_ub.numel() != 1:
             raise ValueError("scale_ub must hold one element")
-    if out is None:
-        out = torch.empty((a, D), dtype=torch.uint8, device=device)
-    if out_scale is None:
-        out_scale = torch.empty(a, dtype=torch.float32, device=device)
-    _need(out, "out", torch.uint8, 2, device)
-    _need(out_scale, "out_scale", torch.float32, 1, device)
-    _contig(out, "out")
+    out = _out(out, "out", torch.uint8, (a, D), device)
+    out_scale = _out(out_scale, "out_scale", torch.float32, (a,), device)
     _lib.check(_lib.fn("moe_gather_scale_quant")(
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
         scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream(device)))
@@ -295,8 +292,11 @@ def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, wit
     if out is None:
         out = torch.empty((tokens.shape[0] if out_rows is None else out_rows, D),
                           dtype=torch.bfloat16, device=device)
-    _need(out, "out", torch.bfloat16, 2, device)
-    _contig(out, "out")
+    else:  # any number of rows (rows past its end are skipped), D columns
+        _need(out, "out", torch.bfloat16, 2, device)
+        _contig(out, "out")
+        if out.shape[1] != D:
+            raise ValueError(f"out must have D = {D} columns, got {out.shape[1]}")
     oc = torch.empty(c_hi - c_lo + 1, dtype=torch.int32, device=device) if with_counts else None
     lib = _lib.load()
     em_rows = out.shape[0] if name == "moe_combine_shuffling" else tokens.shape[0]
@@ -401,8 +401,7 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
     flags, T, K, rows, D = _finalize_common(y_permuted, expert_weights, row_of_pair, shared,
                                             gamma, flags, mxfp8, scale_layout)
     device = y_permuted.device
-    if out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
+    out = _out(out, "out", torch.bfloat16, (T, D), device)
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
     _lib.check(_lib.fn("moe_finalize_rmsnorm")(
@@ -444,14 +443,10 @@ def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, 
             raise ValueError(f"{n} has the wrong shape")
     if pre is not None and gamma is None:
         raise ValueError("gamma is required with pre")
-    if residual_out is None:
-        residual_out = torch.empty_like(residual)
-    elif residual_out.data_ptr() == residual.data_ptr():
+    residual_out = _out(residual_out, "residual_out", torch.bfloat16, (T, hc, D), device)
+    if residual_out.numel() and residual_out.data_ptr() == residual.data_ptr():
         raise ValueError("residual_out must not alias residual")
-    if pre is not None and out is None:
-        out = torch.empty((T, D), dtype=torch.bfloat16, device=device)
-    if pre is None:
-        out = None
+    out = _out(out, "out", torch.bfloat16, (T, D), device) if pre is not None else None
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
     _lib.check(_lib.fn("moe_finalize_mhc")(

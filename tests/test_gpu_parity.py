@@ -1078,6 +1078,46 @@ def test_binding_checks_caller_workspaces(dev):
     torch.cuda.synchronize()
 
 
+def test_binding_checks_caller_outputs(dev):
+    """Outputs the caller passes must have the exact shape (or, for the EP
+    re-sort, D columns), dtype and device; a wrong one raises ValueError
+    before any launch."""
+    say("binding outputs")
+    T, E, K, D = 16, 4, 2, 64
+    s = torch.rand((T, E), device=dev)
+    counts, ei, ti, rop = ops.moe_shuffle(s, K)
+    x = torch.randn((T, D), device=dev).to(torch.bfloat16)
+    y = torch.randn((T * K, D), device=dev).to(torch.bfloat16)
+    w = torch.rand((T, K), device=dev)
+    g = torch.ones(D, dtype=torch.bfloat16, device=dev)
+    res = torch.randn((T, 2, D), device=dev).to(torch.bfloat16)
+    post, comb, pre = torch.rand((T, 2), device=dev), torch.rand((T, 2, 2), device=dev), \
+        torch.rand((T, 2), device=dev)
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    bad = [
+        lambda: ops.moe_gather_scale(x, ti, ei, s, out=torch.empty((T * K - 1, D), dtype=bf,
+                                                                   device=dev)),
+        lambda: ops.moe_gather_scale_quant(x, ti, ei, s, out=torch.empty((T * K, D - 16),
+                                                                         dtype=u8, device=dev)),
+        lambda: ops.moe_gather_scale_quant(x, ti, ei, s, out_scale=torch.empty(
+            T * K - 1, dtype=f32, device=dev)),
+        lambda: ops.moe_finalize_rmsnorm(y, w, rop, None, g, 1e-6, out=torch.empty(
+            (T, D // 2), dtype=bf, device=dev)),
+        lambda: ops.moe_finalize_rmsnorm(y, w, rop, None, g, 1e-6, out=torch.empty(
+            (T, D), dtype=bf)),
+        lambda: ops.moe_finalize_mhc(y, w, rop, None, res, post, comb, pre, g, 1e-6,
+                                     residual_out=torch.empty((T, 1, D), dtype=bf, device=dev)),
+        lambda: ops.moe_finalize_mhc(y, w, rop, None, res, post, comb, pre, g, 1e-6,
+                                     out=torch.empty((T - 1, D), dtype=bf, device=dev)),
+        lambda: ops.moe_combine_shuffling(y, counts[:E].view(2, 2).contiguous(),
+                                          out=torch.empty((T * K, D // 2), dtype=bf, device=dev)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    torch.cuda.synchronize()
+
+
 def test_zero_width_rows_are_no_ops(dev):
     """D = 0: every row entry point returns without touching anything."""
     say("zero-width rows")
