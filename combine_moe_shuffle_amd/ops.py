@@ -17,12 +17,13 @@ from . import _lib
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
 def _stream(device):
     """The current stream of the current device, as a raw handle. The library
     launches on the current HIP device, so the tensors must live there."""
-    cur = torch.cuda.current_device()
+    cur = _get_device() if _get_device is not None else torch.cuda.current_device()
     if device.index is not None and device.index != cur:
         raise ValueError(f"the tensors are on {device} but the current device is cuda:{cur}")
     if _raw_stream is not None:
@@ -35,6 +36,20 @@ def _ptr(t):
 
 
 def _need(t, name, dtype, ndim=None, device=None):
+    """t is a GPU tensor of dtype (and ndim dimensions, on device, when given);
+    else ValueError. The common case costs three tensor queries."""
+    try:
+        d = t.get_device()
+        if (t.dtype == dtype and (ndim is None or t.dim() == ndim) and d >= 0
+                and (device is None or device.index is None or d == device.index)):
+            return
+    except AttributeError:
+        pass
+    _need_explain(t, name, dtype, ndim, device)
+
+
+def _need_explain(t, name, dtype, ndim, device):
+    """Raises the ValueError that says which requirement of _need t fails."""
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a tensor")
     if t.dtype != dtype:
@@ -45,6 +60,7 @@ def _need(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} must be on the GPU")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+    raise ValueError(f"{name} is not a usable tensor")
 
 
 def _contig(t, name):
