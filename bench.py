@@ -70,8 +70,10 @@ DISPATCH_METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default 50; 1000 for decode, whose step is a few us)")
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps first (default 5; 50 for decode)")
     p.add_argument("--workload", default="zipf", choices=WORKLOAD_CHOICES)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true",
@@ -396,7 +398,9 @@ def main():
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
     if s.cpu:
         s.cpu["host"] = _host()
-    steps, warm = args.steps, args.warmup
+    short = name == "decode"  # a few us per step: more steps amortise the region's ends
+    steps = args.steps if args.steps is not None else (1000 if short else 50)
+    warm = args.warmup if args.warmup is not None else (50 if short else 5)
     stages = list(s.stages.items())
     graph = args.graph
 
