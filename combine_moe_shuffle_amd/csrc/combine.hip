@@ -43,11 +43,13 @@ __device__ __forceinline__ int clamp_count(const int* p, int hi) {
   return v < 0 ? 0 : (v > hi ? hi : v);
 }
 
-// Ascending bitonic sort of one int per lane across the wave.
-__device__ __forceinline__ int wave_sort_asc(int v, int lane) {
-#pragma unroll
-  for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
+// Ascending bitonic sort of one int per lane over aligned blocks of `width`
+// lanes (a wave-uniform power of two, 1..64): lanes [0, width) end sorted.
+// A token's rows sit in its first n <= width lanes, so only log2(width) of
+// the six merge levels run (three for K = 8 instead of six: each level's
+// lane exchanges are dependent LDS-pipe round trips).
+__device__ __forceinline__ int wave_sort_asc(int v, int lane, int width) {
+  for (int k = 2; k <= width; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       const int o = __shfl_xor(v, j, kWave);
       const bool up = (lane & k) == 0;
@@ -56,6 +58,11 @@ __device__ __forceinline__ int wave_sort_asc(int v, int lane) {
     }
   }
   return v;
+}
+
+// The least power of two >= n, for 1 <= n <= 64.
+__device__ __forceinline__ int sort_width(int n) {
+  return n <= 1 ? 1 : 1 << (32 - __builtin_clz(static_cast<unsigned>(n - 1)));
 }
 
 // Loads group [i0, i0+G) of the n rows listed in ascending order in lanes
@@ -181,7 +188,8 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
   const bool ok = r >= 0 && r < V;
   const int n = __popcll(__ballot(ok));
   if (n == 0) return;
-  const int sorted_rows = wave_sort_asc(ok ? r : INT_MAX, lane);
+  // slots sit in lanes [0, K): sorting K lanes (rounded up) is enough
+  const int sorted_rows = wave_sort_asc(ok ? r : INT_MAX, lane, sort_width(uniform(K)));
 
   const int nch = D >> 3;
   const int slice0 = sl * kWave * CPL;
@@ -444,7 +452,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (n <= kWave) {
     const int r = lane < n ? list[beg + lane] : INT_MAX;
-    const int sorted_rows = wave_sort_asc(r, lane);
+    const int sorted_rows = wave_sort_asc(r, lane, sort_width(uniform(n)));
     if (slice0 + kWave * CPL <= nch)
       reduce_slice<CPL, kGroup, true>(orow, in, D, nch, base, sorted_rows, n);
     else
@@ -537,7 +545,7 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_kernel(
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (n <= kWave) {
     const int r = lane < n ? list[beg + lane] : INT_MAX;
-    const int sorted = wave_sort_asc(r, lane);
+    const int sorted = wave_sort_asc(r, lane, sort_width(uniform(n)));
     // source row of each sorted row: rank * T_K + row (ascending row order kept)
     const int src = lane < n ? rank_of_row(pre, E, epr, sorted) * T_K + sorted : 0;
     if (slice0 + kWave * CPL <= nch)
