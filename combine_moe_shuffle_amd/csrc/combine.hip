@@ -146,19 +146,25 @@ __device__ __forceinline__ void store_acc(const float (&acc)[CPL][8], uint16_t* 
   }
 }
 
-// The whole per-token reduction of one slice: the initial row and the first
-// G expert rows are loaded together, then added in order; later groups
-// follow; one store. n >= 1.
-template <int CPL, int G, bool FULL>
-__device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
-                                             const uint16_t* __restrict__ in, int D, int nch,
-                                             int base, int sorted_rows, int n) {
-  u32x4 o0[CPL];
+// This lane's chunks of the initial (output) row.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void load_init(u32x4 (&o0)[CPL], const uint16_t* __restrict__ orow,
+                                          int nch, int base) {
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = base + j * kWave;
     o0[j] = (FULL || c < nch) ? ld16(orow + c * kChunk) : u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+// The per-token reduction of one slice from its loaded initial row o0: the
+// first G expert rows are loaded, then added in order; later groups follow;
+// one store. n >= 1.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void reduce_slice_from(const u32x4 (&o0)[CPL],
+                                                  uint16_t* __restrict__ orow,
+                                                  const uint16_t* __restrict__ in, int D,
+                                                  int nch, int base, int sorted_rows, int n) {
   u32x4 buf[G][CPL];
   load_rows<CPL, G, FULL>(buf, in, D, nch, base, sorted_rows, 0, n);
   float acc[CPL][8];
@@ -170,6 +176,39 @@ __device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
     add_group<CPL, G, FULL>(acc, buf, nch, base, i0, n);
   }
   store_acc<CPL, FULL>(acc, orow, nch, base);
+}
+
+// The same with the initial row loaded together with the first G expert rows.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
+                                             const uint16_t* __restrict__ in, int D, int nch,
+                                             int base, int sorted_rows, int n) {
+  u32x4 o0[CPL];
+  load_init<CPL, FULL>(o0, orow, nch, base);
+  reduce_slice_from<CPL, G, FULL>(o0, orow, in, D, nch, base, sorted_rows, n);
+}
+
+// One (token, slice) of the by-token combine. The initial row does not depend
+// on the slot rows: when the token is likely routed (t * K < V, true for
+// every token below a shuffle's valid count) it is loaded before them, so the
+// two loads overlap instead of following one another.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void scatter_token(uint16_t* __restrict__ out,
+                                              const uint16_t* __restrict__ in,
+                                              const int* __restrict__ rop, int t, int K, int V,
+                                              int D, int nch, int base, int lane) {
+  int r = lane < K ? rop[static_cast<int64_t>(t) * K + lane] : -1;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  const bool early = static_cast<int64_t>(t) * K < V;  // wave-uniform
+  u32x4 o0[CPL];
+  if (early) load_init<CPL, FULL>(o0, orow, nch, base);
+  const bool ok = r >= 0 && r < V;
+  const int n = __popcll(__ballot(ok));
+  if (n == 0) return;
+  // slots sit in lanes [0, K): sorting K lanes (rounded up) is enough
+  const int sorted_rows = wave_sort_asc(ok ? r : INT_MAX, lane, sort_width(uniform(K)));
+  if (!early) load_init<CPL, FULL>(o0, orow, nch, base);
+  reduce_slice_from<CPL, G, FULL>(o0, orow, in, D, nch, base, sorted_rows, n);
 }
 
 template <int CPL, int G>
@@ -184,20 +223,12 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
   const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
   if (t >= T) return;
   const int V = clamp_count(vrows, a);
-  int r = lane < K ? rop[static_cast<int64_t>(t) * K + lane] : -1;
-  const bool ok = r >= 0 && r < V;
-  const int n = __popcll(__ballot(ok));
-  if (n == 0) return;
-  // slots sit in lanes [0, K): sorting K lanes (rounded up) is enough
-  const int sorted_rows = wave_sort_asc(ok ? r : INT_MAX, lane, sort_width(uniform(K)));
-
   const int nch = D >> 3;
   const int slice0 = sl * kWave * CPL;
-  uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (slice0 + kWave * CPL <= nch)
-    reduce_slice<CPL, G, true>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+    scatter_token<CPL, G, true>(out, in, rop, t, K, V, D, nch, slice0 + lane, lane);
   else
-    reduce_slice<CPL, G, false>(orow, in, D, nch, slice0 + lane, sorted_rows, n);
+    scatter_token<CPL, G, false>(out, in, rop, t, K, V, D, nch, slice0 + lane, lane);
 }
 
 // ---------------------------------------------------------------- general
