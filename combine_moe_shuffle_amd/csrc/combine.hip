@@ -178,16 +178,6 @@ __device__ __forceinline__ void reduce_slice_from(const u32x4 (&o0)[CPL],
   store_acc<CPL, FULL>(acc, orow, nch, base);
 }
 
-// The same with the initial row loaded together with the first G expert rows.
-template <int CPL, int G, bool FULL>
-__device__ __forceinline__ void reduce_slice(uint16_t* __restrict__ orow,
-                                             const uint16_t* __restrict__ in, int D, int nch,
-                                             int base, int sorted_rows, int n) {
-  u32x4 o0[CPL];
-  load_init<CPL, FULL>(o0, orow, nch, base);
-  reduce_slice_from<CPL, G, FULL>(o0, orow, in, D, nch, base, sorted_rows, n);
-}
-
 // One (token, slice) of the by-token combine. The initial row does not depend
 // on the slot rows: when the token is likely routed (t * K < V, true for
 // every token below a shuffle's valid count) it is loaded before them, so the
@@ -482,12 +472,19 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
   const int base = slice0 + lane;
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (n <= kWave) {
+    // the initial row does not depend on the row list: load it alongside
+    const bool full = slice0 + kWave * CPL <= nch;
+    u32x4 o0[CPL];
+    if (full)
+      load_init<CPL, true>(o0, orow, nch, base);
+    else
+      load_init<CPL, false>(o0, orow, nch, base);
     const int r = lane < n ? list[beg + lane] : INT_MAX;
     const int sorted_rows = wave_sort_asc(r, lane, sort_width(uniform(n)));
-    if (slice0 + kWave * CPL <= nch)
-      reduce_slice<CPL, kGroup, true>(orow, in, D, nch, base, sorted_rows, n);
+    if (full)
+      reduce_slice_from<CPL, kGroup, true>(o0, orow, in, D, nch, base, sorted_rows, n);
     else
-      reduce_slice<CPL, kGroup, false>(orow, in, D, nch, base, sorted_rows, n);
+      reduce_slice_from<CPL, kGroup, false>(o0, orow, in, D, nch, base, sorted_rows, n);
   } else {
     float acc[CPL][8];
     load_acc<CPL, false>(acc, orow, nch, base);
@@ -575,14 +572,21 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_kernel(
   const int base = slice0 + lane;
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
   if (n <= kWave) {
+    // the initial row does not depend on the row list: load it alongside
+    const bool full = slice0 + kWave * CPL <= nch;
+    u32x4 o0[CPL];
+    if (full)
+      load_init<CPL, true>(o0, orow, nch, base);
+    else
+      load_init<CPL, false>(o0, orow, nch, base);
     const int r = lane < n ? list[beg + lane] : INT_MAX;
     const int sorted = wave_sort_asc(r, lane, sort_width(uniform(n)));
     // source row of each sorted row: rank * T_K + row (ascending row order kept)
     const int src = lane < n ? rank_of_row(pre, E, epr, sorted) * T_K + sorted : 0;
-    if (slice0 + kWave * CPL <= nch)
-      reduce_slice<CPL, kGroup, true>(orow, in, D, nch, base, src, n);
+    if (full)
+      reduce_slice_from<CPL, kGroup, true>(o0, orow, in, D, nch, base, src, n);
     else
-      reduce_slice<CPL, kGroup, false>(orow, in, D, nch, base, src, n);
+      reduce_slice_from<CPL, kGroup, false>(o0, orow, in, D, nch, base, src, n);
   } else {
     float acc[CPL][8];
     load_acc<CPL, false>(acc, orow, nch, base);
