@@ -77,15 +77,37 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
 }
 
 // ---------------------------------------------------------------- reductions
+// The value a DPP lane move brings to each lane (CTRL selects the source
+// lane); lanes of rows outside ROW_MASK get `identity` instead.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_from(float v, float identity) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(v),
+                                                    CTRL, ROW_MASK, 0xF, false));
+}
+
+// Wave-wide sum and max by DPP lane moves, no LDS-pipe round trips. Quad
+// swaps and the half-row and row mirrors leave each 16-lane row's result in
+// all its lanes; row_bcast15 then folds row 0 into row 1 and row 2 into row
+// 3, row_bcast31 row 1 into row 3, whose lane 63 holds the wave's result
+// (returned to every lane). Every lane of the wave must be active.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v = v + dpp_from<0xB1, 0xF>(v, -0.0f);   // quad_perm [1,0,3,2]
+  v = v + dpp_from<0x4E, 0xF>(v, -0.0f);   // quad_perm [2,3,0,1]
+  v = v + dpp_from<0x141, 0xF>(v, -0.0f);  // row_half_mirror
+  v = v + dpp_from<0x140, 0xF>(v, -0.0f);  // row_mirror
+  v = v + dpp_from<0x142, 0xA>(v, -0.0f);  // row_bcast15 into rows 1 and 3
+  v = v + dpp_from<0x143, 0xC>(v, -0.0f);  // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  const float lo = -__builtin_inff();
+  v = __builtin_fmaxf(v, dpp_from<0xB1, 0xF>(v, lo));
+  v = __builtin_fmaxf(v, dpp_from<0x4E, 0xF>(v, lo));
+  v = __builtin_fmaxf(v, dpp_from<0x141, 0xF>(v, lo));
+  v = __builtin_fmaxf(v, dpp_from<0x140, 0xF>(v, lo));
+  v = __builtin_fmaxf(v, dpp_from<0x142, 0xA>(v, lo));
+  v = __builtin_fmaxf(v, dpp_from<0x143, 0xC>(v, lo));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
