@@ -87,9 +87,14 @@ def parse():
     return p.parse_args()
 
 
+# headers every kernel source includes: part of each kernel's identity
+KERNEL_HEADERS = ["device.hpp", "launch.hpp"]
+
+
 def source_hash(names):
+    """Hash of the kernel sources `names` and the headers they include."""
     h = hashlib.sha256()
-    for n in names:
+    for n in list(names) + KERNEL_HEADERS:
         with open(os.path.join(ROOT, "combine_moe_shuffle_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
