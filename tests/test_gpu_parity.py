@@ -295,6 +295,31 @@ def test_gather_scale_general_long_lists(dev, row_order):
     assert np.array_equal(bits_host(out), want)
 
 
+def test_scatter_add_by_token_any_inverse_map(dev):
+    """An inverse map that no shuffle makes: rows dealt to tokens by a random
+    permutation, half of them valid, so tokens past V/K still own valid rows
+    and tokens before it may own none (the early initial-row load guesses
+    wrong both ways). The result equals the oracle's and the general path's."""
+    g = np.random.default_rng(31)
+    T, K, D = 300, 6, 8 * 90
+    a = T * K
+    perm = g.permutation(a).astype(np.int32)
+    rop = perm.reshape(T, K)
+    ti = np.empty(a, np.int32)
+    ti[perm] = np.repeat(np.arange(T, dtype=np.int32), K)
+    V = a // 2
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("scatter by token, any inverse map", T, K, D, V)
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_by_token(out, bf_dev(y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    out2 = bf_dev(out0, dev)
+    ops.moe_scatter_add(out2, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out2), want)
+
+
 # ---------------------------------------------------------------- padded combine
 PADDED_CASES = [
     # (name, T, D, E, K, EP)
