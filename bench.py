@@ -9,7 +9,8 @@ resident in HBM:
   quant     (T=4096, D=5120, E=16, K=1)
             moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
   prefill   (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
-  decode    (T=128, D=7168, K=8)   moe_finalize_rmsnorm
+  decode    (T=128, D=7168, K=8)   moe_finalize_rmsnorm; the line's "sweep"
+            also times T = 1, 8, 32 and 128 (per call and per kernel)
   prefill-swizzled  prefill with bf16 routing weights and 128x4-tiled scales
   mhc       (T=16384, D=5120, K=4, hc=4) moe_finalize_mhc with MXFP8
             (128x4-tiled scales)
@@ -203,11 +204,13 @@ def setup_dispatch(ctx, wl, with_cpu):
         cpu=cpu_baseline_dispatch(ctx.orc, inp, wl, vtc) if with_cpu else None)
 
 
-def setup_finalize(ctx, wl, with_cpu, variant=False):
-    """variant: bf16 routing weights and the 128x4-tiled scale layout."""
+def setup_finalize(ctx, wl, with_cpu, variant=False, T=None):
+    """variant: bf16 routing weights and the 128x4-tiled scale layout. T: the
+    token count, if not the workload's (the decode sweep)."""
     torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
-    fi = W.finalize_inputs(wl)
-    T, D, K = wl.T, wl.D, wl.K
+    T = wl.T if T is None else T
+    fi = W.finalize_inputs(wl, T=T)
+    D, K = wl.D, wl.K
     w = W.to_bf16_bits(fi.w) if variant else fi.w
     yd = ctx.bf(fi.y)
     wd = ctx.bf(w) if variant else torch.from_numpy(w).to(dev)
@@ -534,7 +537,34 @@ def main():
                      "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic},
         "cpu_baseline": s.cpu,
     }
+    if name == "decode":
+        line["sweep"] = decode_sweep(ctx, W.WORKLOADS[name], steps, warm)
     print(json.dumps(line), flush=True)
+
+
+def decode_sweep(ctx, wl, steps, warm):
+    """The decode finalize at every token count of the sweep: the step launched
+    from Python `steps` times back to back (wall clock per call, launch
+    included) and the kernel's own duration per launch (graph replay)."""
+    torch = ctx.torch
+    out = []
+    for T in wl.sweep_T:
+        sub = setup_finalize(ctx, wl, False, T=T)
+        fn = sub.stages["finalize"]
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t0) * 1e6 / steps
+        k_ms = stage_ms(torch, fn, steps)
+        b = sub.stage_bytes["finalize"]
+        out.append({"tokens": T, "step_us": round(step_us, 2), "kernel_us": round(k_ms * 1e3, 2),
+                    "tokens_per_s": T / (step_us * 1e-6), "bytes": b,
+                    "kernel_gbps": round(b / (k_ms * 1e-3) / 1e9, 1)})
+    return out
 
 
 def load_traffic(kernel, srcs, workload):
