@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true",
                    help="skip the cold-cache steps (profiling runs: every launch then warm)")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the decode line's token-count sweep (profiling runs: every "
+                        "launch at the workload's size)")
     p.add_argument("--graph", action="store_true",
                    help="replay a HIP graph of the step instead of launching its kernels from "
                         "Python (a graph launch costs more than a few kernel launches here)")
@@ -537,7 +540,7 @@ def main():
                      "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic},
         "cpu_baseline": s.cpu,
     }
-    if name == "decode":
+    if name == "decode" and not args.no_sweep:
         line["sweep"] = decode_sweep(ctx, W.WORKLOADS[name], steps, warm)
     print(json.dumps(line), flush=True)
 

@@ -366,16 +366,23 @@ hipError_t launch_gather_scale_quant(const uint16_t* x, int T, int D, const int*
                                      int64_t st, int64_t se, int E, const float* scale_ub,
                                      const int* valid_rows, uint8_t* out_fp8,
                                      float* out_scale, hipStream_t stream) {
-  // one row per workgroup of up to 16 waves; prefer more waves (fewer chunks
-  // per lane) while the row still divides evenly
-  static const int allowed[] = {2, 1, 3, 4, 5, 6, 7, 8};
-  const SliceShape sh = pick_slices(D / kChunk, allowed, 8, 16);
+  // one row per workgroup of up to 16 waves; among the shapes that waste the
+  // fewest lanes, the fewest waves (more chunks per lane): a 5120-wide row in
+  // one wave of 10 chunks per lane measured 15 % faster than in five waves of
+  // 2, with fewer rows sharing a workgroup barrier. 10 chunks per lane take
+  // 121 registers; more would spill under the 1024-thread launch bound.
+  static const int allowed[] = {10, 8, 7, 6, 5, 4, 3, 2, 1};
+  const SliceShape sh = pick_slices(D / kChunk, allowed, 9, 16);
   const dim3 grid(static_cast<unsigned>(a));
   const dim3 block(sh.nsl * kWave);
 #define L(C)                                                                             \
   hipLaunchKernelGGL(quant_rows_kernel<C>, grid, block, 0, stream, x, T, E, D, ti, ei, a, scores, \
                      st, se, scale_ub, valid_rows, out_fp8, out_scale)
-  MOE_DISPATCH_CPL(sh.cpl, L)
+  if (sh.cpl == 10) {
+    L(10);
+  } else {
+    MOE_DISPATCH_CPL(sh.cpl, L)
+  }
 #undef L
   return hipGetLastError();
 }

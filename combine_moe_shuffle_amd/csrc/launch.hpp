@@ -85,8 +85,8 @@ struct SliceShape {
   int cpl;  // chunks per lane
   int nsl;  // slices per row
 };
-// Smallest cpl in `allowed` (ascending) whose slice count is <= max_slices
-// and that wastes the fewest lanes.
+// The entry of `allowed` whose slice count is <= max_slices and that wastes
+// the fewest lanes; among equals, the earlier entry.
 SliceShape pick_slices(int nch, const int* allowed, int n_allowed, int max_slices);
 
 // Instantiate LAUNCH(cpl) for the run-time chunks-per-lane value (1..8).
