@@ -18,8 +18,10 @@ resident in HBM:
             moe_scatter_add_padded
   shuffling rows from EP=8 source ranks for one rank's 32 local experts:
             moe_combine_shuffling -> moe_split_shuffling
-A step launches its kernels from Python (--graph replays a HIP graph of the
-step instead; a graph launch costs more than a few kernel launches here).
+A step launches its kernels from Python through calls prepared once
+(ops.prepare: the op's checks run at set-up, each step repeats its library
+calls; --checked runs the checked op every step). --graph replays a HIP graph
+of the step instead; a graph launch costs more than a few kernel launches here.
 
 1. W untimed steps, then exactly K timed steps between two device
    synchronisations (wall clock, and a HIP event pair around the region): the
@@ -79,6 +81,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true",
                    help="skip the cold-cache steps (profiling runs: every launch then warm)")
+    p.add_argument("--checked", action="store_true",
+                   help="launch every stage through the checked op call (dtype, shape and "
+                        "device checks each call) instead of a call prepared once")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the decode line's token-count sweep (profiling runs: every "
                         "launch at the workload's size)")
@@ -412,7 +417,10 @@ def main():
     short = name == "decode"  # a few us per step: more steps amortise the region's ends
     steps = args.steps if args.steps is not None else (1000 if short else 50)
     warm = args.warmup if args.warmup is not None else (50 if short else 5)
-    stages = list(s.stages.items())
+    # each stage's library calls, checked and converted once (ops.prepare: the
+    # first call runs the op with every check); --checked goes through the
+    # checked op call every time
+    stages = [(n, fn if args.checked else ctx.ops.prepare(fn)) for n, fn in s.stages.items()]
     graph = args.graph
 
     def step():
@@ -521,8 +529,10 @@ def main():
         "vs_baseline": None,
         "dtype": s.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": {**s.config, "launch": "one HIP graph per step" if graph else
-                   "eager (kernels launched from Python)"},
+        "config": {**s.config, "launch": ("one HIP graph per step" if graph else
+                   "eager (kernels launched from Python)") +
+                   (", checked op calls" if args.checked else
+                    ", prepared calls (arguments checked once)")},
         "cold": None if args.no_cold else {
             **{kind: {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
                       "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
@@ -541,11 +551,11 @@ def main():
         "cpu_baseline": s.cpu,
     }
     if name == "decode" and not args.no_sweep:
-        line["sweep"] = decode_sweep(ctx, W.WORKLOADS[name], steps, warm)
+        line["sweep"] = decode_sweep(ctx, W.WORKLOADS[name], steps, warm, args.checked)
     print(json.dumps(line), flush=True)
 
 
-def decode_sweep(ctx, wl, steps, warm):
+def decode_sweep(ctx, wl, steps, warm, checked):
     """The decode finalize at every token count of the sweep: the step launched
     from Python `steps` times back to back (wall clock per call, launch
     included) and the kernel's own duration per launch (graph replay)."""
@@ -554,6 +564,7 @@ def decode_sweep(ctx, wl, steps, warm):
     for T in wl.sweep_T:
         sub = setup_finalize(ctx, wl, False, T=T)
         fn = sub.stages["finalize"]
+        fn = fn if checked else ctx.ops.prepare(fn)
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()

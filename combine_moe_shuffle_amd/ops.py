@@ -5,6 +5,10 @@ contiguity (ValueError), allocates outputs and workspaces with torch, and
 calls the library on torch's current HIP stream. All the work runs in the
 library's gfx950 kernels; there is no CPU path.
 
+prepare(op, ...) runs an op once with its checks and returns a callable that
+repeats its library calls on the same buffers (for loops that call one op on
+fixed buffers every step).
+
 bf16 tensors are torch.bfloat16; FP8 codes and UE8M0 scales are torch.uint8.
 Device-side counts (valid_token_count, valid_rows) are int32 tensors of one
 element on the same device, read by the kernels (no host sync).
@@ -32,7 +36,11 @@ def _stream(device):
 
 
 def _ptr(t):
-    return 0 if t is None else t.data_ptr()
+    if t is None:
+        return 0
+    if _recording is not None:
+        _recorded_tensors.append(t)  # a prepared call points into it: keep it
+    return t.data_ptr()
 
 
 def _need(t, name, dtype, ndim=None, device=None):
@@ -109,6 +117,62 @@ def _scores(scores, device):
     return scores.stride(0), scores.stride(1)
 
 
+# ---------------------------------------------------------------- calls
+_recording = None  # the list a prepare() run appends its library calls to
+_recorded_tensors = []  # and every tensor whose address those calls take
+
+
+def _call(name, *args):
+    """One status-returning library call; its last argument is the stream."""
+    f = _lib.fn(name)
+    if _recording is not None:
+        _recording.append((f, args[:-1]))
+    _lib.check(f(*args))
+
+
+class Prepared:
+    """An op's library calls with their arguments checked and converted once
+    (see prepare). Calling it makes the same calls again on the current stream
+    and returns the op's result (the same tensors, rewritten)."""
+
+    def __init__(self, calls, device, result, keep):
+        self._calls = tuple(calls)
+        self._device = device
+        self._result = result
+        self._keep = keep  # every tensor the calls point into stays alive
+
+    def __call__(self):
+        stream = _stream(self._device)
+        for f, args in self._calls:
+            _lib.check(f(*args, stream))
+        return self._result
+
+
+def prepare(op, *args, **kwargs):
+    """Runs ``op(*args, **kwargs)`` once, with all its checks, and records the
+    library calls it makes; returns a Prepared that repeats exactly those calls
+    (same device pointers, sizes and flags, the then-current stream) without
+    the Python-side checks and allocations. For a loop that calls one op on the
+    same buffers every step (a decode step). The Prepared holds references to
+    the arguments and the result; the caller must not resize them or replace
+    their storage. Device-side counts are read by the kernels at each call, as
+    in the op itself."""
+    global _recording, _recorded_tensors
+    if _recording is not None:
+        raise RuntimeError("prepare() does not nest")
+    calls = []
+    _recording, _recorded_tensors = calls, []
+    try:
+        result = op(*args, **kwargs)
+        keep = _recorded_tensors
+    finally:
+        _recording, _recorded_tensors = None, []
+    if not calls:
+        raise ValueError("the op made no library call (an empty input?)")
+    device = next((t.device for t in keep if t.is_cuda), None)
+    return Prepared(calls, device, result, (keep, args, kwargs, result))
+
+
 # ---------------------------------------------------------------- shuffle
 def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspace=None,
                 out=None):
@@ -141,9 +205,8 @@ def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspac
         ti = torch.empty(T * K, dtype=torch.int32, device=device)
         rop = torch.empty((T, K), dtype=torch.int32, device=device) if row_of_pair else None
     workspace, nbytes = _workspace(workspace, lib.moe_shuffle_workspace_bytes(T, E, K), device)
-    _lib.check(_lib.fn("moe_shuffle")(_ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
-                               _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace), nbytes,
-                               _stream(device)))
+    _call("moe_shuffle", _ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
+          _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace), nbytes, _stream(device))
     return counts, ei, ti, rop
 
 
@@ -183,9 +246,9 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
             workspace, _lib.load().moe_gather_scale_workspace_bytes(T, a), device)
     else:
         workspace = None
-    _lib.check(_lib.fn("moe_gather_scale")(
+    _call("moe_gather_scale",
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(vr), _ptr(out), _ptr(workspace), nbytes, _stream(device)))
+        scores.shape[1], _ptr(vr), _ptr(out), _ptr(workspace), nbytes, _stream(device))
     return out
 
 
@@ -201,9 +264,9 @@ def moe_gather_scale_by_token(x, row_of_pair, expert_indices, scores, valid_rows
     K = row_of_pair.shape[1]
     a = expert_indices.numel()
     out = _out(out, "out", torch.bfloat16, (a, D), device)
-    _lib.check(_lib.fn("moe_gather_scale_by_token")(
+    _call("moe_gather_scale_by_token",
         _ptr(x), T, D, _ptr(row_of_pair), K, _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(vr), _ptr(out), _stream(device)))
+        scores.shape[1], _ptr(vr), _ptr(out), _stream(device))
     return out
 
 
@@ -221,9 +284,9 @@ def moe_gather_scale_quant(x, token_indices, expert_indices, scores, scale_ub=No
             raise ValueError("scale_ub must hold one element")
     out = _out(out, "out", torch.uint8, (a, D), device)
     out_scale = _out(out_scale, "out_scale", torch.float32, (a,), device)
-    _lib.check(_lib.fn("moe_gather_scale_quant")(
+    _call("moe_gather_scale_quant",
         _ptr(x), T, D, _ptr(token_indices), _ptr(expert_indices), a, _ptr(scores), st, se,
-        scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream(device)))
+        scores.shape[1], _ptr(scale_ub), _ptr(vr), _ptr(out), _ptr(out_scale), _stream(device))
     return out, out_scale
 
 
@@ -250,8 +313,8 @@ def moe_scatter_add(out_tokens, in_tokens, token_indices, valid_rows=None, works
         raise ValueError("token_indices must have in_tokens.shape[0] entries")
     lib = _lib.load()
     workspace, nbytes = _workspace(workspace, lib.moe_scatter_add_workspace_bytes(T, a), device)
-    _lib.check(_lib.fn("moe_scatter_add")(_ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
-                                   a, D, _ptr(vr), _ptr(workspace), nbytes, _stream(device)))
+    _call("moe_scatter_add", _ptr(out_tokens), T, _ptr(in_tokens), _ptr(token_indices),
+          a, D, _ptr(vr), _ptr(workspace), nbytes, _stream(device))
     return out_tokens
 
 
@@ -263,9 +326,9 @@ def moe_scatter_add_by_token(out_tokens, in_tokens, row_of_pair, valid_rows=None
     T, D = out_tokens.shape
     if row_of_pair.shape[0] != T:
         raise ValueError("row_of_pair must be (T, K)")
-    _lib.check(_lib.fn("moe_scatter_add_by_token")(
+    _call("moe_scatter_add_by_token",
         _ptr(out_tokens), T, _ptr(in_tokens), _ptr(row_of_pair), row_of_pair.shape[1],
-        in_tokens.shape[0], D, _ptr(vr), _stream(device)))
+        in_tokens.shape[0], D, _ptr(vr), _stream(device))
     return out_tokens
 
 
@@ -288,9 +351,9 @@ def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, w
     lib = _lib.load()
     workspace, nbytes = _workspace(
         workspace, lib.moe_scatter_add_padded_workspace_bytes(T, T_K, E), device)
-    _lib.check(_lib.fn("moe_scatter_add_padded")(_ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
-                                          _ptr(token_indices), _ptr(out_tokens), T, D,
-                                          _ptr(workspace), nbytes, _stream(device)))
+    _call("moe_scatter_add_padded", _ptr(in_tokens), EP, T_K, _ptr(token_counts), E,
+          _ptr(token_indices), _ptr(out_tokens), T, D, _ptr(workspace), nbytes,
+          _stream(device))
     return out_tokens
 
 
@@ -318,10 +381,10 @@ def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, wit
     em_rows = out.shape[0] if name == "moe_combine_shuffling" else tokens.shape[0]
     workspace, nbytes = _workspace(
         workspace, lib.moe_shuffling_workspace_bytes(EP, c_hi - c_lo, em_rows), device)
-    _lib.check(_lib.fn(name)(
+    _call(name,
         _ptr(tokens), tokens.shape[0], _ptr(out), out.shape[0], D, _ptr(counts), EP, C, c_lo,
         c_hi, -1 if rank_stride is None else int(rank_stride), _ptr(oc), _ptr(workspace),
-        nbytes, _stream(device)))
+        nbytes, _stream(device))
     return out, oc
 
 
@@ -420,10 +483,10 @@ def moe_finalize_rmsnorm(y_permuted, expert_weights, row_of_pair, shared, gamma,
     out = _out(out, "out", torch.bfloat16, (T, D), device)
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
-    _lib.check(_lib.fn("moe_finalize_rmsnorm")(
+    _call("moe_finalize_rmsnorm",
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(gamma), float(eps), T, K, D, int(flags), _ptr(out), _ptr(codes), _ptr(scales),
-        _stream(device)))
+        _stream(device))
     return (out, codes, scales) if mxfp8 else out
 
 
@@ -465,11 +528,11 @@ def moe_finalize_mhc(y_permuted, expert_weights, row_of_pair, shared, residual, 
     out = _out(out, "out", torch.bfloat16, (T, D), device) if pre is not None else None
     codes, scales = (_mx_outputs(T, D, flags, device, mx_codes, mx_scales) if mxfp8
                      else (None, None))
-    _lib.check(_lib.fn("moe_finalize_mhc")(
+    _call("moe_finalize_mhc",
         _ptr(y_permuted), rows, _ptr(expert_weights), _ptr(row_of_pair), _ptr(shared),
         _ptr(residual), _ptr(post), _ptr(comb), _ptr(pre),
         _ptr(gamma) if pre is not None else 0, float(eps), T, K, D, hc, int(flags),
-        _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream(device)))
+        _ptr(residual_out), _ptr(out), _ptr(codes), _ptr(scales), _stream(device))
     return (residual_out, out, codes, scales) if mxfp8 else (residual_out, out)
 
 
@@ -481,8 +544,7 @@ def moe_convert_check(values):
     n = values.numel()
     bf = torch.empty(n, dtype=torch.int16, device=values.device)
     e4 = torch.empty(n, dtype=torch.uint8, device=values.device)
-    _lib.check(_lib.fn("moe_convert_check")(_ptr(values), n, _ptr(bf), _ptr(e4),
-                                             _stream(values.device)))
+    _call("moe_convert_check", _ptr(values), n, _ptr(bf), _ptr(e4), _stream(values.device))
     return bf, e4
 
 

@@ -307,3 +307,56 @@ def test_fast_call_rejects_like_ctypes(lib):
         s_ct = getattr(lib, name)(*args)
         m_ct = lib.moe_last_error().decode()
         assert s_fast == s_ct != OK and m_fast == m_ct, name
+
+
+def test_prepare_records_and_replays_library_calls(monkeypatch):
+    """ops.prepare: the op runs once with its checks; each replay repeats the
+    recorded library calls with the same arguments and the then-current
+    stream, keeps alive every tensor whose address a call takes (workspaces
+    the op allocated itself included) and returns the op's result."""
+    import gc
+    import weakref
+
+    import torch
+
+    from combine_moe_shuffle_amd import ops
+
+    seen = []
+
+    def entry(*args):
+        seen.append(args)
+        return 0
+
+    monkeypatch.setattr(_lib, "fn", lambda name: entry)
+    streams = iter([11, 22, 33])
+    monkeypatch.setattr(ops, "_stream", lambda device: next(streams))
+    refs = []
+
+    def op(t):
+        scratch = torch.empty(16, dtype=torch.uint8)   # the op's own workspace
+        refs.append(weakref.ref(scratch))
+        ops._call("moe_a", ops._ptr(t), 7, ops._ptr(scratch), ops._stream(t.device))
+        ops._call("moe_b", ops._ptr(t), 2.5, ops._stream(t.device))
+        return t
+
+    x = torch.zeros(4)
+    p = ops.prepare(op, x)
+    gc.collect()
+    assert refs[0]() is not None, "the op's workspace must outlive the op"
+    assert len(seen) == 2                                # the set-up run
+    assert p() is x
+    assert seen[2][:-1] == seen[0][:-1] and seen[3][:-1] == seen[1][:-1]
+    assert seen[2][-1] == seen[3][-1] == 33              # the replay's stream
+    assert seen[0][2] == refs[0]().data_ptr()
+    del p
+    gc.collect()
+    assert refs[0]() is None
+
+    with pytest.raises(ValueError, match="no library call"):
+        ops.prepare(lambda: None)
+
+    def nested():
+        ops.prepare(op, x)
+    with pytest.raises(RuntimeError, match="does not nest"):
+        ops.prepare(nested)
+    assert ops._recording is None

@@ -1069,6 +1069,49 @@ def test_every_op_is_deterministic(dev):
         assert torch.equal(ms, outs[0][2])
 
 
+def test_prepared_calls_match_checked_calls(dev):
+    """ops.prepare: each replay gives the bits of the checked op on the
+    current inputs (changed in place between replays), and the workspace the
+    shuffle allocated for itself survives allocator churn between replays."""
+    T, D, E, K, vtc = 300, 1024, 16, 4, 250
+    inp, _, _, _, _ = _dispatch_case(T, D, E, K, vtc)
+    s = torch.from_numpy(inp.scores).to(dev)
+    x = bf_dev(inp.x, dev)
+    vtc_d = scalar_dev(vtc, dev)
+    say("prepared", T, D, E, K, vtc)
+    shuffle = ops.prepare(ops.moe_shuffle, s, K, vtc_d)
+    counts, ei, ti, rop = shuffle()
+    rows = torch.zeros((T * K, D), dtype=torch.bfloat16, device=dev)
+    gather = ops.prepare(ops.moe_gather_scale_by_token, x, rop, ei, s, counts[E:], rows)
+    g = np.random.default_rng(5)
+    for rep in range(3):
+        junk = [torch.full((1 << 20,), rep, dtype=torch.int32, device=dev) for _ in range(4)]
+        del junk                                   # the caching allocator reuses these
+        new_s = g.standard_normal((T, E)).astype(np.float32)
+        s.copy_(torch.from_numpy(new_s))
+        got = shuffle()
+        assert got[0] is counts and got[3] is rop
+        gather()
+        wc, wei, wti, wrop = orc.shuffle(new_s, K, vtc)
+        assert np.array_equal(counts.cpu().numpy(), wc), rep
+        assert np.array_equal(ti.cpu().numpy(), wti), rep
+        assert np.array_equal(rop.cpu().numpy(), wrop), rep
+        V = int(wc[E])
+        want = orc.gather_scale(inp.x, wti, wei, new_s, V)
+        assert np.array_equal(bits_host(rows)[:V], want[:V]), rep
+
+    fi = W.finalize_inputs(W.WORKLOADS["decode"], T=32, D=7168, K=8)
+    y = bf_dev(fi.y, dev)
+    args = (y, torch.from_numpy(fi.w).to(dev), i32_dev(fi.row_of_pair, dev),
+            bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev), fi.eps)
+    fin = ops.prepare(ops.moe_finalize_rmsnorm, *args, mxfp8=True)
+    for rep in range(2):
+        y.copy_(bf_dev(W.to_bf16_bits(g.standard_normal(fi.y.shape).astype(np.float32)), dev))
+        o, mc, ms = fin()
+        ro, rmc, rms = ops.moe_finalize_rmsnorm(*args, mxfp8=True)
+        assert torch.equal(o, ro) and torch.equal(mc, rmc) and torch.equal(ms, rms), rep
+
+
 def test_binding_checks_caller_workspaces(dev):
     """A workspace the caller passes must be a contiguous tensor on the same
     GPU (else ValueError before any launch); any dtype works, its size counted
