@@ -1112,6 +1112,74 @@ def test_prepared_calls_match_checked_calls(dev):
         assert torch.equal(o, ro) and torch.equal(mc, rmc) and torch.equal(ms, rms), rep
 
 
+def test_prepared_calls_cover_every_op(dev):
+    """Every other op prepared once and replayed twice gives the bits of two
+    checked calls on twin buffers; the in-place combines accumulate twice
+    either way."""
+    g = np.random.default_rng(9)
+    T, D, E, K = 200, 640, 16, 4
+    rnd = lambda *sh: W.to_bf16_bits(g.standard_normal(sh).astype(np.float32))  # noqa: E731
+    s = torch.from_numpy(g.standard_normal((T, E)).astype(np.float32)).to(dev)
+    x, y, out0 = bf_dev(rnd(T, D), dev), bf_dev(rnd(T * K, D), dev), rnd(T, D)
+    counts, ei, ti, rop = ops.moe_shuffle(s, K, scalar_dev(180, dev))
+    vr = counts[E:]
+    fi = W.finalize_inputs(W.WORKLOADS["mhc"], T=8, D=1024, K=4)
+    m = W.mhc_inputs(W.WORKLOADS["mhc"], T=8, D=1024, hc=4)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    cnt = g.integers(0, 6, size=(4, 8)).astype(np.int32)
+    tok = bf_dev(rnd(int(cnt.sum()), 256), dev)
+    slabs = bf_dev(rnd(2, T * K, D), dev)
+
+    def zeros_like_rows():
+        return torch.zeros((T * K, D), dtype=torch.bfloat16, device=dev)
+
+    cases = {
+        "gather lists": lambda o: ops.moe_gather_scale(x, ti, ei, s, vr, o),
+        "gather rows": lambda o: ops.moe_gather_scale(x, ti, ei, s, vr, o, row_order=True),
+        "quant": lambda o: ops.moe_gather_scale_quant(x, ti, ei, s, None, vr, o[0], o[1]),
+        "scatter": lambda o: ops.moe_scatter_add(o, y, ti, vr),
+        "scatter by token": lambda o: ops.moe_scatter_add_by_token(o, y, rop, vr),
+        "padded": lambda o: ops.moe_scatter_add_padded(slabs, counts[:E].contiguous(), ti, o),
+        "combine_shuffling": lambda o: ops.moe_combine_shuffling(tok, i32_dev(cnt, dev), 2, 6,
+                                                                 out=o),
+        "mhc": lambda o: ops.moe_finalize_mhc(
+            bf_dev(fi.y, dev), f32(fi.w), i32_dev(fi.row_of_pair, dev), bf_dev(fi.shared, dev),
+            bf_dev(m.residual, dev), f32(m.post), f32(m.comb), f32(m.pre),
+            bf_dev(fi.gamma, dev), fi.eps, residual_out=o[0], out=o[1], mxfp8=True,
+            mx_codes=o[2], mx_scales=o[3]),
+    }
+
+    def buffers(name):
+        if name.startswith("gather"):
+            return zeros_like_rows()
+        if name == "quant":
+            return (torch.zeros((T * K, D), dtype=torch.uint8, device=dev),
+                    torch.zeros(T * K, dtype=torch.float32, device=dev))
+        if name.startswith("scatter") or name == "padded":
+            return bf_dev(out0, dev)
+        if name == "combine_shuffling":
+            return torch.zeros_like(tok)
+        return (torch.zeros((8, 4, 1024), dtype=torch.bfloat16, device=dev),
+                torch.zeros((8, 1024), dtype=torch.bfloat16, device=dev),
+                torch.zeros((8, 1024), dtype=torch.uint8, device=dev),
+                torch.zeros(ops._lib.load().moe_mxfp8_scale_bytes(8, 1024, 0), dtype=torch.uint8,
+                            device=dev))
+
+    def flat(r):
+        return [t for t in (r if isinstance(r, tuple) else (r,)) if isinstance(t, torch.Tensor)]
+
+    for name, run in cases.items():
+        say("prepared", name)
+        a, b = buffers(name), buffers(name)
+        run(a)
+        ra = run(a)
+        p = ops.prepare(run, b)
+        rb = p()
+        torch.cuda.synchronize()
+        for u, v in zip(flat(a) + flat(ra), flat(b) + flat(rb)):
+            assert torch.equal(u, v), name
+
+
 def test_binding_checks_caller_workspaces(dev):
     """A workspace the caller passes must be a contiguous tensor on the same
     GPU (else ValueError before any launch); any dtype works, its size counted
