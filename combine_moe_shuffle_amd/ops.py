@@ -15,6 +15,8 @@ element on the same device, read by the kernels (no host sync).
 """
 from __future__ import annotations
 
+import threading
+
 import torch
 
 from . import _lib
@@ -38,8 +40,9 @@ def _stream(device):
 def _ptr(t):
     if t is None:
         return 0
-    if _recording is not None:
-        _recorded_tensors.append(t)  # a prepared call points into it: keep it
+    keep = getattr(_rec, "tensors", None)
+    if keep is not None:
+        keep.append(t)  # a prepared call points into it: keep it
     return t.data_ptr()
 
 
@@ -118,15 +121,17 @@ def _scores(scores, device):
 
 
 # ---------------------------------------------------------------- calls
-_recording = None  # the list a prepare() run appends its library calls to
-_recorded_tensors = []  # and every tensor whose address those calls take
+# per thread: while prepare() runs an op, .calls collects its library calls and
+# .tensors every tensor whose address they take (other threads are unaffected)
+_rec = threading.local()
 
 
 def _call(name, *args):
     """One status-returning library call; its last argument is the stream."""
     f = _lib.fn(name)
-    if _recording is not None:
-        _recording.append((f, args[:-1]))
+    calls = getattr(_rec, "calls", None)
+    if calls is not None:
+        calls.append((f, args[:-1]))
     _lib.check(f(*args))
 
 
@@ -157,16 +162,14 @@ def prepare(op, *args, **kwargs):
     the arguments and the result; the caller must not resize them or replace
     their storage. Device-side counts are read by the kernels at each call, as
     in the op itself."""
-    global _recording, _recorded_tensors
-    if _recording is not None:
+    if getattr(_rec, "calls", None) is not None:
         raise RuntimeError("prepare() does not nest")
-    calls = []
-    _recording, _recorded_tensors = calls, []
+    calls, keep = [], []
+    _rec.calls, _rec.tensors = calls, keep
     try:
         result = op(*args, **kwargs)
-        keep = _recorded_tensors
     finally:
-        _recording, _recorded_tensors = None, []
+        _rec.calls = _rec.tensors = None
     if not calls:
         raise ValueError("the op made no library call (an empty input?)")
     device = next((t.device for t in keep if t.is_cuda), None)

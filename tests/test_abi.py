@@ -359,4 +359,20 @@ def test_prepare_records_and_replays_library_calls(monkeypatch):
         ops.prepare(op, x)
     with pytest.raises(RuntimeError, match="does not nest"):
         ops.prepare(nested)
-    assert ops._recording is None
+    assert getattr(ops._rec, "calls", None) is None
+
+    # a call made by another thread while prepare() runs is not recorded
+    import threading
+    other = threading.Thread(target=lambda: ops._call("moe_c", 1, 0))
+
+    def op_with_thread(t):
+        other.start()
+        other.join()
+        ops._call("moe_a", ops._ptr(t), ops._stream(t.device))
+        return t
+    monkeypatch.setattr(ops, "_stream", lambda device: 44)
+    n0 = len(seen)
+    p = ops.prepare(op_with_thread, x)
+    assert len(seen) == n0 + 2                     # both calls ran once
+    p()
+    assert seen[-1] == seen[-2] and seen[-1][0] == x.data_ptr()   # only moe_a replayed
