@@ -173,6 +173,8 @@ def prepare(op, *args, **kwargs):
     if not calls:
         raise ValueError("the op made no library call (an empty input?)")
     device = next((t.device for t in keep if t.is_cuda), None)
+    if device is None:
+        raise ValueError("the op's library calls point into no GPU tensor")
     return Prepared(calls, device, result, (keep, args, kwargs, result))
 
 
