@@ -172,9 +172,9 @@ def prepare(op, *args, **kwargs):
         _rec.calls = _rec.tensors = None
     if not calls:
         raise ValueError("the op made no library call (an empty input?)")
-    device = next((t.device for t in keep if t.is_cuda), None)
-    if device is None:
-        raise ValueError("the op's library calls point into no GPU tensor")
+    if not keep:
+        raise ValueError("the op's library calls point into no tensor")
+    device = next((t.device for t in keep if t.is_cuda), keep[0].device)
     return Prepared(calls, device, result, (keep, args, kwargs, result))
 
 
