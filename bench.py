@@ -596,20 +596,24 @@ def load_traffic(kernel, srcs, workload):
 
 
 # ------------------------------------------------------------------ CPU oracle
-def _median_time(fn, reps):
-    """Median wall time of `reps` runs of fn, the process pinned to one core
-    meanwhile (the oracle is single-threaded)."""
+CPU_SAMPLE_S = 10.0  # about this much single-core oracle time per baseline
+
+
+def _median_time(fn):
+    """Median wall time of runs of fn, the process pinned to one core meanwhile
+    (the oracle is single-threaded): at least 3 runs, more while they add up
+    to under CPU_SAMPLE_S seconds (at most 25). Returns (median, runs)."""
     old = os.sched_getaffinity(0)
     os.sched_setaffinity(0, {min(old)})
     try:
         ts = []
-        for _ in range(reps):
+        while len(ts) < 3 or (sum(ts) < CPU_SAMPLE_S and len(ts) < 25):
             t0 = time.perf_counter()
             fn()
             ts.append(time.perf_counter() - t0)
     finally:
         os.sched_setaffinity(0, old)
-    return float(np.median(ts))
+    return float(np.median(ts)), len(ts)
 
 
 def _host():
@@ -629,7 +633,7 @@ def _host():
 
 def cpu_baseline_dispatch(orc, inp, wl, vtc):
     """The oracle on the same step (shuffle, gather, scatter-add), single
-    thread; median of 3 runs."""
+    thread; the median over about CPU_SAMPLE_S seconds of runs."""
     K = wl.K
     stage_t = {"shuffle": [], "gather": [], "scatter": []}
     rows = np.empty((wl.T * K, wl.D), np.uint16)
@@ -649,10 +653,10 @@ def cpu_baseline_dispatch(orc, inp, wl, vtc):
         for k, d in zip(stage_t, (t1 - t0, t2 - t1, t3 - t2)):
             stage_t[k].append(d)
 
-    t = _median_time(run, 3)
+    t, runs = _median_time(run)
     return {"value": vtc / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole step (shuffle, gather, scatter-add) of the {wl.name} "
-                      f"workload, {vtc} valid tokens; median of 3 runs, "
+                      f"workload, {vtc} valid tokens; median of {runs} runs, "
                       f"{t:.2f} s each",
             "stage_s": {k: round(float(np.median(v)), 4) for k, v in stage_t.items()}}
 
@@ -668,9 +672,9 @@ def cpu_baseline_finalize(orc, fi, wl, w, flags, name):
                              np.ascontiguousarray(fi.shared[sub]), fi.gamma, fi.eps,
                              flags=flags | (4 if flags & 2 else 0), mxfp8=wl.mxfp8)
 
-    t = _median_time(run, 3)
+    t, runs = _median_time(run)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {T} tokens of the {name} finalize; median of 3 "
+            "sample": f"first {n} of {T} tokens of the {name} finalize; median of {runs} "
                       f"runs, {t:.2f} s each"}
 
 
@@ -684,9 +688,9 @@ def cpu_baseline_mhc(orc, fi, m, wl):
                          c(m.residual[sub]), c(m.post[sub]), c(m.comb[sub]), c(m.pre[sub]),
                          fi.gamma, fi.eps, flags=4, mxfp8=True)
 
-    t = _median_time(run, 3)
+    t, runs = _median_time(run)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {wl.T} tokens of the mhc finalize; median of 3 runs, "
+            "sample": f"first {n} of {wl.T} tokens of the mhc finalize; median of {runs} runs, "
                       f"{t:.2f} s each"}
 
 
@@ -706,10 +710,10 @@ def cpu_baseline_padded(orc, W, wl):
     def run():
         orc.scatter_add_padded(out0.copy(), slabs, counts[:wl.E], ti)
 
-    t = _median_time(run, 3)
+    t, runs = _median_time(run)
     return {"value": vtc / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"T={T} tokens of the same routing ({vtc} valid), EP={wl.ep}; median "
-                      f"of 3 runs, {t:.2f} s each"}
+                      f"of {runs} runs, {t:.2f} s each"}
 
 
 def cpu_baseline_shuffling(orc, counts, D, wl):
@@ -723,9 +727,9 @@ def cpu_baseline_shuffling(orc, counts, D, wl):
         em, _ = orc.combine_shuffling(tok, counts, 0, EG, None, out=np.empty_like(tok))
         orc.split_shuffling(em, counts, 0, EG, None, out=np.empty_like(tok))
 
-    t = _median_time(run, 3)
+    t, runs = _median_time(run)
     return {"value": rows / t, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole step ({rows} rows, combine + split); median of 3 runs, "
+            "sample": f"the whole step ({rows} rows, combine + split); median of {runs} runs, "
                       f"{t:.2f} s each"}
 
 
