@@ -540,6 +540,8 @@ def main():
             "stage_us_after_read": {n: round(cold_stage[n] * 1e3, 2) for n in names},
             "roofline_frac_after_read":
                 s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "routed_rows_per_s": (s.config["routed_rows"] / (ms_step * 1e-3)
+                              if "routed_rows" in s.config else None),
         "hbm_gbps": total_bytes / (ms_step * 1e-3) / 1e9,
         "hbm_frac": total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "stage_us": {n: round(st_ms[n] * 1e3, 2) for n in names},
