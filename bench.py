@@ -145,6 +145,57 @@ def stage_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+# ------------------------------------------------------------------ algorithmic bytes
+# Per launch: unique inputs read once, outputs written once, valid rows only
+# (rows past the valid count are neither read nor written). bf16 rows are 2*D
+# bytes; indices, counts, scores and fp32 weights 4 bytes.
+def dispatch_bytes(T, D, E, K, vtc, quant):
+    """shuffle: scores + token/expert indices and row_of_pair + counts;
+    gather: x once per routed token (bf16) or per row (FP8 rowwise, codes and
+    scales out) + the routed rows + the indices and scores it reads;
+    scatter: the routed rows + each routed token's row read and written +
+    row_of_pair."""
+    a, V, row_b = T * K, vtc * K, D * 2
+    shuffle = T * E * 4 + 3 * a * 4 + (E + 1) * 4
+    if quant:
+        gather = V * row_b + V * D + V * 4 + 2 * V * 4 + V * 4
+    else:
+        gather = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
+    scatter = V * row_b + 2 * vtc * row_b + T * K * 4
+    return {"shuffle": shuffle, "gather": gather, "scatter": scatter}
+
+
+def finalize_bytes(T, D, K, scale_bytes=None, bf16_weights=False):
+    """K expert rows, shared row and output per token, gamma once, the slot
+    rows and weights; with MXFP8 (scale_bytes given) the codes and scales."""
+    row_b = D * 2
+    b = T * K * row_b + 2 * T * row_b + row_b + T * K * (6 if bf16_weights else 8)
+    if scale_bytes is not None:
+        b += T * D + scale_bytes
+    return b
+
+
+def mhc_bytes(T, D, K, hc, scale_bytes):
+    """The finalize's bytes plus the hc residual streams read and written and
+    the per-token mixing coefficients (post, pre: hc each; comb: hc*hc)."""
+    row_b = D * 2
+    return (T * K * row_b + T * row_b + 2 * T * hc * row_b + T * row_b + row_b + T * K * 8 +
+            T * hc * 8 + T * hc * hc * 4 + T * D + scale_bytes)
+
+
+def padded_bytes(D, E, K, vtc):
+    """The routed rows from the slabs, each routed token's row read and
+    written, the rows' token indices and the expert counts."""
+    V, row_b = vtc * K, D * 2
+    return V * row_b + 2 * vtc * row_b + V * 4 + E * 4
+
+
+def shuffling_bytes(rows, D, EP, EG):
+    """Every moved row read and written once, the count matrix and the
+    output counts."""
+    return 2 * rows * D * 2 + EP * EG * 4 + (EG + 1) * 4
+
+
 # ------------------------------------------------------------------ workloads
 def setup_dispatch(ctx, wl, with_cpu):
     torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
@@ -187,18 +238,9 @@ def setup_dispatch(ctx, wl, with_cpu):
     def scatter():
         ops.moe_scatter_add_by_token(out, y, rop, vr)
 
-    # algorithmic bytes per launch (unique data read once, written once)
-    row_b = D * 2
-    shuffle_bytes = T * E * 4 + 3 * a * 4 + (E + 1) * 4
-    if quant:
-        gather_bytes = V * row_b + V * D + V * 4 + 2 * V * 4 + V * 4
-    else:
-        gather_bytes = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
-    scatter_bytes = V * row_b + 2 * vtc * row_b + T * K * 4
     return SimpleNamespace(
         stages={"shuffle": shuffle, "gather": gather, "scatter": scatter},
-        stage_bytes={"shuffle": shuffle_bytes, "gather": gather_bytes,
-                     "scatter": scatter_bytes},
+        stage_bytes=dispatch_bytes(T, D, E, K, vtc, quant),
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
         config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} valid_token_count={vtc}",
                 "tokens": T, "hidden": D, "experts": E, "top_k": K,
@@ -236,10 +278,7 @@ def setup_finalize(ctx, wl, with_cpu, variant=False, T=None):
         ops.moe_finalize_rmsnorm(yd, wd, ropd, shd, gd, wl.eps, out=outd, mxfp8=mx,
                                  scale_layout=layout, mx_codes=codes, mx_scales=scales)
 
-    row_b = D * 2
-    fin_bytes = T * K * row_b + 2 * T * row_b + row_b + T * K * (6 if variant else 8)
-    if mx:
-        fin_bytes += T * D + sbytes
+    fin_bytes = finalize_bytes(T, D, K, sbytes if mx else None, bf16_weights=variant)
     name = wl.name + ("-swizzled" if variant else "")
     return SimpleNamespace(
         stages={"finalize": finalize}, stage_bytes={"finalize": fin_bytes},
@@ -275,11 +314,9 @@ def setup_mhc(ctx, wl, with_cpu):
                              residual_out=res_out, out=outd, mxfp8=True,
                              scale_layout="swizzled", mx_codes=codes, mx_scales=scales)
 
-    row_b = D * 2
-    nbytes = (T * K * row_b + T * row_b + 2 * T * hc * row_b + T * row_b + row_b + T * K * 8 +
-              T * hc * 8 + T * hc * hc * 4 + T * D + sbytes)
     return SimpleNamespace(
-        stages={"finalize_mhc": finalize_mhc}, stage_bytes={"finalize_mhc": nbytes},
+        stages={"finalize_mhc": finalize_mhc},
+        stage_bytes={"finalize_mhc": mhc_bytes(T, D, K, hc, sbytes)},
         units_per_step=T, unit="tokens/s",
         metric="mHC finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
         config={"workload": f"{wl.name}: T={T} D={D} K={K} hc={hc} MXFP8 128x4-tiled scales",
@@ -319,10 +356,9 @@ def setup_padded(ctx, wl, with_cpu):
     def padded_scatter():
         ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
 
-    row_b = D * 2
-    nbytes = V * row_b + 2 * vtc * row_b + V * 4 + E * 4
     return SimpleNamespace(
-        stages={"padded_scatter": padded_scatter}, stage_bytes={"padded_scatter": nbytes},
+        stages={"padded_scatter": padded_scatter},
+        stage_bytes={"padded_scatter": padded_bytes(D, E, K, vtc)},
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
         config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} EP={EP} "
                             f"valid_token_count={vtc} static (EP, T*K, D) buffer",
@@ -357,8 +393,7 @@ def setup_shuffling(ctx, wl, with_cpu):
     def split_shuffling():
         ops.moe_split_shuffling(em, counts, 0, EG, None, out=back, workspace=ws_s)
 
-    row_b = D * 2
-    nb = 2 * rows * row_b + EP * EG * 4 + (EG + 1) * 4
+    nb = shuffling_bytes(rows, D, EP, EG)
     return SimpleNamespace(
         stages={"combine_shuffling": combine_shuffling, "split_shuffling": split_shuffling},
         stage_bytes={"combine_shuffling": nb, "split_shuffling": nb},
