@@ -115,15 +115,33 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
   // loads first, all of them, from clamped (always valid) addresses; the
   // keys of dead tokens and of experts >= E are masked to 0 afterwards
   float sv[kTokPerWave][PL];
+  // contiguous rows that every lane fills (E == 64 * PL) and 16-byte aligned
+  // lane runs: one 16-byte load per 4 experts instead of four 4-byte loads
+  const bool vec = (PL % 4 == 0) && se == 1 && E == kWave * PL && st % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
 #pragma unroll
   for (int q = 0; q < kTokPerWave; ++q) {
     const int t = t0 + wave + q * nwaves;
     live[q] = t < vtc;  // wave-uniform
     const float* srow = scores + static_cast<int64_t>(live[q] ? t : 0) * st;
+    if (vec) {
 #pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      const int e = min(lane * PL + j, E - 1);
-      sv[q][j] = srow[static_cast<int64_t>(e) * se];
+      for (int j = 0; j < PL; j += 4) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(srow + lane * PL + j);
+        sv[q][j] = v4.x;
+        if constexpr (PL >= 4) {
+          sv[q][j + 1] = v4.y;
+          sv[q][j + 2] = v4.z;
+          sv[q][j + 3] = v4.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PL; ++j) {
+        const int e = min(lane * PL + j, E - 1);
+        sv[q][j] = srow[static_cast<int64_t>(e) * se];
+      }
     }
   }
 #pragma unroll
