@@ -200,8 +200,9 @@ def test_gather_scale_bit_exact(dev, case, path):
 
 @pytest.mark.parametrize("ub", [None, 1200.0, 1e-3])
 @pytest.mark.parametrize("shape", [(96, 8 * (64 * 5 + 7), 6, 2, 90), (40, 5120, 16, 1, None),
-                                   (20, 8, 3, 2, None), (6, 65536, 4, 1, None)],
-                         ids=["ragged", "D5120", "D8", "Dmax"])
+                                   (20, 8, 3, 2, None), (6, 65536, 4, 1, None),
+                                   (30, 8 * 637, 16, 2, 25)],
+                         ids=["ragged", "D5120", "D8", "Dmax", "one-wave-ragged"])
 def test_gather_scale_quant(dev, ub, shape):
     T, D, E, K, vtc = shape
     inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=3)
@@ -465,6 +466,7 @@ FIN_CASES = [
     ("many-tokens", 2100, 640, 4, 0.05, True, 0, True),  # the many-token shape
     ("K1", 9, 256, 1, 0.0, False, 0, True),
     ("Dmax", 3, 65536, 2, 0.0, True, 0, True),         # the widest row
+    ("tiny-ragged", 5, 32 * 49, 8, 0.1, True, 0, True),  # <= 32 tokens, partial last wave
 ]
 
 
