@@ -15,7 +15,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_shuffle.so")
 # MOE_ABI_VERSION of include/moe_shuffle.h that SIGNATURES describes
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -33,6 +33,8 @@ SIGNATURES = {
     "moe_shuffle_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_shuffle": (_status, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p,
                               _sz, _p]),
+    "moe_shuffle_noalloc": (_status, [_p, _i64, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p,
+                                      _p]),
     "moe_gather_scale_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_gather_scale": (_status, [_p, _i32, _i32, _p, _p, _i32, _p, _i64, _i64, _i32, _p,
                                    _p, _p, _sz, _p]),

@@ -4,8 +4,16 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "moe_shuffle.h"
 #include "launch.hpp"
+
+// The workspace of moe_shuffle_noalloc: a static device array, one copy per
+// GPU. In host code `scratch` names a host-side stand-in, never a device
+// address; the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -83,11 +91,10 @@ size_t moe_shuffle_workspace_bytes(int32_t T, int32_t E, int32_t K) {
   return moe::shuffle_workspace_bytes(T, E, K);
 }
 
-moe_status_t moe_shuffle(const float* scores, int64_t stride_t, int64_t stride_e, int32_t T,
-                         int32_t E, int32_t K, const int32_t* valid_token_count,
-                         int32_t* counts, int32_t* expert_indices, int32_t* token_indices,
-                         int32_t* row_of_pair, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+static moe_status_t check_shuffle(const float* scores, int64_t stride_t, int64_t stride_e,
+                                  int32_t T, int32_t E, int32_t K, const int32_t* counts,
+                                  const int32_t* expert_indices,
+                                  const int32_t* token_indices) {
   REQUIRE(T >= 0, MOE_ERR_INVALID_ARG, "T must be >= 0 (got %d)", T);
   moe_status_t s = check_scores(scores, stride_t, stride_e, T, E);
   if (s != MOE_OK) return s;
@@ -97,8 +104,20 @@ moe_status_t moe_shuffle(const float* scores, int64_t stride_t, int64_t stride_e
   REQUIRE(static_cast<int64_t>(T) * K < (int64_t{1} << 31), MOE_ERR_INVALID_ARG,
           "T*K must be < 2^31");
   REQUIRE(counts != nullptr, MOE_ERR_INVALID_ARG, "counts is NULL");
-  if (T > 0) {
+  if (T > 0)
     REQUIRE(expert_indices && token_indices, MOE_ERR_INVALID_ARG, "index outputs are NULL");
+  return MOE_OK;
+}
+
+moe_status_t moe_shuffle(const float* scores, int64_t stride_t, int64_t stride_e, int32_t T,
+                         int32_t E, int32_t K, const int32_t* valid_token_count,
+                         int32_t* counts, int32_t* expert_indices, int32_t* token_indices,
+                         int32_t* row_of_pair, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  moe_status_t s =
+      check_shuffle(scores, stride_t, stride_e, T, E, K, counts, expert_indices, token_indices);
+  if (s != MOE_OK) return s;
+  if (T > 0) {
     const size_t need = moe::shuffle_workspace_bytes(T, E, K);
     REQUIRE(workspace != nullptr && workspace_bytes >= need, MOE_ERR_WORKSPACE,
             "shuffle workspace needs %zu bytes (got %zu)", need, workspace_bytes);
@@ -109,6 +128,72 @@ moe_status_t moe_shuffle(const float* scores, int64_t stride_t, int64_t stride_e
                                         counts, expert_indices, token_indices, row_of_pair,
                                         workspace, static_cast<hipStream_t>(stream)),
                     "moe_shuffle");
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device
+
+// The device address of this GPU's copy of `scratch`, where GPU = the
+// current device, which must also be the stream's. Taken once per device.
+moe_status_t noalloc_scratch(void* stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    REQUIRE(sdev == dev, MOE_ERR_INVALID_ARG,
+            "the stream belongs to device %d but the current device is %d", sdev, dev);
+  }
+  REQUIRE(dev >= 0 && dev < kMaxScratchDevices, MOE_ERR_UNSUPPORTED,
+          "device %d is beyond the %d devices the static scratch serves", dev,
+          kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_shuffle_noalloc(const float* scores, int64_t stride_t, int64_t stride_e,
+                                 int32_t T, int32_t E, int32_t K,
+                                 const int32_t* valid_token_count, int32_t* counts,
+                                 int32_t* expert_indices, int32_t* token_indices,
+                                 int32_t* row_of_pair, void* stream) {
+  moe_status_t s =
+      check_shuffle(scores, stride_t, stride_e, T, E, K, counts, expert_indices, token_indices);
+  if (s != MOE_OK) return s;
+  void* ws = nullptr;
+  if (T > 0) {
+    const size_t need = moe::shuffle_workspace_bytes(T, E, K);
+    REQUIRE(need <= MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_WORKSPACE,
+            "moe_shuffle_noalloc: T=%d, E=%d, K=%d need %zu bytes of scratch, more than the "
+            "%zu the library holds",
+            T, E, K, need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+    s = noalloc_scratch(stream, &ws);
+    if (s != MOE_OK) return s;
+  }
+  // T == 0 only writes counts (all zero) and touches no scratch
+  return hip_status(moe::launch_shuffle(scores, stride_t, stride_e, T, E, K, valid_token_count,
+                                        counts, expert_indices, token_indices, row_of_pair, ws,
+                                        static_cast<hipStream_t>(stream)),
+                    "moe_shuffle_noalloc");
 }
 
 static moe_status_t check_gather(const moe_bf16_t* x, int32_t T, int32_t D, int32_t a,

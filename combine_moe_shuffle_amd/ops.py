@@ -179,6 +179,29 @@ def prepare(op, *args, **kwargs):
 
 
 # ---------------------------------------------------------------- shuffle
+def _shuffle_outputs(out, T, E, K, row_of_pair, device):
+    """The four shuffle outputs: the caller's (checked) or new tensors."""
+    if out is None:
+        counts = torch.empty(E + 1, dtype=torch.int32, device=device)
+        ei = torch.empty(T * K, dtype=torch.int32, device=device)
+        ti = torch.empty(T * K, dtype=torch.int32, device=device)
+        rop = torch.empty((T, K), dtype=torch.int32, device=device) if row_of_pair else None
+        return counts, ei, ti, rop
+    counts, ei, ti, rop = out
+    for t, n, numel in ((counts, "counts", E + 1), (ei, "expert_indices", T * K),
+                        (ti, "token_indices", T * K)):
+        _need(t, n, torch.int32, device=device)
+        _contig(t, n)
+        if t.numel() != numel:
+            raise ValueError(f"{n} must have {numel} elements")
+    if rop is not None:
+        _need(rop, "row_of_pair", torch.int32, device=device)
+        _contig(rop, "row_of_pair")
+        if rop.numel() != T * K:
+            raise ValueError(f"row_of_pair must have {T * K} elements")
+    return counts, ei, ti, rop
+
+
 def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspace=None,
                 out=None):
     """Top-k routing + stable counting sort of (token, expert) pairs by expert.
@@ -191,27 +214,25 @@ def moe_shuffle(scores, K, valid_token_count=None, *, row_of_pair=True, workspac
     T, E = scores.shape
     vtc = _scalar_i32(valid_token_count, "valid_token_count", device)
     lib = _lib.load()
-    if out is not None:
-        counts, ei, ti, rop = out
-        for t, n, numel in ((counts, "counts", E + 1), (ei, "expert_indices", T * K),
-                            (ti, "token_indices", T * K)):
-            _need(t, n, torch.int32, device=device)
-            _contig(t, n)
-            if t.numel() != numel:
-                raise ValueError(f"{n} must have {numel} elements")
-        if rop is not None:
-            _need(rop, "row_of_pair", torch.int32, device=device)
-            _contig(rop, "row_of_pair")
-            if rop.numel() != T * K:
-                raise ValueError(f"row_of_pair must have {T * K} elements")
-    else:
-        counts = torch.empty(E + 1, dtype=torch.int32, device=device)
-        ei = torch.empty(T * K, dtype=torch.int32, device=device)
-        ti = torch.empty(T * K, dtype=torch.int32, device=device)
-        rop = torch.empty((T, K), dtype=torch.int32, device=device) if row_of_pair else None
+    counts, ei, ti, rop = _shuffle_outputs(out, T, E, K, row_of_pair, device)
     workspace, nbytes = _workspace(workspace, lib.moe_shuffle_workspace_bytes(T, E, K), device)
     _call("moe_shuffle", _ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
           _ptr(ei), _ptr(ti), _ptr(rop), _ptr(workspace), nbytes, _stream(device))
+    return counts, ei, ti, rop
+
+
+def moe_shuffle_noalloc(scores, K, valid_token_count=None, *, row_of_pair=True, out=None):
+    """moe_shuffle through the entry point that allocates nothing: its
+    workspace is the library's static per-GPU scratch. With ``out`` given the
+    call allocates nothing here either. Calls on one GPU share that scratch,
+    so they must be ordered (one stream)."""
+    device = scores.device
+    st, se = _scores(scores, device)
+    T, E = scores.shape
+    vtc = _scalar_i32(valid_token_count, "valid_token_count", device)
+    counts, ei, ti, rop = _shuffle_outputs(out, T, E, K, row_of_pair, device)
+    _call("moe_shuffle_noalloc", _ptr(scores), st, se, T, E, K, _ptr(vtc), _ptr(counts),
+          _ptr(ei), _ptr(ti), _ptr(rop), _stream(device))
     return counts, ei, ti, rop
 
 

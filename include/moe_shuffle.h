@@ -25,7 +25,9 @@
  *  - The caller owns all memory. The library allocates nothing, keeps no
  *    pointer after a call returns and holds no state; calls are reentrant.
  *    Calls that share output or workspace memory must be ordered by the
- *    caller (same stream, or events).
+ *    caller (same stream, or events). The one exception is
+ *    moe_shuffle_noalloc, whose workspace is a static device array of the
+ *    library (see there).
  *  - Errors: all argument checks run on the host before any launch. On a
  *    failed check nothing is enqueued and the status says why
  *    (moe_last_error() gives a message for the calling thread):
@@ -74,7 +76,7 @@ typedef enum {
 } moe_status_t;
 
 /* Version of this ABI (bumped on any signature change). */
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 MOE_API int moe_abi_version(void);
 
 /* Static name of a status code. */
@@ -127,6 +129,36 @@ MOE_API moe_status_t moe_shuffle(const float *scores, int64_t stride_t, int64_t 
                          int32_t *expert_indices, int32_t *token_indices,
                          int32_t *row_of_pair, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_shuffle_noalloc -- moe_shuffle without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * serving loops that must not call the allocator, harnesses that forbid it.
+ *
+ * Same arguments, results and checks as moe_shuffle, and the same kernels.
+ * The workspace is instead a static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES bytes, of which each GPU the library runs on
+ * holds its own copy until the process ends. The call allocates nothing and
+ * calls no allocating routine. Its kernels write every scratch byte they read
+ * before reading it, so nothing needs clearing between calls.
+ *
+ * Errors, beyond moe_shuffle's:
+ *   MOE_ERR_WORKSPACE    moe_shuffle_workspace_bytes(T, E, K) exceeds
+ *                        MOE_NOALLOC_SCRATCH_BYTES (e.g. T = 8192, E = 256,
+ *                        K = 8 needs 512 KiB)
+ *   MOE_ERR_INVALID_ARG  `stream` belongs to another device than the
+ *                        current one (the scratch address is per device)
+ *   MOE_ERR_HIP          the scratch address could not be obtained
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, or threads without ordering) race and give
+ * undefined results. Order them on one stream.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+MOE_API moe_status_t moe_shuffle_noalloc(const float *scores, int64_t stride_t,
+                                 int64_t stride_e, int32_t T, int32_t E, int32_t K,
+                                 const int32_t *valid_token_count, int32_t *counts,
+                                 int32_t *expert_indices, int32_t *token_indices,
+                                 int32_t *row_of_pair, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_gather_scale -- dispatch: gather token rows into expert order, scaled

@@ -66,7 +66,7 @@ def test_signature_table_arity_matches_header(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_str(0) == b"MOE_OK"
     assert lib.moe_status_str(3) == b"MOE_ERR_WORKSPACE"
 
@@ -109,6 +109,19 @@ def test_shuffle_rejects(lib):
     # T*K overflow
     assert f(FAKE, 64, 1, 1 << 30, 64, 8, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
              None) == INVALID
+
+
+@host_only
+def test_shuffle_noalloc_rejects(lib):
+    f = lib.moe_shuffle_noalloc
+    # the workspace the sizes need exceeds the static scratch: refused before
+    # any HIP call
+    assert f(FAKE, 256, 1, 1 << 20, 256, 8, None, FAKE, FAKE, FAKE, None, None) == WORKSPACE
+    assert "scratch" in _err(lib)
+    # the shuffle's own checks come first
+    assert f(FAKE, 8, 1, 4, 8, 9, None, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert f(FAKE, 2048, 1, 4, 2048, 8, None, FAKE, FAKE, FAKE, None, None) == UNSUPPORTED
+    assert f(FAKE, 8, 1, 64, 8, 2, None, None, FAKE, FAKE, None, None) == INVALID
 
 
 @host_only
