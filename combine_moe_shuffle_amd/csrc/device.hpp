@@ -99,6 +99,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = v + dpp_from<0x143, 0xC>(v, -0.0f);  // row_bcast31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// The same sum in fp64: each DPP step moves the two 32-bit halves of the
+// double with the same control (lanes of masked rows get -0.0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_from_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xFFFFFFFFu), CTRL,
+                                             ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(0x80000000u),
+                                             static_cast<int>(u >> 32), CTRL, ROW_MASK, 0xF,
+                                             false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                        static_cast<uint32_t>(lo));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = v + dpp_from_f64<0xB1, 0xF>(v);
+  v = v + dpp_from_f64<0x4E, 0xF>(v);
+  v = v + dpp_from_f64<0x141, 0xF>(v);
+  v = v + dpp_from_f64<0x140, 0xF>(v);
+  v = v + dpp_from_f64<0x142, 0xA>(v);
+  v = v + dpp_from_f64<0x143, 0xC>(v);
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(u & 0xFFFFFFFFu), 63));
+  const uint32_t hi =
+      static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), 63));
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
 __device__ __forceinline__ float wave_max(float v) {
   const float lo = -__builtin_inff();
   v = __builtin_fmaxf(v, dpp_from<0xB1, 0xF>(v, lo));

@@ -162,18 +162,23 @@ __device__ __forceinline__ void routed_sum(u32x4 (&h)[CPL], const u32x4 (&sh)[CP
 }
 
 // RMSNorm of the bf16 row x (this lane's chunks) and its optional MXFP8:
-// ss in fp32 (flags bit 0: squares rounded to bf16), lane tree then waves in
-// order through LDS; inv = correctly rounded 1/sqrt(ss/D + eps);
+// squares in fp32 (flags bit 0: rounded to bf16), summed in fp64 (lane, wave
+// tree, then waves in order through LDS) and rounded once to fp32. A square
+// of a bf16 value has at most 16 significant bits, so the fp64 sum is exact or
+// off by a few fp64 ulps; its fp32 rounding can then depend on the reduction
+// order only when the exact sum lies that close to the midpoint of two fp32
+// values (one fp32 ulp is 2^29 fp64 ulps). inv = correctly rounded
+// 1/sqrt(ss/D + eps);
 // out = bf16((x * inv) * gamma); MXFP8 of the bf16 output.
 template <int CPL, bool MX, bool FULL>
 __device__ __forceinline__ void norm_out(const u32x4 (&x)[CPL], const u32x4 (&gm)[CPL],
-                                         float* wave_ss, int t, int D, int nch, int base,
+                                         double* wave_ss, int t, int D, int nch, int base,
                                          int lane, int wave, int nwaves, float eps,
                                          uint32_t flags, uint16_t* __restrict__ out,
                                          uint8_t* __restrict__ codes,
                                          uint8_t* __restrict__ scales) {
   const int cols = D >> 5;
-  float ss = 0.0f;
+  double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = base + j * kWave;
@@ -184,16 +189,16 @@ __device__ __forceinline__ void norm_out(const u32x4 (&x)[CPL], const u32x4 (&gm
       for (int i = 0; i < 8; ++i) {
         float sq = hf[i] * hf[i];
         if (flags & 1u) sq = bf16_lo(pack_bf16x2(sq, 0.0f));
-        ss = ss + sq;
+        ss = ss + static_cast<double>(sq);
       }
     }
   }
-  ss = wave_sum(ss);
+  ss = wave_sum_f64(ss);
   if (lane == 0) wave_ss[wave] = ss;
   __syncthreads();
-  float total = 0.0f;
+  double total = 0.0;
   for (int v = 0; v < nwaves; ++v) total = total + wave_ss[v];
-  const float mean = total / static_cast<float>(D);
+  const float mean = static_cast<float>(total) / static_cast<float>(D);
   const float inv = static_cast<float>(1.0 / sqrt(static_cast<double>(mean + eps)));
 
   uint16_t* orow = out + static_cast<int64_t>(t) * D;
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_kernel(
     const int* __restrict__ rop, const uint16_t* __restrict__ shared,
     const uint16_t* __restrict__ gamma, float eps, int T, int K, int D, uint32_t flags,
     uint16_t* __restrict__ out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ float wave_ss[kMaxWaves];
+  __shared__ double wave_ss[kMaxWaves];
 
   const int t = blockIdx.x;
   if (t >= T) {
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kMaxWaves* kWave) void finalize_mhc_kernel(
     const uint16_t* __restrict__ gamma, float eps, int T, int K, int D, uint32_t flags,
     uint16_t* __restrict__ residual_out, uint16_t* __restrict__ out,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  __shared__ float wave_ss[kMaxWaves];
+  __shared__ double wave_ss[kMaxWaves];
 
   const int t = blockIdx.x;
   if (t >= T) {

@@ -572,12 +572,13 @@ int orc_mxfp8_swizzle(const uint8_t *rowmajor /* [M, cols] */, int M, int cols,
  *  [MH] AllReduceMHC.finalize folds the shared-expert output into the same
  *       sum; reading: the shared value is added after the routed sum and the
  *       total is rounded once to bf16 (h).
- *  [MH] _LamportMHCDeviceKernel RMSNorm: fp32 sum of h^2 over the row;
- *       inv = rsqrt(sum / D + eps); output bf16((h * inv) * gamma).
- *       With flags bit 0, each square is the bf16-rounded bf16 product, as in
- *       the [K3] default (non fp32_internal) mode.
- *       The row sum is sequential in d; inv is the correctly rounded
- *       reciprocal square root (computed in double and rounded once).
+ *  [MH] _LamportMHCDeviceKernel RMSNorm: sum of h^2 over the row (fp32
+ *       squares; reading: the sum rounded once to fp32 from its exact value,
+ *       see rmsnorm_row); inv = rsqrt(sum / D + eps); output
+ *       bf16((h * inv) * gamma). With flags bit 0, each square is the
+ *       bf16-rounded bf16 product, as in the [K3] default (non fp32_internal)
+ *       mode. inv is the correctly rounded reciprocal square root (computed
+ *       in double and rounded once).
  *  [MH] MXFP8 of the bf16 output, per 32-element block: UE8M0 byte from the
  *       block max (orc_ue8m0_from_amax); codes = E4M3(o * 2^(127 - byte)).
  *       Scales are stored row-major, [T, D/32]; with flags bit 2 in the
@@ -585,20 +586,26 @@ int orc_mxfp8_swizzle(const uint8_t *rowmajor /* [M, cols] */, int M, int cols,
  *  flags bit 1: the weights are bf16 (uint16 bits), widened exactly.
  * mx_codes and mx_scales are both NULL or both set; shared may be NULL. */
 /* RMSNorm of one bf16 row ([MH] _LamportMHCDeviceKernel; [K3] routed role):
- * ss = sum of x^2 in fp32, sequential in d (flags bit 0: each square rounded
- * to bf16 first); inv = correctly rounded 1/sqrt(ss/D + eps); out =
- * bf16((x * inv) * gamma). */
+ * each square x^2 in fp32 (flags bit 0: rounded to bf16); their sum taken in
+ * double, sequential in d, and rounded once to fp32 (ss); inv = correctly
+ * rounded 1/sqrt(ss/D + eps); out = bf16((x * inv) * gamma).
+ * Reading: the pages sum the squares in fp32 in an order set by their thread
+ * layout, so the fp32 value depends on that order; the value every order
+ * approximates is the exact sum. A square of a bf16 value has at most 16
+ * significant bits, so the double sum is exact or off by a few double ulps,
+ * and its rounding to fp32 is the fp32 nearest the exact sum unless the exact
+ * sum lies that close to the midpoint of two fp32 values. */
 static void rmsnorm_row(const uint16_t *x, const uint16_t *gamma, float eps, int D,
                         unsigned flags, uint16_t *out)
 {
-    float ss = 0.0f;
+    double ss = 0.0;
     for (int d = 0; d < D; ++d) {
         float v = orc_bf16_to_f32(x[d]);
         float sq = v * v;
         if (flags & 1u) sq = orc_bf16_to_f32(orc_f32_to_bf16(sq));
-        ss = ss + sq;
+        ss = ss + (double)sq;
     }
-    float mean = ss / (float)D;
+    float mean = (float)ss / (float)D;
     float arg = mean + eps;
     float inv = (float)(1.0 / sqrt((double)arg));
     for (int d = 0; d < D; ++d) {

@@ -3,12 +3,13 @@ same seeded inputs.
 
 Bar: integer outputs (shuffle) and the bf16 gather are bit-exact; the combine
 is designed bit-exact (same fp32 addition order as the oracle); the finalize
-output is within |gpu - ref| <= 2e-2 + 1e-2 * |ref| (its row sum of squares is
-a tree reduction, the oracle's is sequential); FP8 codes may differ by at most
-one code on at most 0.1 % of elements (they are expected to be exact); MXFP8
-codes and scales are exact when the oracle quantises the GPU's own bf16
-output (the split check), so quantiser parity is separate from RMSNorm
-rounding.
+output must be within |gpu - ref| <= 2e-2 + 1e-2 * |ref| and is designed
+bit-exact too (both sides take the row's sum of squares in fp64 and round it
+once to fp32, so the kernel's tree and the oracle's sequence agree); FP8 and
+MXFP8 codes may differ by at most one code on at most 0.1 % of elements
+(expected exact). MXFP8 is checked twice: end to end against the oracle's
+own codes and scales, and split (the oracle quantising the GPU's own bf16
+output), which separates quantiser parity from RMSNorm rounding.
 
 Sizes: small shapes spanning several slices and a ragged tail, the edge cases
 (empty, single token, K = E, valid count 0 / T / beyond T, ties, strided
@@ -447,11 +448,31 @@ def test_combine_split_shuffling_bit_exact(dev, case):
 
 # ---------------------------------------------------------------- finalize
 def _close(got_bits, want_bits, what):
+    """The finalize bar (|gpu - ref| <= 2e-2 + 1e-2 |ref|), then bit-exactness,
+    which the fp64 sum of squares on both sides is designed to give."""
     g = orc.bf16_to_f32(got_bits).astype(np.float64)
     r = orc.bf16_to_f32(want_bits).astype(np.float64)
     err = np.abs(g - r)
     tol = 2e-2 + 1e-2 * np.abs(r)
     assert np.all(err <= tol), f"{what}: max abs {err.max():.3e}"
+    ndiff = int(np.count_nonzero(got_bits != want_bits))
+    if ndiff:
+        say(what, f"differs from the oracle in {ndiff} of {got_bits.size} elements, "
+                  f"max abs {err.max():.3e}")
+    assert ndiff == 0, f"{what}: {ndiff} elements differ from the oracle (within tolerance)"
+
+
+def assert_mx_end_to_end(codes, scales, want_codes, want_scales, what):
+    """MXFP8 codes and UE8M0 scales against the oracle's own end-to-end output:
+    codes at most one code apart on at most 0.1 % of elements; reported, then
+    required exact (as designed)."""
+    d = np.abs(ordinal(codes) - ordinal(want_codes))
+    sd = np.abs(scales.astype(np.int32) - want_scales.astype(np.int32))
+    say(what, f"end to end: codes differ {np.mean(d > 0):.2e} (max distance "
+              f"{d.max(initial=0)}), scale bytes differ {np.mean(sd > 0):.2e}")
+    assert_fp8_close(codes, want_codes, what)
+    assert np.array_equal(scales, want_scales), f"{what}: scale bytes differ"
+    assert np.array_equal(codes, want_codes), f"{what}: codes differ"
 
 
 FIN_CASES = [
@@ -478,16 +499,17 @@ def test_finalize_rmsnorm(dev, case):
     shared = fi.shared if with_shared else None
     say("finalize", name, T, D, K, flags, mx)
     want = orc.finalize_rmsnorm(fi.y, fi.w, fi.row_of_pair, shared, fi.gamma, fi.eps,
-                                flags=flags, mxfp8=False)
+                                flags=flags, mxfp8=mx)
     res = ops.moe_finalize_rmsnorm(bf_dev(fi.y, dev), torch.from_numpy(fi.w).to(dev),
                                    i32_dev(fi.row_of_pair, dev),
                                    None if shared is None else bf_dev(shared, dev),
                                    bf_dev(fi.gamma, dev), fi.eps, flags=flags, mxfp8=mx)
     out = res[0] if mx else res
     got = bits_host(out)
-    _close(got, want, name)
+    _close(got, want[0] if mx else want, name)
     if mx:
         codes, scales = res[1].cpu().numpy(), res[2].cpu().numpy()
+        assert_mx_end_to_end(codes, scales, want[1], want[2], name)
         oc, os_ = orc.mxfp8_quantize(got)        # the split check
         assert np.array_equal(scales, os_)
         assert_fp8_close(codes, oc, "mxfp8")
@@ -510,8 +532,9 @@ def test_finalize_variants(dev, case):
     flags = (2 if bfw else 0)
     w = W.to_bf16_bits(fi.w) if bfw else fi.w
     say("finalize variant", name, T, D, K, bfw, swz)
-    want = orc.finalize_rmsnorm(fi.y, w, fi.row_of_pair, fi.shared, fi.gamma, fi.eps,
-                                flags=flags)
+    want, wcodes, wscales = orc.finalize_rmsnorm(
+        fi.y, w, fi.row_of_pair, fi.shared, fi.gamma, fi.eps,
+        flags=flags | (4 if swz else 0), mxfp8=True)
     wd = bf_dev(w, dev) if bfw else torch.from_numpy(w).to(dev)
     out, codes, scales = ops.moe_finalize_rmsnorm(
         bf_dev(fi.y, dev), wd, i32_dev(fi.row_of_pair, dev), bf_dev(fi.shared, dev),
@@ -519,6 +542,7 @@ def test_finalize_variants(dev, case):
         scale_layout="swizzled" if swz else "rowmajor")
     got = bits_host(out)
     _close(got, want, name)
+    assert_mx_end_to_end(codes.cpu().numpy(), scales.cpu().numpy(), wcodes, wscales, name)
     oc, rm = orc.mxfp8_quantize(got)            # split check on the GPU's own output
     assert np.array_equal(codes.cpu().numpy(), oc)
     want_scales = orc.mxfp8_swizzle(rm) if swz else rm
@@ -552,7 +576,8 @@ def test_finalize_mhc(dev, case):
     pre = None if mode == "res" else m.pre
     say("finalize mhc", name, T, D, K, hc, mode, swz, flags)
     want = orc.finalize_mhc(fi.y, w, fi.row_of_pair, fi.shared, m.residual, m.post, m.comb,
-                            pre, fi.gamma if pre is not None else None, fi.eps, flags=flags)
+                            pre, fi.gamma if pre is not None else None, fi.eps,
+                            flags=flags | (4 if (mx and swz) else 0), mxfp8=mx)
     wd = bf_dev(w, dev) if bfw else torch.from_numpy(w).to(dev)
     f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
     res = ops.moe_finalize_mhc(
@@ -568,6 +593,7 @@ def test_finalize_mhc(dev, case):
     got = bits_host(res[1])
     _close(got, want[1], name)
     if mx:
+        assert_mx_end_to_end(res[2].cpu().numpy(), res[3].cpu().numpy(), want[2], want[3], name)
         oc, rm = orc.mxfp8_quantize(got)        # split check on the GPU's own output
         assert np.array_equal(res[2].cpu().numpy(), oc)
         assert np.array_equal(res[3].cpu().numpy(), orc.mxfp8_swizzle(rm) if swz else rm)
@@ -773,8 +799,12 @@ def test_prefill_finalize_full_size(dev):
         bf_dev(fi.y, dev), torch.from_numpy(fi.w).to(dev), i32_dev(fi.row_of_pair, dev),
         bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev), fi.eps, mxfp8=True)
     got = bits_host(out)
-    want = orc.finalize_rmsnorm(fi.y, fi.w, fi.row_of_pair, fi.shared, fi.gamma, fi.eps)
+    want, wcodes, wscales = orc.finalize_rmsnorm(fi.y, fi.w, fi.row_of_pair, fi.shared,
+                                                 fi.gamma, fi.eps, mxfp8=True)
     _close(got, want, "prefill")
+    # MXFP8 end to end: the GPU's codes and scales against the oracle's own
+    assert_mx_end_to_end(codes.cpu().numpy(), scales.cpu().numpy(), wcodes, wscales,
+                         "prefill mxfp8")
     oc, os_ = orc.mxfp8_quantize(got)
     assert np.array_equal(scales.cpu().numpy(), os_)
     assert_fp8_close(codes.cpu().numpy(), oc, "prefill mxfp8")
@@ -792,8 +822,11 @@ def test_prefill_swizzled_finalize_full_size(dev):
         bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev), fi.eps, mxfp8=True,
         scale_layout="swizzled")
     got = bits_host(out)
-    want = orc.finalize_rmsnorm(fi.y, wb, fi.row_of_pair, fi.shared, fi.gamma, fi.eps, flags=2)
+    want, wcodes, wscales = orc.finalize_rmsnorm(fi.y, wb, fi.row_of_pair, fi.shared, fi.gamma,
+                                                 fi.eps, flags=2 | 4, mxfp8=True)
     _close(got, want, "prefill-swizzled")
+    assert_mx_end_to_end(codes.cpu().numpy(), scales.cpu().numpy(), wcodes, wscales,
+                         "prefill-swizzled mxfp8")
     oc, os_ = orc.mxfp8_quantize(got)
     assert np.array_equal(scales.cpu().numpy(), orc.mxfp8_swizzle(os_))
     assert_fp8_close(codes.cpu().numpy(), oc, "prefill-swizzled mxfp8")
@@ -812,10 +845,12 @@ def test_mhc_finalize_full_size(dev):
         bf_dev(m.residual, dev), f32(m.post), f32(m.comb), f32(m.pre), bf_dev(fi.gamma, dev),
         fi.eps, mxfp8=True, scale_layout="swizzled")
     want = orc.finalize_mhc(fi.y, fi.w, fi.row_of_pair, fi.shared, m.residual, m.post, m.comb,
-                            m.pre, fi.gamma, fi.eps)
+                            m.pre, fi.gamma, fi.eps, flags=4, mxfp8=True)
     _close(bits_host(res_out), want[0], "mhc residual_out")
     got = bits_host(out)
     _close(got, want[1], "mhc out")
+    assert_mx_end_to_end(codes.cpu().numpy(), scales.cpu().numpy(), want[2], want[3],
+                         "mhc mxfp8")
     oc, rm = orc.mxfp8_quantize(got)
     assert np.array_equal(scales.cpu().numpy(), orc.mxfp8_swizzle(rm))
     assert_fp8_close(codes.cpu().numpy(), oc, "mhc mxfp8")
@@ -897,35 +932,53 @@ def test_shuffling_workload_full_size(dev):
 
 def test_c_abi_consumer(dev, tmp_path):
     """A plain C program (tests/c_abi_consumer.c: gcc, the header and the HIP
-    runtime only) runs shuffle -> gather by token -> scatter by token on the
-    tiny workload, as a child process; its outputs equal the oracle's."""
+    runtime only) runs moe_shuffle, moe_gather_scale (token_indices) and its
+    by-token form, moe_gather_scale_quant, moe_scatter_add (token_indices) and
+    its by-token form, and moe_finalize_rmsnorm with MXFP8 on the tiny
+    workload, as a child process; every output equals the oracle's."""
     import subprocess
     exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_consumer")
     assert os.path.exists(exe), "build the library first: it also builds the C consumer"
     wl = W.WORKLOADS["tiny"]
     T, D, E, K = wl.T, wl.D, wl.E, wl.K
+    a = T * K
     inp = W.dispatch_inputs(wl, out0="normal")
+    fi = W.finalize_inputs(W.WORKLOADS["decode"], T=T, D=D, K=K)
     fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(fin, "wb") as f:
         f.write(np.array([T, E, K, D], np.int32).tobytes())
-        for arr in (inp.scores, inp.x, inp.y, inp.out0):
+        for arr in (inp.scores, inp.x, inp.y, inp.out0, fi.w, fi.shared, fi.gamma,
+                    np.array([fi.eps], np.float32)):
             f.write(np.ascontiguousarray(arr).tobytes())
     say("c consumer", T, D, E, K)
     r = subprocess.run([exe, str(fin), str(fout)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     buf = np.fromfile(fout, dtype=np.uint8)
-    a = T * K
-    sizes = [(E + 1) * 4, a * 4, a * 4, a * 4, a * D * 2, T * D * 2]
+    sizes = [(E + 1) * 4, a * 4, a * 4, a * 4, a * D * 2, a * D * 2, a * D, a * 4,
+             T * D * 2, T * D * 2, T * D * 2, T * D, T * D // 32]
     assert buf.size == sum(sizes)
     parts = np.split(buf, np.cumsum(sizes)[:-1])
     gc, gei, gti, grop = (p.view(np.int32) for p in parts[:4])
-    rows, out = parts[4].view(np.uint16).reshape(a, D), parts[5].view(np.uint16).reshape(T, D)
+    rows, rows_g = (p.view(np.uint16).reshape(a, D) for p in parts[4:6])
+    codes, qscale = parts[6].reshape(a, D), parts[7].view(np.float32)
+    out, out_g, fo = (p.view(np.uint16).reshape(T, D) for p in parts[8:11])
+    mc, ms = parts[11].reshape(T, D), parts[12].reshape(T, D // 32)
     counts, ei, ti, rop = orc.shuffle(inp.scores, K)
     V = int(counts[E])
     assert np.array_equal(gc, counts) and np.array_equal(gei, ei) and np.array_equal(gti, ti)
     assert np.array_equal(grop, rop.ravel())
-    assert np.array_equal(rows[:V], orc.gather_scale(inp.x, ti, ei, inp.scores, V)[:V])
-    assert np.array_equal(out, orc.scatter_add(inp.out0.copy(), inp.y, ti, V))
+    want_rows = orc.gather_scale(inp.x, ti, ei, inp.scores, V)
+    assert np.array_equal(rows[:V], want_rows[:V])
+    assert np.array_equal(rows_g[:V], want_rows[:V])
+    wq, ws = orc.gather_scale_quant(inp.x, ti, ei, inp.scores, None, V)
+    assert np.array_equal(codes[:V], wq[:V])
+    assert np.array_equal(qscale[:V].view(np.uint32), ws[:V].view(np.uint32))
+    want_out = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+    assert np.array_equal(out, want_out) and np.array_equal(out_g, want_out)
+    wo, wc, wsc = orc.finalize_rmsnorm(inp.y, fi.w, rop.reshape(T, K), fi.shared, fi.gamma,
+                                       fi.eps, mxfp8=True)
+    _close(fo, wo, "c consumer finalize")
+    assert_mx_end_to_end(mc, ms, wc, wsc, "c consumer mxfp8")
 
 
 @pytest.mark.parametrize("seed", range(32))

@@ -7,11 +7,17 @@ bf16 rounding; untouched tokens keep their bits.
 finalize: special cases that reduce to torch.nn.functional.rms_norm; an fp64
 evaluation of the weighted sum; the constant-row closed form; exact invariance
 under power-of-two scaling (eps = 0); the bf16-square mode against torch's
-bf16 multiply.
+bf16 multiply; the RMSNorm bit for bit against exact rational arithmetic (the
+sum of squares rounded once to fp32 from its exact value, the correctly
+rounded inverse square root), on rows where a plain fp32 running sum rounds
+differently.
 MXFP8: the scale byte is the round-up power of two of each block's max; codes
 are torch's E4M3 cast of the scaled block; re-quantising the dequantised block
 is the identity.
 """
+from decimal import Decimal, localcontext
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -173,6 +179,79 @@ def test_finalize_bf16_square_mode(orc):
     inv = torch.rsqrt(sq.sum(1, keepdim=True) / 512 + fi.eps)
     ref = ((h.float() * inv) * _bf(fi.gamma).float()).to(torch.bfloat16).float()
     assert torch.allclose(got, ref, rtol=2.0 ** -7, atol=1e-6)
+
+
+def _f32_nearest(q):
+    """The binary32 value nearest the positive rational q, ties to even (q in
+    the normal range)."""
+    q = Fraction(q)
+    assert q > 0
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    scaled = q / Fraction(2) ** (e - 23)          # in [2^23, 2^24)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return np.float32(m * 2.0 ** (e - 23))        # m <= 2^24: exact
+
+
+def _rmsnorm_exact(h_bits, gamma_bits, eps, bf16_squares=False):
+    """RMSNorm of bf16 rows from exact arithmetic: squares in fp32 (exact for
+    bf16 values; rounded to bf16 in the bf16-square mode), their exact
+    rational sum rounded once to fp32, mean and mean + eps in fp32, inverse
+    square root rounded once from a 60-digit decimal value, then
+    bf16((h * inv) * gamma) in fp32 with torch's bf16 cast."""
+    h = _bf(h_bits).float().numpy()
+    g = _bf(gamma_bits).float().numpy()
+    T, D = h.shape
+    out = np.empty_like(h)
+    for t in range(T):
+        sq = (h[t] * h[t]).astype(np.float32)
+        if bf16_squares:
+            sq = _bf(W.to_bf16_bits(sq)).float().numpy()
+        ss = _f32_nearest(sum(Fraction(float(v)) for v in sq))
+        arg = np.float32(np.float32(ss / np.float32(D)) + np.float32(eps))
+        with localcontext() as ctx:
+            ctx.prec = 60
+            inv = _f32_nearest(Fraction(Decimal(1) / Decimal(float(arg)).sqrt()))
+        out[t] = (h[t] * inv).astype(np.float32) * g
+    return W.to_bf16_bits(out.astype(np.float32))
+
+
+def _rmsnorm_fp32_running_sum(h_bits, gamma_bits, eps):
+    """The same with the squares added one by one in fp32 (the reading the
+    exact-sum pin must tell apart)."""
+    h = _bf(h_bits).float().numpy()
+    g = _bf(gamma_bits).float().numpy()
+    D = h.shape[1]
+    ss = np.add.accumulate((h * h).astype(np.float32), axis=1, dtype=np.float32)[:, -1]
+    arg = (ss / np.float32(D) + np.float32(eps)).astype(np.float32)
+    inv = (1.0 / np.sqrt(arg.astype(np.float64))).astype(np.float32)
+    return W.to_bf16_bits(((h * inv[:, None]).astype(np.float32) * g).astype(np.float32))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+def test_finalize_rmsnorm_exact_sum_of_squares(orc, flags):
+    g = np.random.default_rng(11)
+    T, D = 6, 4096
+    y = g.standard_normal((T, D)).astype(np.float32)
+    y[:3, 0] = 4096.0          # a large first square: a running fp32 sum drops the rest
+    y[3, :] *= np.float32(1e-3)
+    y = W.to_bf16_bits(y)
+    gamma = W.to_bf16_bits(g.uniform(0.5, 1.5, D).astype(np.float32))
+    rop = np.arange(T, dtype=np.int32).reshape(T, 1)
+    w = np.ones((T, 1), np.float32)     # h = y exactly (fma(1, y, 0), one bf16 rounding)
+    got = orc.finalize_rmsnorm(y, w, rop, None, gamma, 1e-6, flags=flags)
+    want = _rmsnorm_exact(y, gamma, 1e-6, bf16_squares=bool(flags))
+    assert np.array_equal(got, want)
+    if not flags:
+        # the crafted rows tell the two readings apart
+        running = _rmsnorm_fp32_running_sum(y, gamma, 1e-6)
+        assert not np.array_equal(running[:3], want[:3])
 
 
 # ---------------------------------------------------------------- MXFP8
