@@ -6,6 +6,9 @@ A step is one pass of the path over one batch of synthetic input, already
 resident in HBM:
   zipf      (default; T=8192, D=7168, E=256, K=8, valid_token_count=6000)
             moe_shuffle -> moe_gather_scale_by_token -> moe_scatter_add_by_token
+  zipf-general  the same step through the entry points that take
+            token_indices (the pages' gather/scatter arguments): moe_shuffle ->
+            moe_gather_scale (with a workspace) -> moe_scatter_add
   quant     (T=4096, D=5120, E=16, K=1)
             moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
   prefill   (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
@@ -25,14 +28,17 @@ of the step instead; a graph launch costs more than a few kernel launches here.
 
 1. W untimed steps, then exactly K timed steps between two device
    synchronisations (wall clock, and a HIP event pair around the region): the
-   warm steps behind `value`. Then K steps one at a time, each between an
-   event pair with the host waiting for it: p10 / p50 / p90 of an isolated
+   warm steps, reported under "warm" (the previous step's data still in L2
+   and the 256 MB Infinity Cache). Then K steps one at a time, each between
+   an event pair with the host waiting for it: p10 / p50 / p90 of an isolated
    step's latency, launch included ("step_us_isolated").
-2. K cold steps, each after a flush of L2 and the 256 MB Infinity Cache -- a
-   1 GiB read (clean eviction) or a 1 GiB write (whose dirty lines the step
-   then writes back) -- device time with the flushes' own time subtracted,
-   reported under "cold" with each stage alone after a read flush
-   (--no-cold skips them, for profiling runs).
+2. K cold steps, each after a flush of L2 and the Infinity Cache -- a 1 GiB
+   read (clean eviction) or a 1 GiB write (whose dirty lines the step then
+   writes back) -- between two device synchronisations, device time with the
+   flushes' own time (K flushes alone, timed the same way) subtracted; each
+   stage alone after a read flush too. The steps after a read flush are the
+   headline: `value`, `ms_per_step` and `hbm_frac` (--no-cold skips the cold
+   steps, for profiling runs; the headline is then the warm steps).
 3. Each stage alone: K launches captured back to back in one HIP graph,
    replayed once between one HIP event pair on the stream the kernels run on:
    each stage's average duration per launch, the kernels' own time.
@@ -65,8 +71,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-WORKLOAD_CHOICES = ["zipf", "quant", "prefill", "decode", "prefill-swizzled", "mhc", "padded",
-                    "shuffling"]
+WORKLOAD_CHOICES = ["zipf", "zipf-general", "quant", "prefill", "decode", "prefill-swizzled",
+                    "mhc", "padded", "shuffling"]
 DISPATCH_METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1xMI355X"
 
 
@@ -149,19 +155,21 @@ def stage_ms(torch, fn, reps):
 # Per launch: unique inputs read once, outputs written once, valid rows only
 # (rows past the valid count are neither read nor written). bf16 rows are 2*D
 # bytes; indices, counts, scores and fp32 weights 4 bytes.
-def dispatch_bytes(T, D, E, K, vtc, quant):
+def dispatch_bytes(T, D, E, K, vtc, quant, general=False):
     """shuffle: scores + token/expert indices and row_of_pair + counts;
     gather: x once per routed token (bf16) or per row (FP8 rowwise, codes and
     scales out) + the routed rows + the indices and scores it reads;
     scatter: the routed rows + each routed token's row read and written +
-    row_of_pair."""
+    row_of_pair. The general entry points read the valid rows' token indices
+    instead of row_of_pair (V instead of T*K index words)."""
     a, V, row_b = T * K, vtc * K, D * 2
     shuffle = T * E * 4 + 3 * a * 4 + (E + 1) * 4
+    idx = V * 4 if general else T * K * 4
     if quant:
         gather = V * row_b + V * D + V * 4 + 2 * V * 4 + V * 4
     else:
-        gather = vtc * row_b + V * row_b + T * K * 4 + V * 4 + V * 4
-    scatter = V * row_b + 2 * vtc * row_b + T * K * 4
+        gather = vtc * row_b + V * row_b + idx + V * 4 + V * 4
+    scatter = V * row_b + 2 * vtc * row_b + idx
     return {"shuffle": shuffle, "gather": gather, "scatter": scatter}
 
 
@@ -197,7 +205,10 @@ def shuffling_bytes(rows, D, EP, EG):
 
 
 # ------------------------------------------------------------------ workloads
-def setup_dispatch(ctx, wl, with_cpu):
+def setup_dispatch(ctx, wl, with_cpu, general=False):
+    """general: gather and scatter through the entry points that take
+    token_indices (moe_gather_scale with a workspace, moe_scatter_add)
+    instead of the shuffle's inverse map."""
     torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
     inp = W.dispatch_inputs(wl)
     T, D, E, K = wl.T, wl.D, wl.E, wl.K
@@ -225,6 +236,11 @@ def setup_dispatch(ctx, wl, with_cpu):
 
     counts, ei, ti, rop = shuf_out
     vr = counts[E:]
+    if general:
+        ws_g = torch.empty(max(1, ctx.lib.moe_gather_scale_workspace_bytes(T, a)),
+                           dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(max(1, ctx.lib.moe_scatter_add_workspace_bytes(T, a)),
+                           dtype=torch.uint8, device=dev)
 
     def shuffle():
         ops.moe_shuffle(scores, K, vtc_d, workspace=ws, out=shuf_out)
@@ -232,22 +248,30 @@ def setup_dispatch(ctx, wl, with_cpu):
     def gather():
         if quant:
             ops.moe_gather_scale_quant(x, ti, ei, scores, ub, vr, rows, rscale)
+        elif general:
+            ops.moe_gather_scale(x, ti, ei, scores, vr, rows, workspace=ws_g)
         else:
             ops.moe_gather_scale_by_token(x, rop, ei, scores, vr, rows)
 
     def scatter():
-        ops.moe_scatter_add_by_token(out, y, rop, vr)
+        if general:
+            ops.moe_scatter_add(out, y, ti, vr, workspace=ws_s)
+        else:
+            ops.moe_scatter_add_by_token(out, y, rop, vr)
 
+    name = wl.name + ("-general" if general else "")
+    stage_names = (("gather_scale_quant", "scatter_add_by_token") if quant else
+                   ("gather_scale (token_indices, workspace)", "scatter_add (token_indices)")
+                   if general else ("gather_scale_by_token", "scatter_add_by_token"))
     return SimpleNamespace(
         stages={"shuffle": shuffle, "gather": gather, "scatter": scatter},
-        stage_bytes=dispatch_bytes(T, D, E, K, vtc, quant),
+        stage_bytes=dispatch_bytes(T, D, E, K, vtc, quant, general),
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
-        config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} valid_token_count={vtc}",
+        config={"workload": f"{name}: T={T} D={D} E={E} K={K} valid_token_count={vtc}",
                 "tokens": T, "hidden": D, "experts": E, "top_k": K,
                 "valid_token_count": vtc, "routed_rows": V,
-                "stages": "shuffle -> " + ("gather_scale_quant" if quant else
-                                           "gather_scale_by_token") +
-                " -> scatter_add_by_token"},
+                "stages": "shuffle -> " + " -> ".join(stage_names)},
+        traffic_key=name,
         dtype="bf16" if not quant else "bf16->fp8e4m3",
         kernel_src={"shuffle": ["shuffle.hip"], "gather": ["gather.hip"],
                     "scatter": ["combine.hip"]},
@@ -437,6 +461,8 @@ def main():
     name = args.workload
     if name in ("zipf", "quant"):
         s = setup_dispatch(ctx, W.WORKLOADS[name], with_cpu)
+    elif name == "zipf-general":
+        s = setup_dispatch(ctx, W.WORKLOADS["zipf"], with_cpu, general=True)
     elif name in ("prefill", "decode"):
         s = setup_finalize(ctx, W.WORKLOADS[name], with_cpu)
     elif name == "prefill-swizzled":
@@ -543,11 +569,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    ms_step = elapsed * 1e3 / steps
+    warm_ms = elapsed * 1e3 / steps
+    # the headline: the steps after a read flush (inputs in HBM, not in the
+    # caches); the warm steps when the cold ones were skipped
+    ms_step = cold["read"] if "read" in cold else warm_ms
     total_bytes = sum(s.stage_bytes.values())
     dom = max(names, key=lambda n: st_ms[n])
     achieved = s.stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom, s.kernel_src[dom], getattr(s, "traffic_key", name))
+
+    def rates(ms):
+        return {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
+                "hbm_gbps": total_bytes / (ms * 1e-3) / 1e9,
+                "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
     line = {
         "metric": s.metric,
@@ -557,8 +591,13 @@ def main():
         "steps": steps,
         "warmup": warm,
         "ms_per_step": ms_step,
-        "ms_per_step_device": region_ms / steps,
-        "step_us_isolated": {"p10": round(p10, 2), "p50": round(p50, 2), "p90": round(p90, 2)},
+        "headline": ("cold: K steps, each after a 1 GiB read that evicts L2 and the "
+                     "Infinity Cache, device time with the K reads' own time subtracted"
+                     if "read" in cold else
+                     "warm: K steps back to back (cold steps skipped)"),
+        "warm": {**rates(warm_ms), "ms_per_step_device": region_ms / steps,
+                 "step_us_isolated": {"p10": round(p10, 2), "p50": round(p50, 2),
+                                      "p90": round(p90, 2)}},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -569,9 +608,7 @@ def main():
                    (", checked op calls" if args.checked else
                     ", prepared calls (arguments checked once)")},
         "cold": None if args.no_cold else {
-            **{kind: {"ms_per_step": ms, "value": s.units_per_step / (ms * 1e-3),
-                      "hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-               for kind, ms in cold.items()},
+            **{kind: rates(ms) for kind, ms in cold.items()},
             "stage_us_after_read": {n: round(cold_stage[n] * 1e3, 2) for n in names},
             "roofline_frac_after_read":
                 s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
@@ -584,7 +621,10 @@ def main():
                        for n in names},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic},
+                     "bytes_per_launch": s.stage_bytes[dom], "traffic": traffic,
+                     "duration": "the kernel's average launch duration, launches back to "
+                                 "back (what the rocprofv3 kernel trace shows); after a "
+                                 "read flush: cold.roofline_frac_after_read"},
         "cpu_baseline": s.cpu,
     }
     if name == "decode" and not args.no_sweep:

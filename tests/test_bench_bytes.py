@@ -23,6 +23,17 @@ def test_zipf_dispatch_bytes():
     _close(sum(b.values()), 1644.4)
 
 
+def test_zipf_general_dispatch_bytes():
+    # the entry points that take token_indices read the 48000 valid rows' token
+    # indices (0.19 MB) where the by-token ones read row_of_pair (8192*8 words)
+    b = bench.dispatch_bytes(8192, 7168, 256, 8, 6000, quant=False, general=True)
+    byt = bench.dispatch_bytes(8192, 7168, 256, 8, 6000, quant=False)
+    assert b["shuffle"] == byt["shuffle"]
+    assert b["gather"] == byt["gather"] - 8192 * 8 * 4 + 48000 * 4
+    assert b["scatter"] == byt["scatter"] - 8192 * 8 * 4 + 48000 * 4
+    _close(b["scatter"], 688.128 + 2 * 86.016 + 0.192)
+
+
 def test_quant_dispatch_bytes():
     # T=4096, D=5120, E=16, K=1: one row per token, FP8 codes 1 byte per element
     b = bench.dispatch_bytes(4096, 5120, 16, 1, 4096, quant=True)
