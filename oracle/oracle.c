@@ -24,9 +24,12 @@
  *
  * Parity status: every function here is pinned by a CPU test against
  * something other than itself (brute force, torch library casts/routines,
- * closed forms, invariants). The one unpinned value is the scale of an
- * all-zero row in gather_scale_quant, which depends on an EPS constant the
- * pages do not print ("parity unpinned" for that value only).
+ * exact rational arithmetic, closed forms, invariants). Parity unpinned, as
+ * readings of steps the pages call but do not print: the scale of an
+ * all-zero row in gather_scale_quant (an EPS constant), the round-up
+ * direction of the UE8M0 scale, the 128x4 tile order of the swizzled
+ * scales, and the EP re-sort layout; each is pinned against a restatement
+ * of its reading, not against the pages.
  */
 #include <math.h>
 #include <stdint.h>
