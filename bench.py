@@ -652,9 +652,23 @@ def decode_sweep(ctx, wl, steps, warm, checked):
         step_us = (time.perf_counter() - t0) * 1e6 / steps
         k_ms = stage_ms(torch, fn, steps)
         b = sub.stage_bytes["finalize"]
-        out.append({"tokens": T, "step_us": round(step_us, 2), "kernel_us": round(k_ms * 1e3, 2),
-                    "tokens_per_s": T / (step_us * 1e-6), "bytes": b,
-                    "kernel_gbps": round(b / (k_ms * 1e-3) / 1e9, 1)})
+        rec = {"tokens": T, "step_us": round(step_us, 2), "kernel_us": round(k_ms * 1e3, 2),
+               "tokens_per_s": T / (step_us * 1e-6), "bytes": b,
+               "kernel_gbps": round(b / (k_ms * 1e-3) / 1e9, 1)}
+        # floors on the same launch path and shape: an empty kernel, and two
+        # dependent 16-byte loads + a store per thread
+        for kind, key in ((0, "floor_empty"), (1, "floor_2loads")):
+            ff = ctx.ops.prepare(ctx.ops.moe_launch_floor, kind, T, wl.D, device=ctx.dev)
+            for _ in range(warm):
+                ff()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                ff()
+            torch.cuda.synchronize()
+            rec[key + "_step_us"] = round((time.perf_counter() - t0) * 1e6 / steps, 2)
+            rec[key + "_kernel_us"] = round(stage_ms(torch, ff, steps) * 1e3, 2)
+        out.append(rec)
     return out
 
 

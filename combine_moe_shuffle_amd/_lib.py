@@ -59,6 +59,8 @@ SIGNATURES = {
     "moe_finalize_mhc": (_status, [_p, _i64, _p, _p, _p, _p, _p, _p, _p, _p, _f32, _i32, _i32,
                                    _i32, _i32, _u32, _p, _p, _p, _p, _p]),
     "moe_convert_check": (_status, [_p, _i64, _p, _p, _p]),
+    "moe_launch_floor_threads": (_i32, [_i32, _i32]),
+    "moe_launch_floor": (_status, [_i32, _i32, _i32, _p, _p, _p]),
 }
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",

@@ -527,4 +527,23 @@ moe_status_t moe_convert_check(const float* in, int64_t n, moe_bf16_t* bf16_out,
                     "moe_convert_check");
 }
 
+int32_t moe_launch_floor_threads(int32_t T, int32_t D) {
+  if (T < 1 || D < 8 || D % 8 != 0 || D > kMaxFinalizeD) return 0;
+  return moe::launch_floor_threads(T, D);
+}
+
+moe_status_t moe_launch_floor(int32_t kind, int32_t T, int32_t D, const void* src, int32_t* dst,
+                              void* stream) {
+  REQUIRE(kind == 0 || kind == 1, MOE_ERR_INVALID_ARG, "kind must be 0 or 1 (got %d)", kind);
+  REQUIRE(T >= 1 && T <= (1 << 20), MOE_ERR_INVALID_ARG, "T must be in [1, 2^20] (got %d)", T);
+  REQUIRE(D >= 8 && D % 8 == 0 && D <= kMaxFinalizeD, MOE_ERR_INVALID_ARG,
+          "D must be a multiple of 8 in [8, %d] (got %d)", kMaxFinalizeD, D);
+  if (kind == 1) {
+    REQUIRE(src != nullptr && dst != nullptr, MOE_ERR_INVALID_ARG, "src and dst are required");
+    REQUIRE(aligned(src, 16) && aligned(dst, 4), MOE_ERR_INVALID_ARG, "src or dst misaligned");
+  }
+  return hip_status(moe::launch_floor(kind, T, D, src, dst, static_cast<hipStream_t>(stream)),
+                    "moe_launch_floor");
+}
+
 }  // extern "C"

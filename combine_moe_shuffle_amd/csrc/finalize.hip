@@ -178,6 +178,8 @@ __device__ __forceinline__ void norm_out(const u32x4 (&x)[CPL], const u32x4 (&gm
                                          uint8_t* __restrict__ codes,
                                          uint8_t* __restrict__ scales) {
   const int cols = D >> 5;
+  // the lane's squares summed as a tree (short dependent chains; in fp64 the
+  // order does not matter)
   double ss = 0.0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
@@ -185,12 +187,14 @@ __device__ __forceinline__ void norm_out(const u32x4 (&x)[CPL], const u32x4 (&gm
     if (FULL || c < nch) {
       float hf[8];
       unpack8(x[j], hf);
+      double d[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float sq = hf[i] * hf[i];
         if (flags & 1u) sq = bf16_lo(pack_bf16x2(sq, 0.0f));
-        ss = ss + static_cast<double>(sq);
+        d[i] = static_cast<double>(sq);
       }
+      ss = ss + (((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7])));
     }
   }
   ss = wave_sum_f64(ss);
@@ -421,22 +425,27 @@ __global__ void convert_kernel(const float* __restrict__ in, int64_t n,
 
 }  // namespace
 
+// up to 32 tokens: two chunks per lane (a 7168-wide row in 7 waves measured
+// 0.2 us faster than in 14 at 1-32 tokens: fewer waves to launch and to meet
+// at the barrier); up to 2047 tokens: one chunk per lane and up to 16 waves
+// per token (latency); more: two chunks per lane, fewer waves per token
+SliceShape finalize_launch_shape(int T, int D) {
+  const int nch = D / kChunk;
+  static const int tiny_t[] = {2, 1, 4, 8};
+  static const int small_t[] = {1, 2, 4, 8};
+  static const int large_t[] = {2, 4, 8, 1};
+  return T <= 32   ? pick_slices(nch, tiny_t, 4, kMaxWaves)
+         : T < 2048 ? pick_slices(nch, small_t, 4, kMaxWaves)
+                    : pick_slices(nch, large_t, 4, kMaxWaves);
+}
+
 hipError_t launch_finalize_rmsnorm(const uint16_t* y, int64_t rows, const void* w,
                                    const int* row_of_pair, const uint16_t* shared,
                                    const uint16_t* gamma, float eps, int T, int K, int D,
                                    uint32_t flags, uint16_t* out, uint8_t* mx_codes,
                                    uint8_t* mx_scales, hipStream_t stream) {
-  // up to 32 tokens: two chunks per lane (a 7168-wide row in 7 waves measured
-  // 0.2 us faster than in 14 at 1-32 tokens: fewer waves to launch and to meet
-  // at the barrier); up to 2047 tokens: one chunk per lane and up to 16 waves
-  // per token (latency); more: two chunks per lane, fewer waves per token
   const int nch = D / kChunk;
-  static const int tiny_t[] = {2, 1, 4, 8};
-  static const int small_t[] = {1, 2, 4, 8};
-  static const int large_t[] = {2, 4, 8, 1};
-  const SliceShape sh = T <= 32   ? pick_slices(nch, tiny_t, 4, kMaxWaves)
-                        : T < 2048 ? pick_slices(nch, small_t, 4, kMaxWaves)
-                                   : pick_slices(nch, large_t, 4, kMaxWaves);
+  const SliceShape sh = finalize_launch_shape(T, D);
   // with swizzled MXFP8 scales, one more workgroup per padding row (up to a
   // multiple of 128 rows) zeroes that row's scales
   const int pad_rows = (mx_codes && (flags & 4u)) ? (T + 127) / 128 * 128 - T : 0;

@@ -77,6 +77,11 @@ hipError_t launch_finalize_mhc(const uint16_t* y, int64_t rows, const void* w,
 hipError_t launch_convert_check(const float* in, int64_t n, uint16_t* bf16_out,
                                 uint8_t* e4m3_out, hipStream_t stream);
 
+// floor.hip: latency floors of the finalize's launch shape
+int launch_floor_threads(int T, int D);
+hipError_t launch_floor(int kind, int T, int D, const void* src, void* dst,
+                        hipStream_t stream);
+
 // Row-slice layout of the streaming kernels: a row of D bf16 values is
 // nch = D/8 chunks of 16 bytes; a wave covers one slice of 64*cpl chunks,
 // lane l taking chunks base + j*64 + l (j < cpl), so every load and store

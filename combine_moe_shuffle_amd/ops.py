@@ -574,6 +574,35 @@ def moe_convert_check(values):
     return bf, e4
 
 
+def moe_launch_floor(kind, T, D, src=None, dst=None, device=None):
+    """A kernel with the finalize's launch shape for (T, D) that does nothing
+    (kind 0) or two dependent 16-byte loads and a store per thread (kind 1):
+    latency floors to time beside the finalize. For kind 1, ``src`` is an
+    int32 tensor of 4 * n values (n = T * threads; the first of every 4 is an
+    element index) and ``dst`` an int32 tensor of n; both made when None."""
+    lib = _lib.load()
+    threads = lib.moe_launch_floor_threads(T, D)
+    if threads <= 0:
+        raise ValueError(f"no finalize launch shape for T={T}, D={D}")
+    n = T * threads
+    device = device or (src.device if src is not None else torch.device("cuda", 0))
+    if kind == 1:
+        if src is None:
+            src = torch.randint(0, n, (n, 4), dtype=torch.int32, device=device)
+        if dst is None:
+            dst = torch.empty(n, dtype=torch.int32, device=device)
+        for t, nm, numel in ((src, "src", 4 * n), (dst, "dst", n)):
+            _need(t, nm, torch.int32, device=device)
+            _contig(t, nm)
+            if t.numel() != numel:
+                raise ValueError(f"{nm} must have {numel} elements")
+    elif dst is None:
+        dst = torch.empty(1, dtype=torch.int32, device=device)  # not written
+    _call("moe_launch_floor", kind, T, D, _ptr(src if kind == 1 else None), _ptr(dst),
+          _stream(device))
+    return dst
+
+
 # The pages' names for the same operations
 gather_scale_dense_tokens = moe_gather_scale
 gather_scale_quant_dense_tokens = moe_gather_scale_quant

@@ -436,6 +436,23 @@ MOE_API moe_status_t moe_finalize_mhc(const moe_bf16_t *y_permuted, int64_t rows
 MOE_API moe_status_t moe_convert_check(const float *in, int64_t n, moe_bf16_t *bf16_out,
                                uint8_t *e4m3_out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * moe_launch_floor -- measurement aid: a kernel with moe_finalize_rmsnorm's
+ * grid and workgroup shape for (T, D), T workgroups of
+ * moe_launch_floor_threads(T, D) threads, that does
+ *   kind 0  nothing (the cost of the launch itself), or
+ *   kind 1  per thread i < n = T * threads: a = src[i]; b = src[a.x % n];
+ *           dst[i] = b.x + b.y + b.z + b.w (two dependent 16-byte loads and a
+ *           store: the two memory round trips a finalize token takes).
+ * Timed beside the finalize they bound what it can reach when it is
+ * latency-bound (few tokens). src: n 16-byte elements (4 x uint32); dst: n
+ * int32. Both may be NULL for kind 0. T in [1, 2^20], D % 8 == 0 and
+ * 8 <= D <= 65536.
+ * ---------------------------------------------------------------------- */
+MOE_API int32_t moe_launch_floor_threads(int32_t T, int32_t D);
+MOE_API moe_status_t moe_launch_floor(int32_t kind, int32_t T, int32_t D, const void *src,
+                              int32_t *dst, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

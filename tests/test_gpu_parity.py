@@ -96,6 +96,26 @@ def test_device_conversions_match_oracle_encoders(dev):
     assert np.array_equal(e4[fin], orc.f32_to_e4m3(clipped)[fin])
 
 
+def test_launch_floor_kernels(dev):
+    """The latency-floor kernels of the finalize's launch shape run, and the
+    two-load kernel computes dst[i] = sum of the words of src[src[i].x % n]."""
+    from combine_moe_shuffle_amd import _lib
+    lib = _lib.load()
+    for T, D in ((1, 7168), (128, 7168), (5, 1024)):
+        threads = lib.moe_launch_floor_threads(T, D)
+        assert threads % 64 == 0 and 64 <= threads <= 1024
+        n = T * threads
+        g = np.random.default_rng(T)
+        src = g.integers(0, 1 << 20, size=(n, 4)).astype(np.int32)
+        say("launch floor", T, D, threads)
+        dst = ops.moe_launch_floor(1, T, D, src=torch.from_numpy(src).to(dev))
+        ops.moe_launch_floor(0, T, D, device=dev)
+        torch.cuda.synchronize()
+        pick = src[src[:, 0].astype(np.uint32) % n]
+        want = pick.astype(np.uint32).sum(axis=1, dtype=np.uint32).view(np.int32)
+        assert np.array_equal(dst.cpu().numpy(), want)
+
+
 # ---------------------------------------------------------------- shuffle
 SHUFFLE_CASES = [
     # (name, T, E, K, vtc, score kind)
