@@ -8,6 +8,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_addoption(parser):
+    parser.addoption("--random-shape-seeds", type=int, default=32,
+                     help="how many seeded random shapes the randomized GPU parity test "
+                          "draws (default 32)")
+
+
+def pytest_generate_tests(metafunc):
+    if "random_seed" in metafunc.fixturenames:
+        n = metafunc.config.getoption("--random-shape-seeds")
+        metafunc.parametrize("random_seed", range(n))
+
+
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; parity through the C ABI")
