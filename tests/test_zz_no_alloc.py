@@ -71,6 +71,28 @@ def test_noalloc_shuffle_matches_workspace_shuffle(dev):
         assert np.array_equal(got[3].cpu().numpy().reshape(-1), rop.reshape(-1)), name
 
 
+def test_noalloc_shuffle_on_a_side_stream(dev):
+    """On a stream of its own (the scratch address is checked against the
+    stream's device), then on the default stream with fewer tokens: both equal
+    moe_shuffle."""
+    wl = W.WORKLOADS["zipf"]
+    for T, stream in ((3000, torch.cuda.Stream()), (100, None)):
+        scores = torch.from_numpy(W.router_scores(wl, T=T)).to(dev)
+        say("noalloc shuffle, stream", T, stream is not None)
+        got = _outputs(T, wl.E, wl.K, dev, -5)
+        if stream is not None:
+            stream.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(stream):
+                ops.moe_shuffle_noalloc(scores, wl.K, out=got)
+            torch.cuda.current_stream().wait_stream(stream)
+        else:
+            ops.moe_shuffle_noalloc(scores, wl.K, out=got)
+        want = ops.moe_shuffle(scores, wl.K)
+        torch.cuda.synchronize()
+        for g, w_ in zip(got, want):
+            assert torch.equal(g.view(-1), w_.view(-1))
+
+
 def test_noalloc_shuffle_rejects_beyond_scratch(dev):
     # T = 2^20 tokens at E = 256, K = 8 needs 32 MiB + 32 MiB of workspace
     T, E, K = 1 << 20, 256, 8
