@@ -273,7 +273,9 @@ def setup_dispatch(ctx, wl, with_cpu, general=False):
                 "stages": "shuffle -> " + " -> ".join(stage_names)},
         traffic_key=name,
         dtype="bf16" if not quant else "bf16->fp8e4m3",
-        kernel_src={"shuffle": ["shuffle.hip"], "gather": ["gather.hip"],
+        kernel_src={"shuffle": ["shuffle.hip"],
+                    # the general gather builds its row lists with combine.hip's kernel
+                    "gather": ["gather.hip", "combine.hip"] if general else ["gather.hip"],
                     "scatter": ["combine.hip"]},
         cpu=cpu_baseline_dispatch(ctx.orc, inp, wl, vtc) if with_cpu else None)
 
