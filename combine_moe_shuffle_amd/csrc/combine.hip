@@ -16,11 +16,12 @@
 //  by_token  the inverse map row_of_pair[t, 0..K) written by the shuffle;
 //            invalid slots dropped and the rest sorted in-wave.
 //  general   only token_indices is known: a CSR of rows per token is built
-//            first (count with atomics on per-token counters, exclusive scan,
-//            fill; one launch of per-token-range workgroups up to 131072
-//            rows, four launches beyond); the order inside a token's list then
-//            depends on the atomics, so the reduce kernel sorts each list
-//            before adding.
+//            first. Up to 131072 rows it takes two launches: chunks of 1024
+//            rows bucket their (row, token) pairs by 128-token range, then
+//            one workgroup per range counts its tokens' rows, scans and
+//            fills; beyond that, four launches (count, scan, slot, fill). The
+//            order inside a token's list depends on atomics either way, so
+//            the reduce kernel sorts each list before adding.
 //  padded    the general path over the static-shape expert-parallel layout
 //            [EP, T_K, D]: each row is read from the slab of the rank that
 //            owns its expert.
@@ -307,23 +308,35 @@ __global__ void csr_fill_kernel(const int* __restrict__ ti, int T, int a,
   if (static_cast<unsigned>(t) < static_cast<unsigned>(T)) list[start[t] + slot[r]] = r;
 }
 
-// The CSR in one launch: workgroup b owns tokens [b*kRangeT, (b+1)*kRangeT).
-// It reads every valid row's token index (from L2 after the first
-// workgroup), counts its own tokens' rows in LDS and the rows of all lower
-// tokens in registers -- the latter is its offset in the CSR, so no
-// workgroup waits for another -- scans its counters into start[], and fills
-// its tokens' lists by advancing them. With counts (the padded layout) each
-// workgroup takes the valid row count from the expert prefix, which
-// workgroup 0 also writes (prefix[0..E], prefix[E] = rows covered, clamped to
-// a). The order inside a token's list follows the LDS atomics; the reduce
-// kernels sort it. Used while every workgroup's two passes over the indices
-// stay short (a <= kRangeMaxRows).
-constexpr int kRangeT = 256;           // tokens per workgroup
-constexpr int kRangeMaxRows = 131072;  // rows read twice by every workgroup
-constexpr int kRangeUnroll = 8;        // index loads in flight per thread
+// The CSR in two launches, for up to kRangeMaxRows rows and kMaxRanges
+// token ranges of kRangeT tokens:
+//  csr_bucket  one workgroup per kBucketRows rows (one per thread): groups its
+//              rows by token range in LDS (counting sort over the ranges) and
+//              writes them range by range as (row, token) pairs, with each
+//              range's count and chunk-local start ([range][chunk] matrices).
+//  csr_range   one workgroup per token range: finds its rows in every chunk
+//              from the two matrices (its place in the final list is the sum
+//              of its chunk-local starts), counts them per token in LDS --
+//              each row taking its slot within its token and staged in LDS --
+//              scans the counts into start[], and writes each staged row to
+//              start + slot.
+// Each workgroup reads only its own rows. With counts (the padded layout)
+// every bucket workgroup takes the valid row count from the expert prefix,
+// which workgroup 0 also writes (prefix[0..E], prefix[E] = rows covered,
+// clamped to a). The order inside a token's list follows the LDS atomics; the
+// reduce kernels sort it.
+constexpr int kRangeT = 128;           // tokens per range
+constexpr int kRangeMaxRows = 131072;  // rows the two-launch build takes
+constexpr int kBucketRows = kScanThreads;
+constexpr int kMaxChunks = kRangeMaxRows / kBucketRows;  // 128
+constexpr int kMaxRanges = 2048;
 constexpr int kRangeStage = 8192;      // a range's rows kept in LDS for the fill
 static_assert(kRangeT <= 256, "the staged fill packs the token offset in 8 bits");
+static_assert(kMaxRanges <= 2 * kScanThreads, "the bucket scan takes two ranges per thread");
 
+// Exclusive scan of one value per thread over a workgroup of NT threads;
+// `total` gets the sum. Syncs the workgroup; wave_tot holds NT / 64 entries.
+template <int NT = kScanThreads>
 __device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* wave_tot,
                                                int& total) {
   int incl = v;
@@ -336,7 +349,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* w
   __syncthreads();
   int base = 0;
   total = 0;
-  for (int w = 0; w < kScanThreads / kWave; ++w) {
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
     const int wt = wave_tot[w];
     if (w < wave) base += wt;
     total += wt;
@@ -344,112 +358,143 @@ __device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* w
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(kScanThreads) void csr_range_build_kernel(
+// The valid row count: min(sum of counts, a) with counts (workgroup 0 writes
+// the expert prefix), else *vrows clamped to [0, a]. Syncs the workgroup.
+__device__ __forceinline__ int csr_valid_rows(const int* __restrict__ vrows,
+                                              const int* __restrict__ counts, int E, int a,
+                                              int* __restrict__ prefix, int lane, int wave,
+                                              int* wave_tot) {
+  if (!counts) return clamp_count(vrows, a);
+  const int tid = threadIdx.x;
+  const int v = tid < E ? max(counts[tid], 0) : 0;  // E <= kScanThreads
+  int total;
+  const int excl = block_excl_scan(v, lane, wave, wave_tot, total);
+  if (blockIdx.x == 0) {
+    if (tid < E) prefix[tid] = min(excl, a);
+    if (tid == 0) prefix[E] = min(total, a);
+  }
+  return min(total, a);
+}
+
+__global__ __launch_bounds__(kScanThreads) void csr_bucket_kernel(
     const int* __restrict__ ti, int T, int a, const int* __restrict__ vrows,
-    const int* __restrict__ counts, int E, int* __restrict__ prefix, int* __restrict__ start,
-    int* __restrict__ list) {
-  __shared__ int cnt[kRangeT];
-  __shared__ int wave_tot[3][kScanThreads / kWave];
-  __shared__ int stage_row[kRangeStage];
-  __shared__ int stage_pos[kRangeStage];  // token offset | slot << 8
-  __shared__ int nstage;
+    const int* __restrict__ counts, int E, int* __restrict__ prefix, int nrange, int G,
+    int* __restrict__ rcnt, int* __restrict__ roff, int2* __restrict__ packed) {
+  __shared__ int hist[kMaxRanges];
+  __shared__ int wave_tot[2][kScanThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int lo = blockIdx.x * kRangeT;
-  const int n = min(kRangeT, T - lo);
-  int V;
-  if (counts) {  // E <= kScanThreads, one expert per thread
-    const int v = tid < E ? max(counts[tid], 0) : 0;
-    int total;
-    const int excl = block_excl_scan(v, lane, wave, wave_tot[0], total);
-    if (blockIdx.x == 0) {
-      if (tid < E) prefix[tid] = min(excl, a);
-      if (tid == 0) prefix[E] = min(total, a);
-    }
-    V = min(total, a);
-  } else {
-    V = clamp_count(vrows, a);
+  const int g = blockIdx.x;
+  const int r = g * kBucketRows + tid;
+  const int t_raw = r < a ? ti[r] : -1;  // issued before the valid count is known
+  for (int i = tid; i < nrange; i += kScanThreads) hist[i] = 0;
+  const int V = csr_valid_rows(vrows, counts, E, a, prefix, lane, wave, wave_tot[0]);
+  const int t = r < V ? t_raw : -1;
+  const bool valid = static_cast<unsigned>(t) < static_cast<unsigned>(T);
+  const int q = valid ? t / kRangeT : 0;
+  __syncthreads();
+  const int pos = valid ? atomicAdd(&hist[q], 1) : 0;
+  __syncthreads();
+  // chunk-local starts of the ranges: two ranges per thread
+  const int c0 = 2 * tid < nrange ? hist[2 * tid] : 0;
+  const int c1 = 2 * tid + 1 < nrange ? hist[2 * tid + 1] : 0;
+  int total;
+  const int s0 = block_excl_scan(c0 + c1, lane, wave, wave_tot[1], total);
+  if (2 * tid < nrange) {
+    rcnt[static_cast<int64_t>(2 * tid) * G + g] = c0;
+    roff[static_cast<int64_t>(2 * tid) * G + g] = s0;
   }
+  if (2 * tid + 1 < nrange) {
+    rcnt[static_cast<int64_t>(2 * tid + 1) * G + g] = c1;
+    roff[static_cast<int64_t>(2 * tid + 1) * G + g] = s0 + c0;
+  }
+  __syncthreads();  // every count read before the starts overwrite them
+  if (2 * tid < nrange) hist[2 * tid] = s0;
+  if (2 * tid + 1 < nrange) hist[2 * tid + 1] = s0 + c0;
+  __syncthreads();
+  if (valid) packed[static_cast<int64_t>(g) * kBucketRows + hist[q] + pos] = make_int2(r, t);
+}
+
+constexpr int kRangeThreads = 1024;  // at least one thread per token of a range
+static_assert(kRangeThreads >= kRangeT && kMaxChunks <= kRangeThreads, "range kernel shape");
+__global__ __launch_bounds__(kRangeThreads) void csr_range_kernel(
+    int T, int G, const int* __restrict__ rcnt, const int* __restrict__ roff,
+    const int2* __restrict__ packed, int* __restrict__ start, int* __restrict__ list) {
+  __shared__ int cnt[kRangeT];
+  __shared__ int seg[kMaxChunks + 1];  // exclusive prefix of this range's chunk counts
+  __shared__ int soff[kMaxChunks];     // chunk-local start of this range
+  __shared__ int wave_tot[3][kRangeThreads / kWave];
+  __shared__ int stage_row[kRangeStage];
+  __shared__ int stage_pos[kRangeStage];  // token offset | slot << 8
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int q = blockIdx.x;
+  const int lo = q * kRangeT;
+  const int n = min(kRangeT, T - lo);
+  const int c = tid < G ? rcnt[static_cast<int64_t>(q) * G + tid] : 0;
+  const int o = tid < G ? roff[static_cast<int64_t>(q) * G + tid] : 0;
   if (tid < kRangeT) cnt[tid] = 0;
-  if (tid == 0) nstage = 0;
+  int nq;
+  const int sc = block_excl_scan<kRangeThreads>(c, lane, wave, wave_tot[0], nq);  // syncs
+  int base;
+  (void)block_excl_scan<kRangeThreads>(o, lane, wave, wave_tot[1], base);         // rows of lower ranges
+  if (tid < G) {
+    seg[tid] = sc;
+    soff[tid] = o;
+  }
+  if (tid == 0) seg[G] = nq;
   __syncthreads();
 
-  // pass 1: count this range's rows -- each takes its slot within its token
-  // and is staged in LDS (one position counter update per wave and batch) --
-  // and the rows of tokens below the range in `below`. Every load of a batch
-  // issues before the first use (clamped index; rows past V are dropped by
-  // the select).
-  int below = 0;
-  for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
-    int tv[kRangeUnroll];
-#pragma unroll
-    for (int u = 0; u < kRangeUnroll; ++u) {
-      const int r = r0 + u * kScanThreads + tid;
-      const int t = ti[min(r, V - 1)];
-      tv[u] = r < V ? t : -1;
+  // count: row i of the range sits in chunk g with seg[g] <= i < seg[g+1]
+  const bool staged = nq <= kRangeStage;
+  for (int i = tid; i < nq; i += kRangeThreads) {
+    int lo_g = 0, hi_g = G;  // seg[lo_g] <= i < seg[hi_g]
+    while (hi_g - lo_g > 1) {
+      const int mid = (lo_g + hi_g) >> 1;
+      if (seg[mid] <= i) lo_g = mid;
+      else hi_g = mid;
     }
-#pragma unroll
-    for (int u = 0; u < kRangeUnroll; ++u) {
-      const int rel = tv[u] - lo;
-      const bool in = static_cast<unsigned>(rel) < static_cast<unsigned>(n);
-      if (!in && static_cast<unsigned>(tv[u]) < static_cast<unsigned>(lo)) ++below;
-      const uint64_t m = __ballot(in);
-      if (m != 0) {  // wave-uniform
-        const int leader = __builtin_ctzll(m);
-        int wbase = 0;
-        if (lane == leader) wbase = atomicAdd(&nstage, __popcll(m));
-        wbase = __shfl(wbase, leader, kWave);
-        if (in) {
-          const int slot = atomicAdd(&cnt[rel], 1);
-          const int sp = wbase + __popcll(m & ((uint64_t{1} << lane) - 1u));
-          if (sp < kRangeStage) {
-            stage_row[sp] = r0 + u * kScanThreads + tid;
-            stage_pos[sp] = rel | (slot << 8);
-          }
-        }
-      }
+    const int2 e = packed[static_cast<int64_t>(lo_g) * kBucketRows + soff[lo_g] + (i - seg[lo_g])];
+    const int rel = e.y - lo;
+    const int slot = atomicAdd(&cnt[rel], 1);
+    if (staged) {
+      stage_row[i] = e.x;
+      stage_pos[i] = rel | (slot << 8);
     }
   }
-  int below_total;
-  (void)block_excl_scan(below, lane, wave, wave_tot[1], below_total);  // syncs: cnt complete
+  __syncthreads();
 
-  // exclusive scan of the range's counters (one per thread), offset by below
-  const int c = tid < n ? cnt[tid] : 0;
+  // exclusive scan of the range's counters (one per thread), offset by base
+  const int cv = tid < n ? cnt[tid] : 0;
   int range_total;
-  const int pos = below_total + block_excl_scan(c, lane, wave, wave_tot[2], range_total);
+  const int pos = base + block_excl_scan<kRangeThreads>(cv, lane, wave, wave_tot[2], range_total);
   if (tid < n) {
     start[lo + tid] = pos;
     cnt[tid] = pos;
   }
-  if (lo + n == T && tid == 0) start[T] = below_total + range_total;
+  if (lo + n == T && tid == 0) start[T] = base + range_total;
   __syncthreads();
 
-  // fill: staged rows go straight to start + slot; a range with more rows
-  // than the stage holds reads the indices again instead, each row taking the
-  // next free position of its token
-  const int ns = nstage;
-  if (ns <= kRangeStage) {
-    for (int i = tid; i < ns; i += kScanThreads) {
+  if (staged) {
+    for (int i = tid; i < nq; i += kRangeThreads) {
       const int p = stage_pos[i];
       list[cnt[p & 0xFF] + (p >> 8)] = stage_row[i];
     }
     return;
   }
-  for (int r0 = 0; r0 < V; r0 += kScanThreads * kRangeUnroll) {
-    int tv[kRangeUnroll];
-#pragma unroll
-    for (int u = 0; u < kRangeUnroll; ++u) {
-      const int r = r0 + u * kScanThreads + tid;
-      const int t = ti[min(r, V - 1)];
-      tv[u] = r < V ? t : -1;
+  // more rows than the stage holds: read them again, each row taking the next
+  // free position of its token
+  for (int i = tid; i < nq; i += kRangeThreads) {
+    int lo_g = 0, hi_g = G;
+    while (hi_g - lo_g > 1) {
+      const int mid = (lo_g + hi_g) >> 1;
+      if (seg[mid] <= i) lo_g = mid;
+      else hi_g = mid;
     }
-#pragma unroll
-    for (int u = 0; u < kRangeUnroll; ++u) {
-      const int rel = tv[u] - lo;
-      if (static_cast<unsigned>(rel) < static_cast<unsigned>(n))
-        list[atomicAdd(&cnt[rel], 1)] = r0 + u * kScanThreads + tid;
-    }
+    const int2 e = packed[static_cast<int64_t>(lo_g) * kBucketRows + soff[lo_g] + (i - seg[lo_g])];
+    list[atomicAdd(&cnt[e.y - lo], 1)] = e.x;
   }
 }
 
@@ -616,9 +661,22 @@ SliceShape combine_shape(int nch) {
 
 }  // namespace
 
+// The two-launch CSR build applies (else the four-launch one).
+bool two_launch_build(int T, int a) {
+  return a <= kRangeMaxRows && (T + kRangeT - 1) / kRangeT <= kMaxRanges;
+}
+
+// start [T+1], then list [a] and, for the two-launch build, packed (row,
+// token) pairs [a] and the [range][chunk] count and start matrices; for the
+// four-launch build, slot [a].
 size_t scatter_add_workspace_bytes(int T, int a) {
-  return align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
-         2 * align256(static_cast<size_t>(a) * sizeof(int));
+  const size_t head = align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
+                      align256(static_cast<size_t>(a) * sizeof(int));
+  if (!two_launch_build(T, a)) return head + align256(static_cast<size_t>(a) * sizeof(int));
+  const size_t nrange = (static_cast<size_t>(T) + kRangeT - 1) / kRangeT;
+  const size_t G = (static_cast<size_t>(a) + kBucketRows - 1) / kBucketRows;
+  return head + align256(static_cast<size_t>(a) * sizeof(int2)) +
+         2 * align256(nrange * G * sizeof(int));
 }
 
 size_t scatter_add_padded_workspace_bytes(int T, int T_K, int E) {
@@ -626,20 +684,50 @@ size_t scatter_add_padded_workspace_bytes(int T, int T_K, int E) {
          scatter_add_workspace_bytes(T, T_K);
 }
 
+namespace {
+
+// Workspace layout of scatter_add_workspace_bytes(T, a) from `ws`: start
+// [T+1], list [a], then slot [a] (four-launch build) or the two-launch
+// build's buffers (see csr_two_launch).
+void csr_layout(char* ws, int T, int a, int** start, int** list, int** slot) {
+  *start = reinterpret_cast<int*>(ws);
+  ws += align256((static_cast<size_t>(T) + 1) * sizeof(int));
+  *list = reinterpret_cast<int*>(ws);
+  ws += align256(static_cast<size_t>(a) * sizeof(int));
+  *slot = reinterpret_cast<int*>(ws);
+}
+
+void csr_two_launch(const int* ti, int T, int a, const int* valid_rows, const int* counts, int E,
+                    int* prefix, char* ws, int* start, int* list, hipStream_t stream) {
+  const int nrange = (T + kRangeT - 1) / kRangeT;
+  const int G = (a + kBucketRows - 1) / kBucketRows;
+  char* p = ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)) +
+            align256(static_cast<size_t>(a) * sizeof(int));
+  int2* packed = reinterpret_cast<int2*>(p);
+  p += align256(static_cast<size_t>(a) * sizeof(int2));
+  int* rcnt = reinterpret_cast<int*>(p);
+  p += align256(static_cast<size_t>(nrange) * G * sizeof(int));
+  int* roff = reinterpret_cast<int*>(p);
+  hipLaunchKernelGGL(csr_bucket_kernel, dim3(G), dim3(kScanThreads), 0, stream, ti, T, a,
+                     valid_rows, counts, E, prefix, nrange, G, rcnt, roff, packed);
+  hipLaunchKernelGGL(csr_range_kernel, dim3(nrange), dim3(kRangeThreads), 0, stream, T, G,
+                     rcnt, roff, packed, start, list);
+}
+
+}  // namespace
+
 hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const int* counts,
                                      int E, const int* ti, uint16_t* out, int T, int D,
                                      void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   int* prefix = reinterpret_cast<int*>(ws);
   ws += align256((static_cast<size_t>(E) + 1) * sizeof(int));
-  int* cnt = reinterpret_cast<int*>(ws);
-  int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
-  int* list = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
-                                     align256(static_cast<size_t>(T_K) * sizeof(int)));
-  if (T_K <= kRangeMaxRows) {
-    hipLaunchKernelGGL(csr_range_build_kernel, dim3((T + kRangeT - 1) / kRangeT),
-                       dim3(kScanThreads), 0, stream, ti, T, T_K, nullptr, counts, E, prefix,
-                       cnt, list);
+  int* cnt = nullptr;
+  int* list = nullptr;
+  int* slot = nullptr;
+  csr_layout(ws, T, T_K, &cnt, &list, &slot);
+  if (two_launch_build(T, T_K)) {
+    csr_two_launch(ti, T, T_K, nullptr, counts, E, prefix, ws, cnt, list, stream);
   } else {
     hipLaunchKernelGGL(padded_prefix_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
                        E, T_K, prefix);
@@ -705,16 +793,14 @@ hipError_t launch_token_lists(const int* ti, int T, int a, const int* valid_rows
                               void* workspace, const int** start, const int** list,
                               hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
-  int* cnt = reinterpret_cast<int*>(ws);  // [T+1]: counts, then starts
-  int* slot = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(T) + 1) * sizeof(int)));
-  int* lst = reinterpret_cast<int*>(reinterpret_cast<char*>(slot) +
-                                    align256(static_cast<size_t>(a) * sizeof(int)));
+  int* cnt = nullptr;  // [T+1]: counts, then starts
+  int* lst = nullptr;
+  int* slot = nullptr;
+  csr_layout(ws, T, a, &cnt, &lst, &slot);
   *start = cnt;
   *list = lst;
-  if (a <= kRangeMaxRows) {
-    hipLaunchKernelGGL(csr_range_build_kernel, dim3((T + kRangeT - 1) / kRangeT),
-                       dim3(kScanThreads), 0, stream, ti, T, a, valid_rows, nullptr, 0, nullptr,
-                       cnt, lst);
+  if (two_launch_build(T, a)) {
+    csr_two_launch(ti, T, a, valid_rows, nullptr, 0, nullptr, ws, cnt, lst, stream);
   } else {
     hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,
                        T + 1);

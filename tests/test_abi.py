@@ -76,8 +76,12 @@ def test_workspace_sizes(lib):
     assert lib.moe_shuffle_workspace_bytes(8192, 256, 8) == 8192 * 8 * 4 + 256 * 256 * 4
     assert lib.moe_shuffle_workspace_bytes(65, 3, 2) == 768 + 256
     assert lib.moe_shuffle_workspace_bytes(-1, 3, 2) == 0
-    # scatter: (T+1) counters + a slots + a list entries
-    assert lib.moe_scatter_add_workspace_bytes(8192, 65536) == 33024 + 2 * 262144
+    # scatter: (T+1) starts + a list entries, then (a <= 131072 rows, at most
+    # 2048 ranges of 128 tokens) a (row, token) pairs and two [range][chunk of
+    # 1024 rows] int matrices, else a slots
+    assert lib.moe_scatter_add_workspace_bytes(8192, 65536) == (33024 + 262144 + 524288 +
+                                                               2 * 64 * 64 * 4)
+    assert lib.moe_scatter_add_workspace_bytes(1000, 200000) == (4096 + 800000 + 800000)
 
 
 def _err(lib):
@@ -181,7 +185,9 @@ def test_scatter_padded_rejects(lib):
     assert p(FAKE, 1 << 10, 1 << 22, FAKE, 1 << 10, FAKE, FAKE, 16, 64, FAKE, ws,
              None) == INVALID                                                     # EP*T_K
     assert p(None, 2, 0, None, 8, None, None, 16, 64, None, 0, None) == OK        # T_K == 0
-    assert lib.moe_scatter_add_padded_workspace_bytes(16, 64, 8) == 256 + 256 + 2 * 256
+    # expert prefix, starts, list, (row, token) pairs, two 1x1 matrices
+    assert lib.moe_scatter_add_padded_workspace_bytes(16, 64, 8) == 256 + 256 + 256 + 512 + \
+        2 * 256
 
 
 @host_only

@@ -416,7 +416,7 @@ def test_scatter_add_padded_long_lists(dev):
 
 
 def test_scatter_add_csr_multi_launch(dev):
-    """More rows than the one-launch CSR build takes (131072): the general
+    """More rows than the two-launch CSR build takes (131072): the general
     and padded combines build the CSR in four launches."""
     T, D, E, K, EP = 70000, 64, 8, 2, 2
     inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, None, seed=4)
@@ -437,7 +437,7 @@ def test_scatter_add_csr_multi_launch(dev):
 
 
 def test_scatter_add_csr_stage_overflow(dev):
-    """One 256-token range owning more rows (10000) than the CSR build stages
+    """One 128-token range owning more rows (10000) than the CSR build stages
     in LDS (8192): the build falls back to a second pass over the indices."""
     g = np.random.default_rng(13)
     T, D, a = 100, 64, 10000
@@ -455,6 +455,24 @@ def test_scatter_add_csr_stage_overflow(dev):
     want = orc.scatter_add_padded(out0.copy(), slabs, counts, ti)
     out = bf_dev(out0, dev)
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts, dev), i32_dev(ti, dev), out)
+    assert np.array_equal(bits_host(out), want)
+
+
+@pytest.mark.parametrize("T", [2048 * 128, 2048 * 128 + 1])
+def test_scatter_add_csr_most_ranges(dev, T):
+    """The most token ranges the two-launch CSR build takes (2048 of 128
+    tokens), and one token more (four launches), with 131072 rows of which
+    the first 120000 are valid."""
+    g = np.random.default_rng(T)
+    D, a, V = 64, 131072, 120000
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    ti[:80] = T - 1  # the last token, a list of more than 64 rows
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("csr most ranges", T, D, a, V)
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
     assert np.array_equal(bits_host(out), want)
 
 
