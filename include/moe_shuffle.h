@@ -349,9 +349,12 @@ MOE_API moe_status_t moe_split_shuffling(const moe_bf16_t *in, int64_t in_rows,
  *   acc = 0; for k = 0..K-1 with r = row_of_pair[t*K+k] >= 0:
  *       acc = fma(expert_weights[t*K+k], f32(y[r, :]), acc)
  *   if shared: acc = acc + f32(shared[t, :]);   h = bf16_rne(acc)
- *   ss = sum_d f32(h_d)^2 in fp32 (flags bit 0: each square rounded to bf16
- *        first, the bf16-square mode of [K3]); the summation order is the
- *        kernel's (a tree), not sequential
+ *   ss = sum_d f32(h_d)^2, each square in fp32 (flags bit 0: rounded to bf16
+ *        first, the bf16-square mode of [K3]), accumulated in fp64 and
+ *        rounded once to fp32: a square of a bf16 value has at most 16
+ *        significant bits, so the fp64 sum is exact or within a few fp64
+ *        ulps and its fp32 rounding does not depend on the summation order
+ *        except for sums that close to an fp32 rounding midpoint
  *   inv = 1 / sqrt(ss / D + eps), correctly rounded from double
  *   out[t, d] = bf16_rne( (f32(h_d) * inv) * f32(gamma_d) )
  * MXFP8 (mx_codes and mx_scales both set; D % 32 == 0): for each 32-element

@@ -136,6 +136,11 @@ SHUFFLE_CASES = [
     # histogram sizes E * ceil(T/32) around the one-launch scan-and-place limit
     ("hist-8192", 1024, 256, 8, 1000, "normal"),
     ("hist-8448", 1056, 256, 8, 1000, "normal"),
+    # more than 4096 blocks of 32 tokens; experts of ~10000 rows; E not a
+    # multiple of 8
+    ("many-blocks", 140000, 8, 2, 139000, "normal"),
+    ("big-experts", 20000, 2, 1, None, "normal"),
+    ("E12", 3000, 12, 3, 2900, "normal"),
 ]
 
 
