@@ -28,8 +28,10 @@
  * readings of steps the pages call but do not print: the scale of an
  * all-zero row in gather_scale_quant (an EPS constant), the round-up
  * direction of the UE8M0 scale, the 128x4 tile order of the swizzled
- * scales, and the EP re-sort layout; each is pinned against a restatement
- * of its reading, not against the pages.
+ * scales (beyond its innermost axis: the pages' padding stores fix that a
+ * row's 4 columns of a tile are 4 contiguous, 4-aligned bytes), and the EP
+ * re-sort layout; each is pinned against a restatement of its reading, not
+ * against the pages.
  */
 #include <math.h>
 #include <stdint.h>

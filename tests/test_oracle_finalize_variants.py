@@ -76,6 +76,30 @@ def test_swizzle_is_a_bijection_with_zero_padding(orc):
     assert np.all(sw[dead] == 0) and np.all(sw[~dead] == 7)
 
 
+@pytest.mark.parametrize("M,cols", [(1, 4), (130, 8), (200, 160), (129, 12)])
+def test_swizzle_padding_words_as_the_page_stores_them(orc, M, cols):
+    """The "all_reduce_mhc" page (_LamportMHCDeviceKernel, the zeroing of the
+    padding rows' scales) zeroes the padding with one 32-bit store per padding
+    row and 4-column group, at the offset of (row, 4j). For those stores to
+    clear exactly the padding, the layout must keep the 4 scales of a row and
+    column group in 4 contiguous bytes from a 4-aligned offset, and those words
+    must cover the padding entries and no live one. The page fixes this much of
+    the tile order; the order of rows inside a tile stays a reading."""
+    Mp = -(-M // 128) * 128
+    words = set()
+    for row in range(M, Mp):
+        for j in range(cols // 4):
+            base = orc.mxfp8_swizzle_offset(row, 4 * j, cols)
+            assert base % 4 == 0
+            for kk in range(4):
+                assert orc.mxfp8_swizzle_offset(row, 4 * j + kk, cols) == base + kk
+            words.update(range(base, base + 4))
+    pad = {orc.mxfp8_swizzle_offset(m, k, cols) for m in range(M, Mp) for k in range(cols)}
+    live = {orc.mxfp8_swizzle_offset(m, k, cols) for m in range(M) for k in range(cols)}
+    assert words == pad and not (words & live)
+    assert len(pad) + len(live) == orc.mxfp8_scale_bytes(M, 32 * cols, True)
+
+
 def test_swizzle_hand_offsets(orc):
     # cols = 8: two 4-column tiles per 128-row band, 512 bytes each
     cases = {(0, 0): 0, (1, 0): 16, (32, 0): 4, (96, 3): 12 + 3, (0, 1): 1,
