@@ -803,6 +803,103 @@ def test_graph_replay_matches_eager(dev):
             assert torch.equal(got[k], v), (rep, k)
 
 
+def test_graph_replay_general_paths(dev):
+    """The entry points the first graph test leaves out, captured in one HIP
+    graph with caller workspaces: the shuffle that allocates nothing, the
+    general gather (two-launch row-list build), the FP8 rowwise gather, the
+    general and padded combines, and the EP re-sort both ways. Every replay,
+    with the outputs spoiled by eager work in between, equals the eager run
+    bit for bit."""
+    wl = W.WORKLOADS["zipf"]
+    T, D, E, K, vtc, EP = 300, 512, 16, 4, 250, 4
+    inp = W.dispatch_inputs(wl, T=T, D=D, E=E, K=K, vtc=vtc, out0="normal")
+    a = T * K
+    g = np.random.default_rng(31)
+    s = torch.from_numpy(np.ascontiguousarray(inp.scores)).to(dev)
+    x, y, out0 = bf_dev(inp.x, dev), bf_dev(inp.y, dev), bf_dev(inp.out0, dev)
+    slabs = bf_dev(W.to_bf16_bits(g.standard_normal((EP, a, D)).astype(np.float32)), dev)
+    C, lo, hi = 16, 4, 12
+    rcounts = g.integers(0, 6, size=(EP, C)).astype(np.int32)
+    nrows = int(rcounts.sum())
+    tok = bf_dev(W.to_bf16_bits(g.standard_normal((nrows, D)).astype(np.float32)), dev)
+    rc = i32_dev(rcounts, dev)
+    vtc_d = scalar_dev(vtc, dev)
+    lib = ops._lib.load()
+
+    def buffers():
+        i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device=dev)  # noqa: E731
+        u8 = lambda n: torch.empty(max(n, 1), dtype=torch.uint8, device=dev)  # noqa: E731
+        bf = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)  # noqa: E731
+        return dict(
+            shuf=(i32(E + 1), i32(a), i32(a), i32(T, K)), rows=bf(a, D),
+            gws=u8(lib.moe_gather_scale_workspace_bytes(T, a)),
+            codes=torch.empty((a, D), dtype=torch.uint8, device=dev),
+            qs=torch.empty(a, dtype=torch.float32, device=dev),
+            out=out0.clone(), sws=u8(lib.moe_scatter_add_workspace_bytes(T, a)),
+            pout=out0.clone(), pws=u8(lib.moe_scatter_add_padded_workspace_bytes(T, a, E)),
+            cs=bf(nrows, D), cws=u8(lib.moe_shuffling_workspace_bytes(EP, hi - lo, nrows)),
+            ss=bf(nrows, D), sws2=u8(lib.moe_shuffling_workspace_bytes(EP, hi - lo, nrows)))
+
+    def path(b):
+        counts, ei, ti, rop = ops.moe_shuffle_noalloc(s, K, vtc_d, out=b["shuf"])
+        vr = counts[E:]
+        ops.moe_gather_scale(x, ti, ei, s, vr, out=b["rows"], workspace=b["gws"])
+        ops.moe_gather_scale_quant(x, ti, ei, s, None, vr, out=b["codes"], out_scale=b["qs"])
+        ops.moe_scatter_add(b["out"], y, ti, vr, workspace=b["sws"])
+        ops.moe_scatter_add_padded(slabs, counts[:E], ti, b["pout"], workspace=b["pws"])
+        _, oc = ops.moe_combine_shuffling(tok, rc, lo, hi, None, out=b["cs"],
+                                          workspace=b["cws"])
+        ops.moe_split_shuffling(b["cs"], rc, lo, hi, None, out=b["ss"], workspace=b["sws2"])
+        b["oc"] = oc
+
+    def snapshot(b):
+        V = int(b["shuf"][0][E].item())
+        n = int(b["oc"][-1].item())
+        snap = {k: b[k].cpu().clone() for k in ("out", "pout", "oc")}
+        snap.update(rows=b["rows"][:V].cpu().clone(), codes=b["codes"][:V].cpu().clone(),
+                    qs=b["qs"][:V].cpu().clone(), cs=b["cs"][:n].cpu().clone())
+        for i, t in enumerate(b["shuf"]):
+            snap[f"shuf{i}"] = t.cpu().clone()
+        # the split writes back the rows of the local columns only
+        snap["ss"] = b["ss"].cpu().clone()
+        return snap
+
+    say("graph replay, general paths", T, D, E, K, vtc, EP, nrows)
+    eager = buffers()
+    eager["ss"].view(torch.int16).fill_(0x7E00)
+    path(eager)
+    torch.cuda.synchronize()
+    want = snapshot(eager)
+
+    b = buffers()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager pass on the capture stream first
+        path(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        path(b)
+    for rep in range(3):
+        b["out"].copy_(out0)
+        b["pout"].copy_(out0)
+        for k in ("rows", "cs"):
+            b[k].view(torch.int16).fill_(0x7E01 + rep)
+        b["ss"].view(torch.int16).fill_(0x7E00)
+        b["codes"].fill_(0xA5)
+        b["qs"].fill_(-1.0)
+        b["oc"].fill_(-7)
+        for t in b["shuf"]:
+            t.fill_(-3)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = snapshot(b)
+        for k, v in want.items():
+            assert torch.equal(got[k], v), (rep, k)
+
+
 # ---------------------------------------------------------------- full sizes
 @pytest.fixture(scope="module")
 def zipf_inputs():
