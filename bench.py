@@ -71,8 +71,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-WORKLOAD_CHOICES = ["zipf", "zipf-general", "quant", "prefill", "decode", "prefill-swizzled",
-                    "mhc", "padded", "shuffling"]
+WORKLOAD_CHOICES = ["zipf", "zipf-general", "quant", "tiny", "prefill", "decode",
+                    "prefill-swizzled", "mhc", "padded", "shuffling"]
 DISPATCH_METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1xMI355X"
 
 
@@ -80,9 +80,10 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None,
-                   help="timed steps (default 50; 1000 for decode, whose step is a few us)")
+                   help="timed steps (default 50; 1000 for decode and tiny, whose steps "
+                        "take a few us)")
     p.add_argument("--warmup", type=int, default=None,
-                   help="untimed steps first (default 5; 50 for decode)")
+                   help="untimed steps first (default 5; 50 for decode and tiny)")
     p.add_argument("--workload", default="zipf", choices=WORKLOAD_CHOICES)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cold", action="store_true",
@@ -461,7 +462,7 @@ def main():
     ctx = SimpleNamespace(torch=torch, ops=ops, W=W, orc=orc, dev=dev, bf=bf, lib=_lib.load())
     with_cpu = not args.no_cpu_baseline
     name = args.workload
-    if name in ("zipf", "quant"):
+    if name in ("zipf", "quant", "tiny"):
         s = setup_dispatch(ctx, W.WORKLOADS[name], with_cpu)
     elif name == "zipf-general":
         s = setup_dispatch(ctx, W.WORKLOADS["zipf"], with_cpu, general=True)
@@ -477,7 +478,8 @@ def main():
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
     if s.cpu:
         s.cpu["host"] = _host()
-    short = name == "decode"  # a few us per step: more steps amortise the region's ends
+    # a few us per step: more steps amortise the region's ends
+    short = name in ("decode", "tiny")
     steps = args.steps if args.steps is not None else (1000 if short else 50)
     warm = args.warmup if args.warmup is not None else (50 if short else 5)
     # each stage's library calls, checked and converted once (ops.prepare: the

@@ -1,7 +1,8 @@
 // moe_shuffle: top-k routing and the stable counting sort of the
 // (token, expert) pairs by expert, as three launches with no global atomics
 // (two when the histogram of step 1 fits in LDS: scan_place_kernel does
-// steps 2 and 3 in one launch):
+// steps 2 and 3 in one launch; one for up to 64 tokens and 256 experts,
+// where shuffle_small_kernel does all three in one workgroup):
 //
 //  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
 //     the top-k of two tokens at once, the expert axis spread over its 64
@@ -85,30 +86,18 @@ __device__ __forceinline__ int clamp_count(const int* p, int hi) {
   return v < 0 ? 0 : (v > hi ? hi : v);
 }
 
-// PL = expert candidates per lane (E <= 64 * PL).
-template <int PL>
-__global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
-    const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
-    const int* __restrict__ vtc_ptr, int* __restrict__ pair, int* __restrict__ hist,
-    int nblk) {
-  __shared__ uint32_t mask[kMaxE];
-  __shared__ int sel[kTokPerBlock * kMaxK];
-
-  const int blk = blockIdx.x;
-  const int t0 = blk * kTokPerBlock;
-  const int vtc = clamp_count(vtc_ptr, T);
-  const int lane = lane_id();
-  const int wave = uniform(threadIdx.x >> 6);
-  const int nwaves = kSelThreads / kWave;
-
-  for (int e = threadIdx.x; e < E; e += kSelThreads) mask[e] = 0u;
-
-  // ---- top-k: wave w owns tokens w and w+16 of the workgroup and works on
-  // the two together. Lane l holds experts l*PL .. l*PL+PL-1,
-  // sorted by (score desc, id asc); a lower lane always holds lower ids, so
-  // among lanes whose best ties with the wave max the lowest lane holds the
-  // lowest expert id.
-  constexpr int kTokPerWave = kTokPerBlock / (kSelThreads / kWave);  // 2
+// Top-k of TPW tokens in one wave, worked on together so that their lane
+// exchanges overlap: tokens t0 + wave + q * nwaves (q < TPW). Lane l holds
+// experts l*PL .. l*PL+PL-1, sorted by (score desc, id asc); a lower lane
+// always holds lower ids, so among lanes whose best ties with the wave max the
+// lowest lane holds the lowest expert id. Slot k of token i = wave + q *
+// nwaves (relative to t0) goes to sel[i * K + k], for tokens below vtc.
+template <int PL, int TPW>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ scores, int64_t st,
+                                          int64_t se, int E, int K, int vtc, int t0,
+                                          int wave, int nwaves, int lane,
+                                          int* __restrict__ sel) {
+  constexpr int kTokPerWave = TPW;
   uint32_t ku[kTokPerWave][PL];
   int ke[kTokPerWave][PL];
   bool live[kTokPerWave];
@@ -191,6 +180,29 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
 #pragma unroll
   for (int q = 0; q < kTokPerWave; ++q)
     if (live[q] && lane < K) sel[(wave + q * nwaves) * K + lane] = mine[q];
+}
+
+// PL = expert candidates per lane (E <= 64 * PL).
+template <int PL>
+__global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
+    const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
+    const int* __restrict__ vtc_ptr, int* __restrict__ pair, int* __restrict__ hist,
+    int nblk) {
+  __shared__ uint32_t mask[kMaxE];
+  __shared__ int sel[kTokPerBlock * kMaxK];
+
+  const int blk = blockIdx.x;
+  const int t0 = blk * kTokPerBlock;
+  const int vtc = clamp_count(vtc_ptr, T);
+  const int lane = lane_id();
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nwaves = kSelThreads / kWave;
+
+  for (int e = threadIdx.x; e < E; e += kSelThreads) mask[e] = 0u;
+
+  // ---- top-k: wave w owns tokens w and w+16 of the workgroup
+  wave_topk<PL, kTokPerBlock / (kSelThreads / kWave)>(scores, st, se, E, K, vtc, t0, wave,
+                                                       nwaves, lane, sel);
   __syncthreads();
 
   // ---- one bit per valid token in each of its experts' masks
@@ -213,6 +225,74 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
   }
   for (int e = threadIdx.x; e < E; e += kSelThreads)
     hist[static_cast<int64_t>(e) * nblk + blk] = __popc(mask[e]);
+}
+
+// Up to 64 tokens and 256 experts, the whole shuffle in one launch: one
+// workgroup takes the top-k of every token (4 per wave), ORs one bit per token
+// into a 64-bit LDS mask per expert, and places every pair itself: expert e's
+// rows start at the exclusive scan over experts of the mask popcounts, and a
+// pair's rank is the popcount of the mask bits of the tokens before it.
+constexpr int kSmallT = 64;
+constexpr int kSmallMaxE = 256;
+template <int PL>
+__global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
+    const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
+    const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
+    int* __restrict__ ei, int* __restrict__ rop) {
+  __shared__ unsigned long long mask[kSmallMaxE];
+  __shared__ int sel[kSmallT * kMaxK];
+  __shared__ int first[kSmallMaxE];
+  __shared__ int wave_tot[kSelThreads / kWave];
+  const int tid = threadIdx.x;
+  const int vtc = clamp_count(vtc_ptr, T);
+  const int lane = lane_id();
+  const int wave = uniform(tid >> 6);
+  const int nwaves = kSelThreads / kWave;
+
+  for (int e = tid; e < E; e += kSelThreads) mask[e] = 0ull;
+  wave_topk<PL, kSmallT / (kSelThreads / kWave)>(scores, st, se, E, K, vtc, 0, wave, nwaves,
+                                                 lane, sel);
+  __syncthreads();
+  const int npairs = T * K;
+  for (int p = tid; p < npairs; p += kSelThreads) {
+    const int t = p / K;
+    if (t < vtc) atomicOr(&mask[sel[p]], 1ull << t);
+  }
+  __syncthreads();
+
+  // expert e's first row: one expert per thread (E <= 256), scanned
+  const int c = tid < E ? __popcll(mask[tid]) : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = incl - c;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  if (tid < E) {
+    first[tid] = base;
+    counts[tid] = c;
+  }
+  if (tid == 0) counts[E] = vtc * K;
+  __syncthreads();
+
+  for (int p = tid; p < npairs; p += kSelThreads) {
+    const int t = p / K;
+    if (t < vtc) {
+      const int e = sel[p];
+      const int r = first[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
+      ti[r] = t;
+      ei[r] = e;
+      if (rop) rop[p] = r;
+    } else {
+      ti[p] = t;
+      ei[p] = -1;
+      if (rop) rop[p] = -1;
+    }
+  }
 }
 
 // One wave per expert: exclusive scan of hist[e][0..nblk) in place (offsets
@@ -432,6 +512,18 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
   if (T == 0) {
     hipLaunchKernelGGL(zero_counts_kernel, dim3((E + 1 + 255) / 256), dim3(256), 0, stream,
                        counts, E + 1);
+    return hipGetLastError();
+  }
+  if (T <= kSmallT && E <= kSmallMaxE) {
+    const dim3 g(1), b(kSelThreads);
+#define MOE_SMALL(PLV)                                                                        \
+  hipLaunchKernelGGL(shuffle_small_kernel<PLV>, g, b, 0, stream, scores, st, se, T, E, K, vtc, \
+                     counts, token_indices, expert_indices, row_of_pair)
+    const int pls = (E + kWave - 1) / kWave;
+    if (pls <= 1) MOE_SMALL(1);
+    else if (pls <= 2) MOE_SMALL(2);
+    else MOE_SMALL(4);
+#undef MOE_SMALL
     return hipGetLastError();
   }
   const int nblk = (T + kTokPerBlock - 1) / kTokPerBlock;

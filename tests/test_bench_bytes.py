@@ -34,6 +34,15 @@ def test_zipf_general_dispatch_bytes():
     _close(b["scatter"], 688.128 + 2 * 86.016 + 0.192)
 
 
+def test_tiny_dispatch_bytes():
+    # T=64, D=1024, E=8, K=2, every token valid: 128 rows of 2048 bytes
+    b = bench.dispatch_bytes(64, 1024, 8, 2, 64, quant=False)
+    assert b["shuffle"] == 64 * 8 * 4 + 3 * 128 * 4 + 9 * 4
+    assert b["gather"] == 64 * 2048 + 128 * 2048 + 128 * 4 + 2 * 128 * 4
+    assert b["scatter"] == 128 * 2048 + 2 * 64 * 2048 + 128 * 4
+    _close(sum(b.values()), 0.9232)
+
+
 def test_quant_dispatch_bytes():
     # T=4096, D=5120, E=16, K=1: one row per token, FP8 codes 1 byte per element
     b = bench.dispatch_bytes(4096, 5120, 16, 1, 4096, quant=True)

@@ -141,6 +141,13 @@ SHUFFLE_CASES = [
     ("many-blocks", 140000, 8, 2, 139000, "normal"),
     ("big-experts", 20000, 2, 1, None, "normal"),
     ("E12", 3000, 12, 3, 2900, "normal"),
+    # the one-launch form (T <= 64, E <= 256) and just past its limits
+    ("small-ties", 64, 40, 6, 50, "ties"),
+    ("small-top64", 48, 256, 64, None, "normal"),
+    ("small-strided", 33, 48, 5, None, "strided"),
+    ("small-vtc0", 10, 16, 2, 0, "normal"),
+    ("T65", 65, 256, 8, None, "normal"),
+    ("E257-T64", 64, 257, 3, 60, "normal"),
 ]
 
 
