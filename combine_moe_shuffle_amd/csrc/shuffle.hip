@@ -1,8 +1,9 @@
 // moe_shuffle: top-k routing and the stable counting sort of the
 // (token, expert) pairs by expert, as three launches with no global atomics
 // (two when the histogram of step 1 fits in LDS: scan_place_kernel does
-// steps 2 and 3 in one launch; one for up to 64 tokens and 256 experts,
-// where shuffle_small_kernel does all three in one workgroup):
+// steps 2 and 3 in one launch; one for up to 64 tokens with up to 256
+// experts, or 32 tokens with more, where shuffle_small_kernel does all three
+// in one workgroup):
 //
 //  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
 //     the top-k of two tokens at once, the expert axis spread over its 64
@@ -227,21 +228,23 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
     hist[static_cast<int64_t>(e) * nblk + blk] = __popc(mask[e]);
 }
 
-// Up to 64 tokens and 256 experts, the whole shuffle in one launch: one
-// workgroup takes the top-k of every token (4 per wave), ORs one bit per token
-// into a 64-bit LDS mask per expert, and places every pair itself: expert e's
-// rows start at the exclusive scan over experts of the mask popcounts, and a
-// pair's rank is the popcount of the mask bits of the tokens before it.
+// Small batches, the whole shuffle in one launch: one workgroup takes the
+// top-k of every token (TPW per wave: up to 64 tokens with E <= 256, up to 32
+// with more experts, whose candidates take more registers), ORs one bit per
+// token into a 64-bit LDS mask per expert, and places every pair itself:
+// expert e's rows start at the exclusive scan over experts of the mask
+// popcounts, and a pair's rank is the popcount of the mask bits of the tokens
+// before it.
 constexpr int kSmallT = 64;
-constexpr int kSmallMaxE = 256;
-template <int PL>
+constexpr int kSmallWideE = 256;  // above this, up to 32 tokens
+template <int PL, int TPW>
 __global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
     const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
     const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
     int* __restrict__ ei, int* __restrict__ rop) {
-  __shared__ unsigned long long mask[kSmallMaxE];
+  __shared__ unsigned long long mask[kMaxE];
   __shared__ int sel[kSmallT * kMaxK];
-  __shared__ int first[kSmallMaxE];
+  __shared__ int first[kMaxE];
   __shared__ int wave_tot[kSelThreads / kWave];
   const int tid = threadIdx.x;
   const int vtc = clamp_count(vtc_ptr, T);
@@ -250,8 +253,8 @@ __global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
   const int nwaves = kSelThreads / kWave;
 
   for (int e = tid; e < E; e += kSelThreads) mask[e] = 0ull;
-  wave_topk<PL, kSmallT / (kSelThreads / kWave)>(scores, st, se, E, K, vtc, 0, wave, nwaves,
-                                                 lane, sel);
+  static_assert(TPW * (kSelThreads / kWave) <= kSmallT, "tokens of one workgroup");
+  wave_topk<PL, TPW>(scores, st, se, E, K, vtc, 0, wave, nwaves, lane, sel);
   __syncthreads();
   const int npairs = T * K;
   for (int p = tid; p < npairs; p += kSelThreads) {
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
   }
   __syncthreads();
 
-  // expert e's first row: one expert per thread (E <= 256), scanned
+  // expert e's first row: one expert per thread (E <= kSelThreads), scanned
   const int c = tid < E ? __popcll(mask[tid]) : 0;
   int incl = c;
 #pragma unroll
@@ -514,15 +517,21 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
                        counts, E + 1);
     return hipGetLastError();
   }
-  if (T <= kSmallT && E <= kSmallMaxE) {
+  constexpr int kWaves = kSelThreads / kWave;
+  if ((T <= kSmallT && E <= kSmallWideE) || T <= kSmallT / 2) {
     const dim3 g(1), b(kSelThreads);
-#define MOE_SMALL(PLV)                                                                        \
-  hipLaunchKernelGGL(shuffle_small_kernel<PLV>, g, b, 0, stream, scores, st, se, T, E, K, vtc, \
-                     counts, token_indices, expert_indices, row_of_pair)
+#define MOE_SMALL(PLV, TPWV)                                                             \
+  hipLaunchKernelGGL((shuffle_small_kernel<PLV, TPWV>), g, b, 0, stream, scores, st, se, T, \
+                     E, K, vtc, counts, token_indices, expert_indices, row_of_pair)
     const int pls = (E + kWave - 1) / kWave;
-    if (pls <= 1) MOE_SMALL(1);
-    else if (pls <= 2) MOE_SMALL(2);
-    else MOE_SMALL(4);
+    if (E <= kSmallWideE) {
+      if (pls <= 1) MOE_SMALL(1, kSmallT / kWaves);
+      else if (pls <= 2) MOE_SMALL(2, kSmallT / kWaves);
+      else MOE_SMALL(4, kSmallT / kWaves);
+    } else {
+      if (pls <= 8) MOE_SMALL(8, kSmallT / 2 / kWaves);
+      else MOE_SMALL(16, kSmallT / 2 / kWaves);
+    }
 #undef MOE_SMALL
     return hipGetLastError();
   }

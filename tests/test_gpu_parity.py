@@ -141,13 +141,17 @@ SHUFFLE_CASES = [
     ("many-blocks", 140000, 8, 2, 139000, "normal"),
     ("big-experts", 20000, 2, 1, None, "normal"),
     ("E12", 3000, 12, 3, 2900, "normal"),
-    # the one-launch form (T <= 64, E <= 256) and just past its limits
+    # the one-launch form (T <= 64 with E <= 256, T <= 32 with E <= 1024) and
+    # just past its limits
     ("small-ties", 64, 40, 6, 50, "ties"),
     ("small-top64", 48, 256, 64, None, "normal"),
     ("small-strided", 33, 48, 5, None, "strided"),
     ("small-vtc0", 10, 16, 2, 0, "normal"),
+    ("small-E384", 32, 384, 8, 30, "normal"),
+    ("small-E1024-top64", 20, 1024, 64, None, "ties"),
     ("T65", 65, 256, 8, None, "normal"),
     ("E257-T64", 64, 257, 3, 60, "normal"),
+    ("E300-T33", 33, 300, 4, None, "strided"),
 ]
 
 
