@@ -1233,32 +1233,42 @@ def test_randomized_shapes_against_oracle(dev, random_seed):
     out = bf_dev(out0, dev)
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:E].contiguous(), gti, out)
     assert np.array_equal(bits_host(out), want)
-    # finalize and mHC on the shuffle's rows (D a multiple of 32 for MXFP8)
+    # finalize and mHC on the shuffle's rows (D a multiple of 32 for MXFP8);
+    # the finalize's flags drawn per seed: bf16 squares, bf16 weights, and the
+    # 128x4-tiled scales where D allows them
     Df = 32 * max(1, D // 32)
     yf = W.to_bf16_bits(g.standard_normal((T * K, Df)).astype(np.float32))
     w = g.random((T, K)).astype(np.float32)
     shared = W.to_bf16_bits(g.standard_normal((T, Df)).astype(np.float32))
     gamma = W.to_bf16_bits(g.uniform(0.5, 1.5, Df).astype(np.float32))
-    want_o = orc.finalize_rmsnorm(yf, w, rop, shared, gamma, 1e-6)
-    o, mc, ms = ops.moe_finalize_rmsnorm(bf_dev(yf, dev), torch.from_numpy(w).to(dev), grop,
-                                         bf_dev(shared, dev), bf_dev(gamma, dev), 1e-6,
-                                         mxfp8=True)
-    got = bits_host(o)
-    _close(got, want_o, "finalize")
-    oc, os_ = orc.mxfp8_quantize(got)
-    assert np.array_equal(mc.cpu().numpy(), oc) and np.array_equal(ms.cpu().numpy(), os_)
+    fl = int(g.integers(0, 8)) & (7 if Df % 128 == 0 else 3)
+    wk = W.to_bf16_bits(w) if fl & 2 else w
+    say("random finalize flags", fl)
+    want_o, want_c, want_s = orc.finalize_rmsnorm(yf, wk, rop, shared, gamma, 1e-6, flags=fl,
+                                                  mxfp8=True)
+    wdev = bf_dev(wk, dev) if fl & 2 else torch.from_numpy(w).to(dev)
+    o, mc, ms = ops.moe_finalize_rmsnorm(bf_dev(yf, dev), wdev, grop, bf_dev(shared, dev),
+                                         bf_dev(gamma, dev), 1e-6, flags=fl & 1, mxfp8=True,
+                                         scale_layout="swizzled" if fl & 4 else "rowmajor")
+    _close(bits_host(o), want_o, "finalize")
+    assert_mx_end_to_end(mc.cpu().numpy(), ms.cpu().numpy().reshape(-1), want_c,
+                         np.asarray(want_s).reshape(-1), "finalize MXFP8")
     hc = int(g.integers(1, 5))
     res = W.to_bf16_bits(g.standard_normal((T, hc, Df)).astype(np.float32))
     post = g.uniform(0, 2, (T, hc)).astype(np.float32)
     comb = g.random((T, hc, hc)).astype(np.float32)
     pre = g.random((T, hc)).astype(np.float32)
-    wres, wout, _, _ = orc.finalize_mhc(yf, w, rop, shared, res, post, comb, pre, gamma, 1e-6)
+    wres, wout, wmc, wms = orc.finalize_mhc(yf, wk, rop, shared, res, post, comb, pre, gamma,
+                                            1e-6, flags=fl, mxfp8=True)
     f32 = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
-    r_out, m_out = ops.moe_finalize_mhc(bf_dev(yf, dev), f32(w), grop, bf_dev(shared, dev),
-                                        bf_dev(res, dev), f32(post), f32(comb), f32(pre),
-                                        bf_dev(gamma, dev), 1e-6)
+    r_out, m_out, mmc, mms = ops.moe_finalize_mhc(
+        bf_dev(yf, dev), wdev, grop, bf_dev(shared, dev), bf_dev(res, dev), f32(post),
+        f32(comb), f32(pre), bf_dev(gamma, dev), 1e-6, flags=fl & 1, mxfp8=True,
+        scale_layout="swizzled" if fl & 4 else "rowmajor")
     _close(bits_host(r_out), wres, "mhc residual")
     _close(bits_host(m_out), wout, "mhc out")
+    assert_mx_end_to_end(mmc.cpu().numpy(), mms.cpu().numpy().reshape(-1), wmc,
+                         np.asarray(wms).reshape(-1), "mhc MXFP8")
 
 
 def test_every_op_is_deterministic(dev):
