@@ -1269,6 +1269,31 @@ def test_randomized_shapes_against_oracle(dev, random_seed):
     _close(bits_host(m_out), wout, "mhc out")
     assert_mx_end_to_end(mmc.cpu().numpy(), mms.cpu().numpy().reshape(-1), wmc,
                          np.asarray(wms).reshape(-1), "mhc MXFP8")
+    # the EP re-sort both ways: ranks, columns, local range and layout drawn
+    EP, C = int(g.integers(1, 9)), int(g.integers(1, 65))
+    lo = int(g.integers(0, C + 1))
+    hi = int(g.integers(lo, C + 1))
+    rc = g.integers(0, 7, size=(EP, C)).astype(np.int32)
+    packed = bool(g.random() < 0.5)
+    stride = None if packed else int(rc.sum(axis=1).max() + g.integers(0, 4))
+    nrows = max(1, int(rc.sum()) if packed else EP * stride)
+    Dr = 8 * int(g.integers(1, 100))
+    say("random re-sort", EP, C, lo, hi, packed, nrows, Dr)
+    tok = W.to_bf16_bits(g.standard_normal((nrows, Dr)).astype(np.float32))
+    want_c, want_oc = orc.combine_shuffling(tok, rc, lo, hi, stride,
+                                            out=np.full((nrows, Dr), SENTINEL, np.uint16))
+    out_c = torch.full((nrows, Dr), SENTINEL - 65536, dtype=torch.int16,
+                       device=dev).view(torch.bfloat16)
+    out_c, oc = ops.moe_combine_shuffling(bf_dev(tok, dev), i32_dev(rc, dev), lo, hi, stride,
+                                          out=out_c)
+    assert np.array_equal(oc.cpu().numpy(), want_oc)
+    assert np.array_equal(bits_host(out_c), want_c)
+    want_s = orc.split_shuffling(want_c, rc, lo, hi, stride,
+                                 out=np.full((nrows, Dr), SENTINEL, np.uint16))
+    out_s = torch.full((nrows, Dr), SENTINEL - 65536, dtype=torch.int16,
+                       device=dev).view(torch.bfloat16)
+    ops.moe_split_shuffling(out_c, i32_dev(rc, dev), lo, hi, stride, out=out_s)
+    assert np.array_equal(bits_host(out_s), want_s)
 
 
 def test_every_op_is_deterministic(dev):
