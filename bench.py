@@ -11,6 +11,9 @@ resident in HBM:
             moe_gather_scale (with a workspace) -> moe_scatter_add
   quant     (T=4096, D=5120, E=16, K=1)
             moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
+  tiny      (T=64, D=1024, E=8, K=2) the zipf step's calls, launch-bound; the
+            line's "sweep" times the zipf step's calls at decode batch sizes,
+            T = 1, 8, 32, 64 and 128 at D=7168, E=256, K=8
   prefill   (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
   decode    (T=128, D=7168, K=8)   moe_finalize_rmsnorm; the line's "sweep"
             also times T = 1, 8, 32 and 128 (per call and per kernel)
@@ -92,7 +95,7 @@ def parse():
                    help="launch every stage through the checked op call (dtype, shape and "
                         "device checks each call) instead of a call prepared once")
     p.add_argument("--no-sweep", action="store_true",
-                   help="skip the decode line's token-count sweep (profiling runs: every "
+                   help="skip the decode and tiny lines' token-count sweeps (profiling runs: every "
                         "launch at the workload's size)")
     p.add_argument("--graph", action="store_true",
                    help="replay a HIP graph of the step instead of launching its kernels from "
@@ -633,7 +636,43 @@ def main():
     }
     if name == "decode" and not args.no_sweep:
         line["sweep"] = decode_sweep(ctx, W.WORKLOADS[name], steps, warm, args.checked)
+    if name == "tiny" and not args.no_sweep:
+        line["sweep"] = dispatch_sweep(ctx, W.WORKLOADS["zipf"], steps, warm, args.checked)
     print(json.dumps(line), flush=True)
+
+
+DISPATCH_SWEEP_T = (1, 8, 32, 64, 128)
+
+
+def dispatch_sweep(ctx, wl, steps, warm, checked):
+    """The zipf step's calls (shuffle, gather and scatter by token) at decode
+    batch sizes, every token valid: the step launched from Python `steps`
+    times back to back (wall clock per step, launches included) and each
+    stage's kernels alone per launch (graph replay)."""
+    torch = ctx.torch
+    out = []
+    for T in DISPATCH_SWEEP_T:
+        sub = setup_dispatch(ctx, ctx.W.Workload(**{**wl.__dict__, "T": T, "vtc": None}), False)
+        fns = [(n, f if checked else ctx.ops.prepare(f)) for n, f in sub.stages.items()]
+
+        def step():
+            for _, f in fns:
+                f()
+
+        for _ in range(warm):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        step_us = (time.perf_counter() - t0) * 1e6 / steps
+        out.append({"tokens": T, "step_us": round(step_us, 2),
+                    "tokens_per_s": T / (step_us * 1e-6),
+                    "stage_kernel_us": {n: round(stage_ms(torch, f, steps) * 1e3, 2)
+                                        for n, f in fns},
+                    "bytes": sum(sub.stage_bytes.values())})
+    return out
 
 
 def decode_sweep(ctx, wl, steps, warm, checked):

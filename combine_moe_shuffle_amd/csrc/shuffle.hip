@@ -1,9 +1,8 @@
 // moe_shuffle: top-k routing and the stable counting sort of the
 // (token, expert) pairs by expert, as three launches with no global atomics
 // (two when the histogram of step 1 fits in LDS: scan_place_kernel does
-// steps 2 and 3 in one launch; one for up to 64 tokens with up to 256
-// experts, or 32 tokens with more, where shuffle_small_kernel does all three
-// in one workgroup):
+// steps 2 and 3 in one launch; one for up to 32 tokens, or 64 with short
+// top-k rounds, where shuffle_small_kernel does all three in one workgroup):
 //
 //  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
 //     the top-k of two tokens at once, the expert axis spread over its 64
@@ -229,8 +228,8 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
 }
 
 // Small batches, the whole shuffle in one launch: one workgroup takes the
-// top-k of every token (TPW per wave: up to 64 tokens with E <= 256, up to 32
-// with more experts, whose candidates take more registers), ORs one bit per
+// top-k of every token (TPW per wave, the fewest that cover T: up to 32 tokens
+// with any E, up to 64 when the top-k rounds are short), ORs one bit per
 // token into a 64-bit LDS mask per expert, and places every pair itself:
 // expert e's rows start at the exclusive scan over experts of the mask
 // popcounts, and a pair's rank is the popcount of the mask bits of the tokens
@@ -518,20 +517,41 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
     return hipGetLastError();
   }
   constexpr int kWaves = kSelThreads / kWave;
-  if ((T <= kSmallT && E <= kSmallWideE) || T <= kSmallT / 2) {
+  // Up to 32 tokens a wave holds at most two, as in the block kernel, so one
+  // launch costs no more top-k rounds than two. From 33 to 64 tokens a wave
+  // holds four: the two extra tokens' K rounds (longer with more candidates
+  // per lane) outweigh the launch saved once K * candidates per lane is above
+  // 8 (E = 256, K = 8 at 64 tokens: 9.3 us in one launch, 8.6 us in two).
+  const int pl_all = (E + kWave - 1) / kWave;
+  if (T <= kSmallT / 2 || (T <= kSmallT && E <= kSmallWideE && K * pl_all <= 8)) {
     const dim3 g(1), b(kSelThreads);
 #define MOE_SMALL(PLV, TPWV)                                                             \
   hipLaunchKernelGGL((shuffle_small_kernel<PLV, TPWV>), g, b, 0, stream, scores, st, se, T, \
                      E, K, vtc, counts, token_indices, expert_indices, row_of_pair)
+    // the fewest tokens per wave that cover T: each wave's K top-k rounds run
+    // for every token it holds, live or not
+#define MOE_SMALL_T(PLV)                               \
+  do {                                                 \
+    if (T <= kWaves) MOE_SMALL(PLV, 1);                \
+    else if (T <= 2 * kWaves) MOE_SMALL(PLV, 2);       \
+    else MOE_SMALL(PLV, 4);                            \
+  } while (0)
     const int pls = (E + kWave - 1) / kWave;
     if (E <= kSmallWideE) {
-      if (pls <= 1) MOE_SMALL(1, kSmallT / kWaves);
-      else if (pls <= 2) MOE_SMALL(2, kSmallT / kWaves);
-      else MOE_SMALL(4, kSmallT / kWaves);
+      if (pls <= 1) MOE_SMALL_T(1);
+      else if (pls <= 2) MOE_SMALL_T(2);
+      else MOE_SMALL_T(4);
     } else {
-      if (pls <= 8) MOE_SMALL(8, kSmallT / 2 / kWaves);
-      else MOE_SMALL(16, kSmallT / 2 / kWaves);
+      // more than 256 experts: at most two tokens per wave (registers)
+      if (pls <= 8) {
+        if (T <= kWaves) MOE_SMALL(8, 1);
+        else MOE_SMALL(8, 2);
+      } else {
+        if (T <= kWaves) MOE_SMALL(16, 1);
+        else MOE_SMALL(16, 2);
+      }
     }
+#undef MOE_SMALL_T
 #undef MOE_SMALL
     return hipGetLastError();
   }

@@ -141,14 +141,17 @@ SHUFFLE_CASES = [
     ("many-blocks", 140000, 8, 2, 139000, "normal"),
     ("big-experts", 20000, 2, 1, None, "normal"),
     ("E12", 3000, 12, 3, 2900, "normal"),
-    # the one-launch form (T <= 64 with E <= 256, T <= 32 with E <= 1024) and
-    # just past its limits
+    # the one-launch form (up to 32 tokens; up to 64 when K * ceil(E/64) <= 8
+    # and E <= 256) with 1, 2 and 4 tokens per wave, and just past its limits
     ("small-ties", 64, 40, 6, 50, "ties"),
-    ("small-top64", 48, 256, 64, None, "normal"),
+    ("small-T64-E128-K4", 64, 128, 4, 60, "ties"),
+    ("small-top64", 32, 256, 64, None, "normal"),
     ("small-strided", 33, 48, 5, None, "strided"),
     ("small-vtc0", 10, 16, 2, 0, "normal"),
     ("small-E384", 32, 384, 8, 30, "normal"),
-    ("small-E1024-top64", 20, 1024, 64, None, "ties"),
+    ("small-E1024-top64", 16, 1024, 64, None, "ties"),
+    ("small-T17", 17, 256, 8, None, "normal"),
+    ("T64-E256-K8", 64, 256, 8, 50, "normal"),
     ("T65", 65, 256, 8, None, "normal"),
     ("E257-T64", 64, 257, 3, 60, "normal"),
     ("E300-T33", 33, 300, 4, None, "strided"),
