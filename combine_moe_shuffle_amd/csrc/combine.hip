@@ -760,13 +760,15 @@ hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const 
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream) {
-  // G rows in flight: the next power of two >= K, at most 4 (for K = 8 two
-  // groups of 4 measured 1.5 % faster than one of 8: fewer registers, more
-  // waves resident)
-  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : 4);
+  // G rows in flight: the next power of two >= K, at most 4 on a full grid
+  // (for K = 8 two groups of 4 measured 1.5 % faster than one of 8: fewer
+  // registers, more waves resident), 8 on a grid of at most kFewUnits waves,
+  // which is latency-bound and saves the second group's round trip
   static const int allowed[] = {2, 4, 3, 1};
   const SliceShape sh = pick_slices(D / kChunk, allowed, 4, 1 << 20);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+  constexpr int64_t kFewUnits = 4096;
+  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 || units > kFewUnits ? 4 : 8));
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);
 #define L2(C, GV)                                                                          \
@@ -776,7 +778,8 @@ hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
   do {                                \
     if (G == 1) L2(C, 1);             \
     else if (G == 2) L2(C, 2);        \
-    else L2(C, 4);                    \
+    else if (G == 4) L2(C, 4);        \
+    else L2(C, 8);                    \
   } while (0)
   switch (sh.cpl) {
     case 1: LG(1); break;
