@@ -245,26 +245,32 @@ __global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
   __shared__ int sel[kSmallT * kMaxK];
   __shared__ int first[kMaxE];
   __shared__ int wave_tot[kSelThreads / kWave];
+  // the workgroup has as many waves as hold the tokens, TPW each (at most 16)
+  const int nt = blockDim.x;
   const int tid = threadIdx.x;
   const int vtc = clamp_count(vtc_ptr, T);
   const int lane = lane_id();
   const int wave = uniform(tid >> 6);
-  const int nwaves = kSelThreads / kWave;
+  const int nwaves = nt / kWave;
 
-  for (int e = tid; e < E; e += kSelThreads) mask[e] = 0ull;
+  for (int e = tid; e < E; e += nt) mask[e] = 0ull;
   static_assert(TPW * (kSelThreads / kWave) <= kSmallT, "tokens of one workgroup");
   wave_topk<PL, TPW>(scores, st, se, E, K, vtc, 0, wave, nwaves, lane, sel);
   __syncthreads();
   const int npairs = T * K;
-  for (int p = tid; p < npairs; p += kSelThreads) {
+  for (int p = tid; p < npairs; p += nt) {
     const int t = p / K;
     if (t < vtc) atomicOr(&mask[sel[p]], 1ull << t);
   }
   __syncthreads();
 
-  // expert e's first row: one expert per thread (E <= kSelThreads), scanned
-  const int c = tid < E ? __popcll(mask[tid]) : 0;
-  int incl = c;
+  // expert e's first row: thread i takes experts [i*per, i*per + per), their
+  // counts summed, the sums scanned over the workgroup
+  const int per = (E + nt - 1) / nt;
+  const int e0 = tid * per;
+  int mine = 0;
+  for (int e = e0; e < min(e0 + per, E); ++e) mine += __popcll(mask[e]);
+  int incl = mine;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const int u = __shfl_up(incl, o, kWave);
@@ -272,16 +278,18 @@ __global__ __launch_bounds__(kSelThreads) void shuffle_small_kernel(
   }
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
-  int base = incl - c;
+  int base = incl - mine;
   for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  if (tid < E) {
-    first[tid] = base;
-    counts[tid] = c;
+  for (int e = e0; e < min(e0 + per, E); ++e) {
+    const int c = __popcll(mask[e]);
+    first[e] = base;
+    counts[e] = c;
+    base += c;
   }
   if (tid == 0) counts[E] = vtc * K;
   __syncthreads();
 
-  for (int p = tid; p < npairs; p += kSelThreads) {
+  for (int p = tid; p < npairs; p += nt) {
     const int t = p / K;
     if (t < vtc) {
       const int e = sel[p];
@@ -524,7 +532,8 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
   // 8 (E = 256, K = 8 at 64 tokens: 9.3 us in one launch, 8.6 us in two).
   const int pl_all = (E + kWave - 1) / kWave;
   if (T <= kSmallT / 2 || (T <= kSmallT && E <= kSmallWideE && K * pl_all <= 8)) {
-    const dim3 g(1), b(kSelThreads);
+    // one token per wave up to 16 tokens: as many waves as tokens
+    const dim3 g(1), b(T <= kWaves ? T * kWave : kSelThreads);
 #define MOE_SMALL(PLV, TPWV)                                                             \
   hipLaunchKernelGGL((shuffle_small_kernel<PLV, TPWV>), g, b, 0, stream, scores, st, se, T, \
                      E, K, vtc, counts, token_indices, expert_indices, row_of_pair)
