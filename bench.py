@@ -12,8 +12,9 @@ resident in HBM:
   quant     (T=4096, D=5120, E=16, K=1)
             moe_shuffle -> moe_gather_scale_quant -> moe_scatter_add_by_token
   tiny      (T=64, D=1024, E=8, K=2) the zipf step's calls, launch-bound; the
-            line's "sweep" times the zipf step's calls at decode batch sizes,
-            T = 1, 8, 32, 64 and 128 at D=7168, E=256, K=8
+            line's "sweep" times the zipf step's calls, by token and through
+            token_indices, at decode batch sizes, T = 1, 8, 32, 64 and 128 at
+            D=7168, E=256, K=8
   prefill   (T=16384, D=5120, K=4) moe_finalize_rmsnorm with MXFP8
   decode    (T=128, D=7168, K=8)   moe_finalize_rmsnorm; the line's "sweep"
             also times T = 1, 8, 32 and 128 (per call and per kernel)
@@ -645,33 +646,37 @@ DISPATCH_SWEEP_T = (1, 8, 32, 64, 128)
 
 
 def dispatch_sweep(ctx, wl, steps, warm, checked):
-    """The zipf step's calls (shuffle, gather and scatter by token) at decode
-    batch sizes, every token valid: the step launched from Python `steps`
-    times back to back (wall clock per step, launches included) and each
-    stage's kernels alone per launch (graph replay)."""
+    """The zipf step's calls at decode batch sizes, every token valid: by token
+    (shuffle, gather and scatter through the inverse map) and through the
+    entry points that take token_indices ("general"). Each is launched from
+    Python `steps` times back to back (wall clock per step, launches included)
+    and each stage's kernels are timed alone per launch (graph replay)."""
     torch = ctx.torch
     out = []
     for T in DISPATCH_SWEEP_T:
-        sub = setup_dispatch(ctx, ctx.W.Workload(**{**wl.__dict__, "T": T, "vtc": None}), False)
-        fns = [(n, f if checked else ctx.ops.prepare(f)) for n, f in sub.stages.items()]
+        rec = {"tokens": T}
+        for key, general in (("", False), ("general_", True)):
+            sub = setup_dispatch(ctx, ctx.W.Workload(**{**wl.__dict__, "T": T, "vtc": None}),
+                                 False, general=general)
+            fns = [(n, f if checked else ctx.ops.prepare(f)) for n, f in sub.stages.items()]
 
-        def step():
-            for _, f in fns:
-                f()
+            def step():
+                for _, f in fns:
+                    f()
 
-        for _ in range(warm):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        step_us = (time.perf_counter() - t0) * 1e6 / steps
-        out.append({"tokens": T, "step_us": round(step_us, 2),
-                    "tokens_per_s": T / (step_us * 1e-6),
-                    "stage_kernel_us": {n: round(stage_ms(torch, f, steps) * 1e3, 2)
-                                        for n, f in fns},
-                    "bytes": sum(sub.stage_bytes.values())})
+            for _ in range(warm):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            step_us = (time.perf_counter() - t0) * 1e6 / steps
+            rec[key + "step_us"] = round(step_us, 2)
+            rec[key + "stage_kernel_us"] = {n: round(stage_ms(torch, f, steps) * 1e3, 2)
+                                            for n, f in fns}
+        rec["tokens_per_s"] = T / (rec["step_us"] * 1e-6)
+        out.append(rec)
     return out
 
 

@@ -16,7 +16,8 @@
 //  by_token  the inverse map row_of_pair[t, 0..K) written by the shuffle;
 //            invalid slots dropped and the rest sorted in-wave.
 //  general   only token_indices is known: a CSR of rows per token is built
-//            first. Up to 131072 rows it takes two launches: chunks of 1024
+//            first. Up to 4096 rows and tokens one workgroup builds it in
+//            LDS; up to 131072 rows it takes two launches: chunks of 1024
 //            rows bucket their (row, token) pairs by 128-token range, then
 //            one workgroup per range counts its tokens' rows, scans and
 //            fills; beyond that, four launches (count, scan, slot, fill). The
@@ -498,6 +499,64 @@ __global__ __launch_bounds__(kRangeThreads) void csr_range_kernel(
   }
 }
 
+// Small builds (up to kSmallRows rows and kSmallTok tokens) in one
+// workgroup and one launch: each valid row's token and its slot within the
+// token (an LDS atomic on the token's counter) stay in LDS, the counters are
+// scanned into start[], and each row goes to start[t] + slot. The order inside
+// a token's list depends on the atomics, as in the larger builds.
+constexpr int kSmallRows = 4096;
+constexpr int kSmallTok = 4096;
+static_assert(kSmallTok % kScanThreads == 0, "the token scan takes whole runs per thread");
+__global__ __launch_bounds__(kScanThreads) void csr_small_kernel(
+    const int* __restrict__ ti, int T, int a, const int* __restrict__ vrows,
+    const int* __restrict__ counts, int E, int* __restrict__ prefix, int* __restrict__ start,
+    int* __restrict__ list) {
+  __shared__ int cnt[kSmallTok];
+  __shared__ int tok[kSmallRows];
+  __shared__ int slot[kSmallRows];
+  __shared__ int wave_tot[2][kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  for (int i = tid; i < T; i += kScanThreads) cnt[i] = 0;
+  const int V = csr_valid_rows(vrows, counts, E, a, prefix, lane, wave, wave_tot[0]);
+  __syncthreads();
+  for (int r = tid; r < V; r += kScanThreads) {
+    const int t = ti[r];
+    const bool valid = static_cast<unsigned>(t) < static_cast<unsigned>(T);
+    tok[r] = valid ? t : -1;
+    if (valid) slot[r] = atomicAdd(&cnt[t], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the counters: thread i owns tokens [i*kPer, i*kPer + kPer)
+  constexpr int kPer = kSmallTok / kScanThreads;
+  int c[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = tid * kPer + q;
+    c[q] = i < T ? cnt[i] : 0;
+    mine += c[q];
+  }
+  int total;
+  int ex = block_excl_scan(mine, lane, wave, wave_tot[1], total);  // syncs
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = tid * kPer + q;
+    if (i < T) {
+      start[i] = ex;
+      cnt[i] = ex;
+    }
+    ex += c[q];
+  }
+  if (tid == 0) start[T] = total;
+  __syncthreads();
+  for (int r = tid; r < V; r += kScanThreads) {
+    const int t = tok[r];
+    if (t >= 0) list[cnt[t] + slot[r]] = r;
+  }
+}
+
 template <int CPL>
 __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
     uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
@@ -661,6 +720,9 @@ SliceShape combine_shape(int nch) {
 
 }  // namespace
 
+// The one-workgroup CSR build applies.
+bool small_build(int T, int a) { return a <= kSmallRows && T <= kSmallTok; }
+
 // The two-launch CSR build applies (else the four-launch one).
 bool two_launch_build(int T, int a) {
   return a <= kRangeMaxRows && (T + kRangeT - 1) / kRangeT <= kMaxRanges;
@@ -726,7 +788,10 @@ hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const 
   int* list = nullptr;
   int* slot = nullptr;
   csr_layout(ws, T, T_K, &cnt, &list, &slot);
-  if (two_launch_build(T, T_K)) {
+  if (small_build(T, T_K)) {
+    hipLaunchKernelGGL(csr_small_kernel, dim3(1), dim3(kScanThreads), 0, stream, ti, T, T_K,
+                       nullptr, counts, E, prefix, cnt, list);
+  } else if (two_launch_build(T, T_K)) {
     csr_two_launch(ti, T, T_K, nullptr, counts, E, prefix, ws, cnt, list, stream);
   } else {
     hipLaunchKernelGGL(padded_prefix_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts,
@@ -802,7 +867,10 @@ hipError_t launch_token_lists(const int* ti, int T, int a, const int* valid_rows
   csr_layout(ws, T, a, &cnt, &lst, &slot);
   *start = cnt;
   *list = lst;
-  if (two_launch_build(T, a)) {
+  if (small_build(T, a)) {
+    hipLaunchKernelGGL(csr_small_kernel, dim3(1), dim3(kScanThreads), 0, stream, ti, T, a,
+                       valid_rows, nullptr, 0, nullptr, cnt, lst);
+  } else if (two_launch_build(T, a)) {
     csr_two_launch(ti, T, a, valid_rows, nullptr, 0, nullptr, ws, cnt, lst, stream);
   } else {
     hipLaunchKernelGGL(csr_zero_kernel, dim3((T + 1 + 255) / 256), dim3(256), 0, stream, cnt,

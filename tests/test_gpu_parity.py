@@ -477,6 +477,40 @@ def test_scatter_add_csr_stage_overflow(dev):
     assert np.array_equal(bits_host(out), want)
 
 
+@pytest.mark.parametrize("T,a", [(4096, 4096), (1, 4096), (4097, 300), (300, 4097)])
+def test_csr_small_build_limits(dev, T, a):
+    """The one-workgroup row-list build (up to 4096 rows and 4096 tokens) at its
+    limits and just past them (the two-launch build): the general gather and
+    combine, and the padded combine, against the oracle."""
+    g = np.random.default_rng(T * 7 + a)
+    D, V = 64, a - a // 5
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    ti[: min(a, 70)] = T - 1  # one token with more than 64 rows
+    x = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    s = g.standard_normal((T, 4)).astype(np.float32)
+    ei = g.integers(0, 4, size=a).astype(np.int32)
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("csr small build limits", T, a, V)
+    rows0 = np.full((a, D), SENTINEL, np.uint16)
+    want_rows = orc.gather_scale(x, ti, ei, s, V, rows0.copy())
+    rows = bf_dev(rows0, dev)
+    ops.moe_gather_scale(bf_dev(x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                         torch.from_numpy(s).to(dev), scalar_dev(V, dev), out=rows)
+    assert np.array_equal(bits_host(rows), want_rows)
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    # padded: 4 experts over 2 ranks covering the first V rows
+    counts = np.array([V // 4, V // 4, V // 4, V - 3 * (V // 4)], np.int32)
+    slabs = W.to_bf16_bits(g.standard_normal((2, a, D)).astype(np.float32))
+    want = orc.scatter_add_padded(out0.copy(), slabs, counts, ti)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts, dev), i32_dev(ti, dev), out)
+    assert np.array_equal(bits_host(out), want)
+
+
 @pytest.mark.parametrize("T", [2048 * 128, 2048 * 128 + 1])
 def test_scatter_add_csr_most_ranges(dev, T):
     """The most token ranges the two-launch CSR build takes (2048 of 128
