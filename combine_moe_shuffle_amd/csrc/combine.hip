@@ -15,14 +15,16 @@
 // Where a token's rows come from:
 //  by_token  the inverse map row_of_pair[t, 0..K) written by the shuffle;
 //            invalid slots dropped and the rest sorted in-wave.
-//  general   only token_indices is known: a CSR of rows per token is built
-//            first. Up to 4096 rows and tokens one workgroup builds it in
-//            LDS; up to 131072 rows it takes two launches: chunks of 1024
-//            rows bucket their (row, token) pairs by 128-token range, then
-//            one workgroup per range counts its tokens' rows, scans and
-//            fills; beyond that, four launches (count, scan, slot, fill). The
-//            order inside a token's list depends on atomics either way, so
-//            the reduce kernel sorts each list before adding.
+//  general   only token_indices is known. Up to 1024 rows each wave finds
+//            its token's rows itself, in ascending order, with no other
+//            launch. Beyond that a CSR of rows per token is built first: up
+//            to 4096 rows and tokens by one workgroup in LDS; up to 131072
+//            rows in two launches (chunks of 1024 rows bucket their (row,
+//            token) pairs by 128-token range, then one workgroup per range
+//            counts its tokens' rows, scans and fills); beyond that in four
+//            (count, scan, slot, fill). The order inside a token's list
+//            depends on atomics, so the reduce kernel sorts each list
+//            before adding.
 //  padded    the general path over the static-shape expert-parallel layout
 //            [EP, T_K, D]: each row is read from the slab of the rank that
 //            owns its expert.
@@ -557,6 +559,53 @@ __global__ __launch_bounds__(kScanThreads) void csr_small_kernel(
   }
 }
 
+// Small general combines (up to kScanRows rows): each (token, slice) wave
+// finds its token's rows itself, with no row-list build and so no launch
+// before it. The wave loads all the token indices at once and adds the rows
+// it finds in ascending order, in batches of up to 64, kScanG in flight.
+constexpr int kScanRows = 1024;
+constexpr int kScanChunks = kScanRows / kWave;
+constexpr int kScanG = 8;
+template <int CPL, bool FULL>
+__device__ __forceinline__ void scan_reduce(uint16_t* __restrict__ orow,
+                                            const uint16_t* __restrict__ in,
+                                            const int (&tv)[kScanChunks], int V, int t, int D,
+                                            int nch, int base, int lane, int* stage) {
+  float acc[CPL][8];
+  load_acc<CPL, FULL>(acc, orow, nch, base);
+  const int n = for_token_rows(tv, V, t, lane, stage, [&](int rows, int nb) {
+    add_rows<CPL, kScanG, FULL>(acc, in, D, nch, base, rows, nb);
+  });
+  if (n) store_acc<CPL, FULL>(acc, orow, nch, base);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_scan_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
+    const int* __restrict__ ti, int a, int D, const int* __restrict__ vrows, int nsl) {
+  __shared__ int stage[kRowWaves][kWave];
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRowWaves + wv;
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int V = clamp_count(vrows, a);
+  int tv[kScanChunks];
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c) {
+    const int r = c * kWave + lane;
+    tv[c] = r < V ? ti[r] : -1;
+  }
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  if (slice0 + kWave * CPL <= nch)
+    scan_reduce<CPL, true>(orow, in, tv, V, t, D, nch, slice0 + lane, lane, stage[wv]);
+  else
+    scan_reduce<CPL, false>(orow, in, tv, V, t, D, nch, slice0 + lane, lane, stage[wv]);
+}
+
 template <int CPL>
 __global__ __launch_bounds__(kRowWaves* kWave) void scatter_csr_kernel(
     uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
@@ -888,14 +937,27 @@ hipError_t launch_token_lists(const int* ti, int T, int a, const int* valid_rows
 hipError_t launch_scatter_add(uint16_t* out, int T, const uint16_t* in, const int* ti,
                               int a, int D, const int* valid_rows, void* workspace,
                               hipStream_t stream) {
-  const int* cnt;
-  const int* list;
-  const hipError_t e = launch_token_lists(ti, T, a, valid_rows, workspace, &cnt, &list, stream);
-  if (e != hipSuccess) return e;
   const SliceShape sh = combine_shape(D / kChunk);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);
+  if (a <= kScanRows) {  // each wave finds its token's rows: no build
+#define LS(C)                                                                             \
+  hipLaunchKernelGGL(scatter_scan_kernel<C>, grid, block, 0, stream, out, T, in, ti, a, D, \
+                     valid_rows, sh.nsl)
+    switch (sh.cpl) {
+      case 1: LS(1); break;
+      case 2: LS(2); break;
+      case 3: LS(3); break;
+      default: LS(4); break;
+    }
+#undef LS
+    return hipGetLastError();
+  }
+  const int* cnt;
+  const int* list;
+  const hipError_t e = launch_token_lists(ti, T, a, valid_rows, workspace, &cnt, &list, stream);
+  if (e != hipSuccess) return e;
 #define L(C)                                                                            \
   hipLaunchKernelGGL(scatter_csr_kernel<C>, grid, block, 0, stream, out, T, in, cnt, list, \
                      D, sh.nsl)

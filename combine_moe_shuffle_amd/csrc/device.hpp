@@ -142,4 +142,40 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // Uniform (scalar) copy of a wave-uniform value.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Number of set bits of m below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+}
+
+// The rows r < V with token index t, found by the wave itself: tv[c] holds
+// token_indices[64c + lane] (-1 from V on). Chunk by chunk a ballot marks the
+// token's rows, which are staged in this wave's 64 LDS words in ascending
+// order and handed to batch(rows, n) up to 64 at a time (lane i of `rows`
+// holds the batch's i-th row; lanes from n on hold no row). Returns the
+// number of rows. V and t are wave-uniform.
+template <int NC, class F>
+__device__ __forceinline__ int for_token_rows(const int (&tv)[NC], int V, int t, int lane,
+                                              int* __restrict__ stage, F&& batch) {
+  int cnt = 0;
+  int total = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c * kWave >= V) break;
+    const bool hit = tv[c] == t;
+    const uint64_t m = __ballot(hit);
+    const int nb = __popcll(m);
+    if (nb == 0) continue;
+    if (cnt + nb > kWave) {
+      batch(stage[lane], cnt);
+      cnt = 0;
+    }
+    if (hit) stage[cnt + lanes_below(m)] = c * kWave + lane;
+    cnt += nb;
+    total += nb;
+  }
+  if (cnt) batch(stage[lane], cnt);
+  return total;
+}
+
 }  // namespace moe

@@ -4,14 +4,17 @@
 // [GS] "mslk/moe/gather_scatter.py": gather_scale_dense_tokens,
 // gather_scale_quant_dense_tokens and their kernels.
 //
-// All three kernels stream rows in the slice layout of launch.hpp: each wave
-// owns 64*cpl 16-byte chunks of one row, one 1 KiB contiguous access per
+// The kernels stream rows in the slice layout of launch.hpp: each wave owns
+// 64*cpl 16-byte chunks of one row, one 1 KiB contiguous access per
 // instruction. Per-row indices and the score are wave-uniform scalar loads.
 //
 //  gather_rows    one (output row, slice) per wave, output-row order.
 //  gather_tokens  one (token, slice) per wave: the token's slice is loaded
 //                 once and written to each of its K rows through the inverse
 //                 map, so x is read from memory once however large K is.
+//  gather_lists   the same from token_indices, through per-token row lists
+//                 built first; gather_scan, for up to 1024 rows, has each
+//                 wave find its token's rows itself instead.
 //  quant_rows     one output row per workgroup (its slices spread over the
 //                 waves); the row stays in registers between the row-max
 //                 reduction (wave max + LDS across waves) and the quantising
@@ -202,6 +205,46 @@ __global__ __launch_bounds__(kRowWaves* kWave) void gather_lists_kernel(
   }
 }
 
+// Small general gathers (up to kScanRows rows): each (token, slice) wave
+// finds its token's rows itself (for_token_rows), with no row-list build and
+// so no launch before it, and writes them up to 64 at a time as
+// gather_lists_kernel does.
+constexpr int kScanRows = 1024;
+constexpr int kScanChunks = kScanRows / kWave;
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void gather_scan_kernel(
+    const uint16_t* __restrict__ x, int T, int E, int D, const int* __restrict__ ti,
+    const int* __restrict__ ei, int a, const float* __restrict__ scores, int64_t st,
+    int64_t se, const int* __restrict__ vrows, uint16_t* __restrict__ out, int nsl) {
+  __shared__ int stage[kRowWaves][kWave];
+  const int lane = lane_id();
+  const int wv = uniform(threadIdx.x >> 6);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRowWaves + wv;
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int V = clamp_count(vrows, a);
+  int tv[kScanChunks];
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c) {
+    const int r = c * kWave + lane;
+    tv[c] = r < V ? ti[r] : -1;
+  }
+  const int nch = D >> 3;
+  const uint16_t* src = x + static_cast<int64_t>(t) * D;
+  const float* srow = scores + static_cast<int64_t>(t) * st;
+  const int slice0 = sl * kWave * CPL;
+  const bool full = slice0 + kWave * CPL <= nch;
+  for_token_rows(tv, V, t, lane, stage[wv], [&](int rows, int nb) {
+    const int my_r = lane < nb ? rows : -1;
+    const uint64_t valid = __ballot(my_r >= 0);
+    if (full)
+      gather_token<CPL, true>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
+    else
+      gather_token<CPL, false>(src, out, D, srow, se, ei, E, my_r, valid, slice0 + lane, nch);
+  });
+}
+
 constexpr float kRowwiseEps = 1e-12f;
 
 template <int CPL>
@@ -317,14 +360,23 @@ hipError_t launch_gather_scale(const uint16_t* x, int T, int D, const int* ti,
   const SliceShape sh = stream_shape(D / kChunk);
   if (workspace) {
     // token order: each x row read once, written to its rows through a CSR
-    // of token_indices built in the workspace
+    // of token_indices built in the workspace, or for small inputs found by
+    // each wave itself
+    const int64_t tunits = static_cast<int64_t>(T) * sh.nsl;
+    const dim3 tgrid(static_cast<unsigned>((tunits + kRowWaves - 1) / kRowWaves));
+    if (a <= kScanRows) {
+#define LS(C)                                                                              \
+  hipLaunchKernelGGL(gather_scan_kernel<C>, tgrid, dim3(kRowWaves * kWave), 0, stream, x, T, \
+                     E, D, ti, ei, a, scores, st, se, valid_rows, out, sh.nsl)
+      MOE_DISPATCH_CPL(sh.cpl, LS)
+#undef LS
+      return hipGetLastError();
+    }
     const int* start;
     const int* list;
     const hipError_t e = launch_token_lists(ti, T, a, valid_rows, workspace, &start, &list,
                                             stream);
     if (e != hipSuccess) return e;
-    const int64_t tunits = static_cast<int64_t>(T) * sh.nsl;
-    const dim3 tgrid(static_cast<unsigned>((tunits + kRowWaves - 1) / kRowWaves));
 #define LT(C)                                                                              \
   hipLaunchKernelGGL(gather_lists_kernel<C>, tgrid, dim3(kRowWaves * kWave), 0, stream, x, T, \
                      E, D, start, list, ei, scores, st, se, out, sh.nsl)
