@@ -4,14 +4,16 @@
 // steps 2 and 3 in one launch; one for up to 32 tokens, or 64 with short
 // top-k rounds, where shuffle_small_kernel does all three in one workgroup):
 //
-//  1. select_rank  (one workgroup per 32 tokens, 16 waves): each wave takes
-//     the top-k of two tokens at once, the expert axis spread over its 64
-//     lanes (K rounds of a DPP wave max over order-preserving score keys, the
-//     lowest tied lane holding the lowest expert id; the two reductions
-//     interleave so their lane-exchange latencies overlap). The workgroup then ORs one bit per
-//     token into a 32-bit LDS mask per expert; a pair's rank inside its
-//     workgroup and expert is the popcount of the mask bits of the tokens
-//     before it, the workgroup's per-expert count the mask's popcount.
+//  1. select_rank  (one workgroup of 16 waves per block of 32 tokens, or of
+//     16 tokens for batches of up to 128): each wave takes the top-k of its
+//     two tokens (or one) at once, the expert axis spread over its 64 lanes
+//     (K rounds of a DPP wave max over order-preserving score keys, the
+//     lowest tied lane holding the lowest expert id; two reductions
+//     interleave so their lane-exchange latencies overlap). The workgroup
+//     then ORs one bit per token into a 32-bit LDS mask per expert; a pair's
+//     rank inside its workgroup and expert is the popcount of the mask bits
+//     of the tokens before it, the workgroup's per-expert count the mask's
+//     popcount.
 //     Writes (expert | rank << 16) per pair and the [E][blocks] histogram.
 //  2. expert_scan  (one wave per expert): exclusive scan of the expert's row
 //     of the histogram over blocks, in place; its total is counts[e].
@@ -182,8 +184,10 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ scores, int6
     if (live[q] && lane < K) sel[(wave + q * nwaves) * K + lane] = mine[q];
 }
 
-// PL = expert candidates per lane (E <= 64 * PL).
-template <int PL>
+// PL = expert candidates per lane (E <= 64 * PL); TPW = tokens per wave, so
+// a block is 16 * TPW tokens (32, or 16 for small batches: one token per
+// wave, half the top-k rounds on each wave's path).
+template <int PL, int TPW>
 __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
     const float* __restrict__ scores, int64_t st, int64_t se, int T, int E, int K,
     const int* __restrict__ vtc_ptr, int* __restrict__ pair, int* __restrict__ hist,
@@ -191,8 +195,10 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
   __shared__ uint32_t mask[kMaxE];
   __shared__ int sel[kTokPerBlock * kMaxK];
 
+  constexpr int kTpb = TPW * (kSelThreads / kWave);
+  static_assert(kTpb <= kTokPerBlock, "one bit per token in a 32-bit mask");
   const int blk = blockIdx.x;
-  const int t0 = blk * kTokPerBlock;
+  const int t0 = blk * kTpb;
   const int vtc = clamp_count(vtc_ptr, T);
   const int lane = lane_id();
   const int wave = uniform(threadIdx.x >> 6);
@@ -201,12 +207,11 @@ __global__ __launch_bounds__(kSelThreads) void select_rank_kernel(
   for (int e = threadIdx.x; e < E; e += kSelThreads) mask[e] = 0u;
 
   // ---- top-k: wave w owns tokens w and w+16 of the workgroup
-  wave_topk<PL, kTokPerBlock / (kSelThreads / kWave)>(scores, st, se, E, K, vtc, t0, wave,
-                                                       nwaves, lane, sel);
+  wave_topk<PL, TPW>(scores, st, se, E, K, vtc, t0, wave, nwaves, lane, sel);
   __syncthreads();
 
   // ---- one bit per valid token in each of its experts' masks
-  const int npairs = kTokPerBlock * K;
+  const int npairs = kTpb * K;
   for (int p = threadIdx.x; p < npairs; p += kSelThreads) {
     const int tl = p / K;
     if (t0 + tl < vtc) atomicOr(&mask[sel[p]], 1u << tl);
@@ -347,9 +352,9 @@ __global__ __launch_bounds__(kScanWaves* kWave) void expert_scan_kernel(
 
 constexpr int kPlaceThreads = 256;
 __global__ __launch_bounds__(kPlaceThreads) void place_kernel(
-    const int* __restrict__ pair, const int* __restrict__ offs, int nblk, int T, int E, int K,
-    const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
-    int* __restrict__ ei, int* __restrict__ rop) {
+    const int* __restrict__ pair, const int* __restrict__ offs, int nblk, int blk_shift, int T,
+    int E, int K, const int* __restrict__ vtc_ptr, int* __restrict__ counts,
+    int* __restrict__ ti, int* __restrict__ ei, int* __restrict__ rop) {
   __shared__ int first[kMaxE];
   __shared__ int wave_tot[kPlaceThreads / kWave];
   const int tid = threadIdx.x;
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(kPlaceThreads) void place_kernel(
   const int v = (have && t < vtc) ? pair[p] : 0;
   const int e = v & 0xFFFF;
   const int rank = v >> 16;
-  const int off = (have && t < vtc) ? offs[static_cast<int64_t>(e) * nblk + t / kTokPerBlock] : 0;
+  const int off = (have && t < vtc) ? offs[static_cast<int64_t>(e) * nblk + (t >> blk_shift)] : 0;
 
   // first[e] = sum of counts[e'] for e' < e: each thread scans E/256 counts,
   // then waves and workgroup combine (E <= 1024 -> at most 4 per thread)
@@ -423,9 +428,9 @@ constexpr int kFuseHist = kPlaceThreads * kFusePer;  // 8192
 __device__ __forceinline__ int fuse_pad(int i) { return i + (i >> 5); }
 
 __global__ __launch_bounds__(kPlaceThreads) void scan_place_kernel(
-    const int* __restrict__ pair, const int* __restrict__ hist, int nblk, int T, int E, int K,
-    const int* __restrict__ vtc_ptr, int* __restrict__ counts, int* __restrict__ ti,
-    int* __restrict__ ei, int* __restrict__ rop) {
+    const int* __restrict__ pair, const int* __restrict__ hist, int nblk, int blk_shift, int T,
+    int E, int K, const int* __restrict__ vtc_ptr, int* __restrict__ counts,
+    int* __restrict__ ti, int* __restrict__ ei, int* __restrict__ rop) {
   __shared__ int pre[kFuseHist + kFuseHist / 32 + 1];
   __shared__ int wave_tot[kPlaceThreads / kWave];
   const int tid = threadIdx.x;
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(kPlaceThreads) void scan_place_kernel(
   }
   if (!have) return;
   if (t < vtc) {
-    const int r = pre[fuse_pad(e * nblk + t / kTokPerBlock)] + rank;
+    const int r = pre[fuse_pad(e * nblk + (t >> blk_shift))] + rank;
     ti[r] = t;
     ei[r] = e;
     if (rop) rop[p] = r;
@@ -509,8 +514,13 @@ size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
 
+// Tokens per top-k block: 16 (one per wave) for batches of up to kHalfBlockT
+// tokens, whose few blocks are latency-bound, else 32.
+constexpr int kHalfBlockT = 128;
+static int block_shift(int T) { return T <= kHalfBlockT ? 4 : 5; }
+
 size_t shuffle_workspace_bytes(int T, int E, int K) {
-  const int nblk = (T + kTokPerBlock - 1) / kTokPerBlock;
+  const int nblk = (T + (1 << block_shift(T)) - 1) >> block_shift(T);
   return align256(static_cast<size_t>(T) * K * sizeof(int)) +
          align256(static_cast<size_t>(E) * nblk * sizeof(int));
 }
@@ -564,33 +574,40 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
 #undef MOE_SMALL
     return hipGetLastError();
   }
-  const int nblk = (T + kTokPerBlock - 1) / kTokPerBlock;
+  const int bs = block_shift(T);
+  const int nblk = (T + (1 << bs) - 1) >> bs;
   char* ws = static_cast<char*>(workspace);
   int* pair = reinterpret_cast<int*>(ws);
   int* hist = reinterpret_cast<int*>(ws + align256(static_cast<size_t>(T) * K * sizeof(int)));
   const int pl = (E + kWave - 1) / kWave;
   const dim3 g1(nblk), b1(kSelThreads);
-#define MOE_SEL(PLV)                                                                     \
-  hipLaunchKernelGGL(select_rank_kernel<PLV>, g1, b1, 0, stream, scores, st, se, T, E, K, \
-                     vtc, pair, hist, nblk)
+#define MOE_SEL2(PLV, TPWV)                                                                 \
+  hipLaunchKernelGGL((select_rank_kernel<PLV, TPWV>), g1, b1, 0, stream, scores, st, se, T, \
+                     E, K, vtc, pair, hist, nblk)
+#define MOE_SEL(PLV)                       \
+  do {                                     \
+    if (bs == 4) MOE_SEL2(PLV, 1);         \
+    else MOE_SEL2(PLV, 2);                 \
+  } while (0)
   if (pl <= 1) MOE_SEL(1);
   else if (pl <= 2) MOE_SEL(2);
   else if (pl <= 4) MOE_SEL(4);
   else if (pl <= 8) MOE_SEL(8);
   else MOE_SEL(16);
 #undef MOE_SEL
+#undef MOE_SEL2
   const int64_t npairs = static_cast<int64_t>(T) * K;
   const int pblocks = static_cast<int>((npairs + kPlaceThreads - 1) / kPlaceThreads);
   if (static_cast<int64_t>(E) * nblk <= kFuseHist) {
     hipLaunchKernelGGL(scan_place_kernel, dim3(pblocks), dim3(kPlaceThreads), 0, stream, pair,
-                       hist, nblk, T, E, K, vtc, counts, token_indices, expert_indices,
+                       hist, nblk, bs, T, E, K, vtc, counts, token_indices, expert_indices,
                        row_of_pair);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kScanWaves - 1) / kScanWaves),
                      dim3(kScanWaves * kWave), 0, stream, hist, E, nblk, counts);
   hipLaunchKernelGGL(place_kernel, dim3(pblocks), dim3(kPlaceThreads), 0, stream, pair, hist,
-                     nblk, T, E, K, vtc, counts, token_indices, expert_indices, row_of_pair);
+                     nblk, bs, T, E, K, vtc, counts, token_indices, expert_indices, row_of_pair);
   return hipGetLastError();
 }
 
