@@ -77,7 +77,7 @@ def test_workspace_sizes(lib):
     assert lib.moe_shuffle_workspace_bytes(8192, 256, 8) == 8192 * 8 * 4 + 256 * 256 * 4
     assert lib.moe_shuffle_workspace_bytes(65, 3, 2) == 768 + 256
     assert lib.moe_shuffle_workspace_bytes(100, 256, 8) == 3328 + 256 * 7 * 4
-    assert lib.moe_shuffle_workspace_bytes(129, 256, 8) == 129 * 8 * 4 + 256 * 5 * 4
+    assert lib.moe_shuffle_workspace_bytes(129, 256, 8) == 4352 + 256 * 5 * 4  # 4128 aligned
     assert lib.moe_shuffle_workspace_bytes(-1, 3, 2) == 0
     # scatter: (T+1) starts + a list entries, then (a <= 131072 rows, at most
     # 2048 ranges of 128 tokens) a (row, token) pairs and two [range][chunk of
