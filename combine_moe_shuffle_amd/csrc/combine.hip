@@ -759,6 +759,81 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_kernel(
   }
 }
 
+// Small padded combines (T_K <= kScanRows): no row-list build. Each
+// workgroup scans the expert counts into an LDS prefix; each (token, slice)
+// wave then finds its token's rows among the first V = prefix[E] as the
+// general scan combine does, and reads each from its owner rank's slab.
+template <int CPL, bool FULL>
+__device__ __forceinline__ void padded_scan_reduce(uint16_t* __restrict__ orow,
+                                                   const uint16_t* __restrict__ in, int T_K,
+                                                   const int* pre, int E, int epr,
+                                                   const int (&tv)[kScanChunks], int V, int t,
+                                                   int D, int nch, int base, int lane,
+                                                   int* stage) {
+  float acc[CPL][8];
+  load_acc<CPL, FULL>(acc, orow, nch, base);
+  const int n = for_token_rows(tv, V, t, lane, stage, [&](int rows, int nb) {
+    const int src = lane < nb ? rank_of_row(pre, E, epr, rows) * T_K + rows : 0;
+    add_rows<CPL, kScanG, FULL>(acc, in, D, nch, base, src, nb);
+  });
+  if (n) store_acc<CPL, FULL>(acc, orow, nch, base);
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_scan_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in, int T_K,
+    const int* __restrict__ counts, int E, int EP, const int* __restrict__ ti, int D,
+    int nsl) {
+  constexpr int NT = kRowWaves * kWave;
+  constexpr int kPer = (kMaxPaddedE + NT - 1) / NT;
+  __shared__ int pre[kMaxPaddedE + 1];
+  __shared__ int wave_tot[kRowWaves];
+  __shared__ int stage[kRowWaves][kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = uniform(tid >> 6);
+  // prefix of the counts: thread i owns experts [i*kPer, i*kPer + kPer)
+  int c[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int e = tid * kPer + q;
+    c[q] = e < E ? max(counts[e], 0) : 0;
+    mine += c[q];
+  }
+  int total;
+  int ex = block_excl_scan<NT>(mine, lane, wv, wave_tot, total);  // syncs
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int e = tid * kPer + q;
+    if (e < E) pre[e] = min(ex, T_K);
+    ex += c[q];
+  }
+  if (tid == 0) pre[E] = min(total, T_K);
+  __syncthreads();
+
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRowWaves + wv;
+  const int t = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(t) * nsl);
+  if (t >= T) return;
+  const int V = pre[E];
+  int tv[kScanChunks];
+#pragma unroll
+  for (int q = 0; q < kScanChunks; ++q) {
+    const int r = q * kWave + lane;
+    tv[q] = r < V ? ti[r] : -1;
+  }
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  if (slice0 + kWave * CPL <= nch)
+    padded_scan_reduce<CPL, true>(orow, in, T_K, pre, E, E / EP, tv, V, t, D, nch,
+                                  slice0 + lane, lane, stage[wv]);
+  else
+    padded_scan_reduce<CPL, false>(orow, in, T_K, pre, E, E / EP, tv, V, t, D, nch,
+                                   slice0 + lane, lane, stage[wv]);
+}
+
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 SliceShape combine_shape(int nch) {
@@ -830,6 +905,22 @@ void csr_two_launch(const int* ti, int T, int a, const int* valid_rows, const in
 hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const int* counts,
                                      int E, const int* ti, uint16_t* out, int T, int D,
                                      void* workspace, hipStream_t stream) {
+  if (T_K <= kScanRows) {  // each wave finds its token's rows: no build
+    const SliceShape sh = combine_shape(D / kChunk);
+    const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+    const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
+#define LS(C)                                                                             \
+  hipLaunchKernelGGL(scatter_padded_scan_kernel<C>, grid, dim3(kRowWaves * kWave), 0, stream, \
+                     out, T, in, T_K, counts, E, EP, ti, D, sh.nsl)
+    switch (sh.cpl) {
+      case 1: LS(1); break;
+      case 2: LS(2); break;
+      case 3: LS(3); break;
+      default: LS(4); break;
+    }
+#undef LS
+    return hipGetLastError();
+  }
   char* ws = static_cast<char*>(workspace);
   int* prefix = reinterpret_cast<int*>(ws);
   ws += align256((static_cast<size_t>(E) + 1) * sizeof(int));
