@@ -477,6 +477,93 @@ def test_scatter_add_csr_stage_overflow(dev):
     assert np.array_equal(bits_host(out), want)
 
 
+@pytest.mark.parametrize("a", [600, 2000, 6000])
+def test_out_of_range_indices_are_skipped(dev, a):
+    """Token, expert and slot indices out of range (negative, or past T, E, V
+    or rows) are preconditions the kernels check before addressing memory:
+    such a row or slot is skipped. Valid rows equal the oracle on the input
+    with the bad rows dropped; rows with a bad index are left unwritten.
+    a = 600, 2000, 6000 take the per-wave row search, the one-workgroup build
+    and the two-launch build of the token_indices paths."""
+    g = np.random.default_rng(a)
+    T, D, E, K = 50, 64, 8, 4
+    V = a - 37
+    ti = g.integers(0, T, size=a).astype(np.int32)
+    ei = g.integers(0, E, size=a).astype(np.int32)
+    bad_t = g.random(a) < 0.1
+    ti[bad_t] = np.where(g.random(int(bad_t.sum())) < 0.5, -3, T + 7)
+    bad_e = g.random(a) < 0.05
+    ei[bad_e] = np.where(g.random(int(bad_e.sum())) < 0.5, -1, E + 2)
+    x = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    s = g.standard_normal((T, E)).astype(np.float32)
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("out-of-range indices", a, int(bad_t.sum()), int(bad_e.sum()))
+    ok_rows = (np.arange(a) < V) & ~bad_t & ~bad_e
+    # gather: the valid rows as the oracle computes them, the others untouched
+    want_rows = orc.gather_scale(x, np.where(ok_rows, ti, 0).astype(np.int32),
+                                 np.where(ok_rows, ei, 0).astype(np.int32), s, V,
+                                 np.full((a, D), SENTINEL, np.uint16))
+    want_rows[~ok_rows] = SENTINEL
+    for row_order in (False, True):
+        rows = bf_dev(np.full((a, D), SENTINEL, np.uint16), dev)
+        ops.moe_gather_scale(bf_dev(x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                             torch.from_numpy(s).to(dev), scalar_dev(V, dev), out=rows,
+                             row_order=row_order)
+        assert np.array_equal(bits_host(rows), want_rows), row_order
+    q, qs = ops.moe_gather_scale_quant(bf_dev(x, dev), i32_dev(ti, dev), i32_dev(ei, dev),
+                                       torch.from_numpy(s).to(dev), None, scalar_dev(V, dev))
+    wq, wqs = orc.gather_scale_quant(x, np.where(ok_rows, ti, 0).astype(np.int32),
+                                     np.where(ok_rows, ei, 0).astype(np.int32), s, None, V)
+    assert np.array_equal(q.cpu().numpy()[ok_rows], wq[ok_rows])
+    assert np.array_equal(qs.cpu().numpy()[ok_rows], wqs[ok_rows])
+    # general combine: a row with a bad token adds nothing (expert ids unused)
+    keep = (np.arange(a) < V) & ~bad_t
+    want = orc.scatter_add(out0.copy(), np.ascontiguousarray(y[keep]),
+                           np.ascontiguousarray(ti[keep]))
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add(out, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    # by-token paths and the finalize: slots outside [0, V) (and past the rows)
+    rop = g.permutation(V)[:T * K].reshape(T, K).astype(np.int32)  # no row twice
+    bad = g.random((T, K)) < 0.15
+    rop[bad] = g.choice(np.array([-1, -9, V, V + 3, a + 100], np.int32), size=int(bad.sum()))
+    okp = (rop >= 0) & (rop < V)
+    rows = bf_dev(np.full((a, D), SENTINEL, np.uint16), dev)
+    ops.moe_gather_scale_by_token(bf_dev(x, dev), i32_dev(rop, dev), i32_dev(ei, dev),
+                                  torch.from_numpy(s).to(dev), scalar_dev(V, dev), rows)
+    got = bits_host(rows)
+    tt, kk = np.nonzero(okp)
+    for t_, r_ in zip(tt, rop[okp]):
+        e_ = ei[r_]
+        if 0 <= e_ < E:
+            w1 = orc.gather_scale(x, np.array([t_], np.int32), np.array([e_], np.int32), s, 1)
+            assert np.array_equal(got[r_], w1[0]), (t_, r_)
+    touched = np.zeros(a, bool)
+    touched[rop[okp]] = True
+    assert np.all(got[~touched] == SENTINEL)
+    # by-token combine: each token adds its valid slots' rows in ascending order
+    want = out0.copy()
+    for t_ in range(T):
+        rr = np.sort(rop[t_][okp[t_]])
+        if rr.size:
+            want[t_] = orc.scatter_add(out0[t_:t_ + 1].copy(), np.ascontiguousarray(y[rr]),
+                                       np.zeros(rr.size, np.int32))[0]
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_by_token(out, bf_dev(y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    # finalize: a slot past the permuted rows is not held
+    rop_f = rop.copy()
+    rop_f[rop_f >= a] = a + 5
+    w = g.random((T, K)).astype(np.float32)
+    gamma = W.to_bf16_bits(g.uniform(0.5, 1.5, D).astype(np.float32))
+    want_o = orc.finalize_rmsnorm(y, w, np.where((rop_f >= 0) & (rop_f < a), rop_f, -1)
+                                  .astype(np.int32), None, gamma, 1e-6)
+    o = ops.moe_finalize_rmsnorm(bf_dev(y, dev), torch.from_numpy(w).to(dev),
+                                 i32_dev(rop_f, dev), None, bf_dev(gamma, dev), 1e-6)
+    _close(bits_host(o), want_o, "finalize, slots past the rows")
+
+
 @pytest.mark.parametrize("T,a", [(4096, 4096), (1, 4096), (4097, 300), (300, 4097)])
 def test_csr_small_build_limits(dev, T, a):
     """The one-workgroup row-list build (up to 4096 rows and 4096 tokens) at its
