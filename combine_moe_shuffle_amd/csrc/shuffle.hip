@@ -535,11 +535,12 @@ hipError_t launch_shuffle(const float* scores, int64_t st, int64_t se, int T, in
     return hipGetLastError();
   }
   constexpr int kWaves = kSelThreads / kWave;
-  // Up to 32 tokens a wave holds at most two, as in the block kernel, so one
-  // launch costs no more top-k rounds than two. From 33 to 64 tokens a wave
-  // holds four: the two extra tokens' K rounds (longer with more candidates
-  // per lane) outweigh the launch saved once K * candidates per lane is above
-  // 8 (E = 256, K = 8 at 64 tokens: 9.3 us in one launch, 8.6 us in two).
+  // Up to 32 tokens a wave holds at most two, and one launch beats two (E =
+  // 256, K = 8: 6.1 us at 32 tokens against 7.7 us for two launches at 64).
+  // From 33 to 64 tokens a wave would hold four: the extra tokens' K rounds
+  // (longer with more candidates per lane) outweigh the launch saved once
+  // K * candidates per lane is above 8 (at 64 tokens: 9.3 us in one launch,
+  // 7.7 us in two with 16-token blocks).
   const int pl_all = (E + kWave - 1) / kWave;
   if (T <= kSmallT / 2 || (T <= kSmallT && E <= kSmallWideE && K * pl_all <= 8)) {
     // one token per wave up to 16 tokens: as many waves as tokens
