@@ -254,10 +254,11 @@ def moe_gather_scale(x, token_indices, expert_indices, scores, valid_rows=None, 
     """out[i] = bf16(x[token_indices[i]] * scores[t, expert_indices[i]]) for
     i < valid_rows; other rows of ``out`` are left as they are.
 
-    By default the rows are visited token by token through a list of each
-    token's rows built in ``workspace`` (allocated when None), reading each x
-    row once; ``row_order=True`` visits them row by row with no workspace.
-    Both give the same bits."""
+    By default the rows are visited token by token, reading each x row once:
+    up to 1024 rows each token's rows are found directly, beyond that through
+    a list of each token's rows built in ``workspace`` (allocated when None,
+    as the library requires it either way); ``row_order=True`` visits them
+    row by row with no workspace. All give the same bits."""
     device, st, se, vr = _gather_common(x, expert_indices, scores, valid_rows)
     _need(token_indices, "token_indices", torch.int32, 1, device)
     _contig(token_indices, "token_indices")

@@ -172,11 +172,13 @@ MOE_API moe_status_t moe_shuffle_noalloc(const float *scores, int64_t stride_t,
  * whose t or e is out of range.
  *
  * With a workspace (>= moe_gather_scale_workspace_bytes(T, a) bytes,
- * 256-byte aligned) the rows are visited token by token through a list of
- * each token's rows built there (one extra launch; four when a > 131072), so
- * each row of x is read from memory once; with workspace == NULL, row by row
- * (x re-read once per row that uses it). The output is the same bit for bit.
- * The workspace is scratch: its contents on entry do not matter.
+ * 256-byte aligned) the rows are visited token by token, so each row of x is
+ * read from memory once: up to 1024 rows each token's rows are found
+ * directly; beyond that through a list of each token's rows built in the
+ * workspace first (one extra launch up to 4096 rows and tokens, two up to
+ * 131072 rows, four beyond). With workspace == NULL, row by row (x re-read
+ * once per row that uses it). The output is the same bit for bit. The
+ * workspace is scratch: its contents on entry do not matter.
  *
  * x     [T, D] bf16;  out [a, D] bf16;  token_indices, expert_indices [a] int32
  * D % 8 == 0.
@@ -244,8 +246,10 @@ MOE_API moe_status_t moe_gather_scale_quant(const moe_bf16_t *x, int32_t T, int3
  * out_tokens [T, D] bf16 in/out;  in_tokens [a, D] bf16;  token_indices [a]
  * valid_rows nullable device int32 scalar (V, clamped to [0, a])
  * workspace  >= moe_scatter_add_workspace_bytes(T, a) bytes, 256-byte aligned
- * D % 8 == 0. Tokens routed to more than 64 valid rows take a slower
- * (quadratic in that count) ordering step; the result is the same.
+ * D % 8 == 0. Up to 1024 rows each token's rows are found directly (one
+ * launch); beyond that a list of each token's rows is built in the workspace
+ * first, and tokens routed to more than 64 valid rows take a slower
+ * (quadratic in that count) ordering step. The result is the same.
  * ---------------------------------------------------------------------- */
 MOE_API size_t moe_scatter_add_workspace_bytes(int32_t T, int32_t a);
 MOE_API moe_status_t moe_scatter_add(moe_bf16_t *out_tokens, int32_t T,
