@@ -938,15 +938,18 @@ def test_graph_replay_matches_eager(dev):
             assert torch.equal(got[k], v), (rep, k)
 
 
-def test_graph_replay_general_paths(dev):
+@pytest.mark.parametrize("T", [300, 100])
+def test_graph_replay_general_paths(dev, T):
     """The entry points the first graph test leaves out, captured in one HIP
     graph with caller workspaces: the shuffle that allocates nothing, the
-    general gather (two-launch row-list build), the FP8 rowwise gather, the
+    general gather (token order), the FP8 rowwise gather, the
     general and padded combines, and the EP re-sort both ways. Every replay,
     with the outputs spoiled by eager work in between, equals the eager run
-    bit for bit."""
+    bit for bit. T = 300 (1200 rows) builds row lists in one workgroup;
+    T = 100 (400 rows) takes the per-wave row search and the shuffle's
+    16-token blocks."""
     wl = W.WORKLOADS["zipf"]
-    T, D, E, K, vtc, EP = 300, 512, 16, 4, 250, 4
+    D, E, K, vtc, EP = 512, 16, 4, T - 50, 4
     inp = W.dispatch_inputs(wl, T=T, D=D, E=E, K=K, vtc=vtc, out0="normal")
     a = T * K
     g = np.random.default_rng(31)
