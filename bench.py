@@ -51,6 +51,12 @@ An event between two kernels costs the stream ~10 us, so no region records
 one inside. The longest stage is the roofline kernel: its algorithmic bytes
 per launch (unique inputs read once, outputs written once, valid rows only)
 over that duration, against the 8 TB/s HBM peak.
+4. "stream_ceiling": the roofline kernel's row bytes in the same read:write
+   mix, moved by a plain contiguous stream (moe_stream_probe: each wave reads R
+   consecutive KiB and writes W, consecutive waves on consecutive memory),
+   timed as in 3 and after a read flush as in 2: the rate that mix reaches on
+   this GPU in the most favourable order, and the kernel's rate as a fraction
+   of it (--no-ceiling skips it).
 
 One JSON line on stdout. value = valid tokens (routed rows for padded and
 shuffling) per second of the whole step. cpu_baseline = the CPU oracle
@@ -101,6 +107,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="replay a HIP graph of the step instead of launching its kernels from "
                         "Python (a graph launch costs more than a few kernel launches here)")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the contiguous-stream probe timed beside the roofline kernel")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="after the timed region, run one plain device copy of this many "
                         "bytes (the calibration kernel of the HBM counter runs)")
@@ -209,6 +217,23 @@ def shuffling_bytes(rows, D, EP, EG):
     return 2 * rows * D * 2 + EP * EG * 4 + (EG + 1) * 4
 
 
+def stream_mix(read_kib, write_kib):
+    """(R, W, units) of the contiguous-stream probe that moves read_kib KiB in
+    and write_kib KiB out: the smallest R:W (each <= 32) equal to the
+    kernel's read:write ratio, units = write_kib / W; None when the byte
+    counts are not whole KiB or no such R, W exist."""
+    from math import gcd
+    if read_kib <= 0 or write_kib <= 0 or read_kib != int(read_kib) or \
+            write_kib != int(write_kib):
+        return None
+    read_kib, write_kib = int(read_kib), int(write_kib)
+    g = gcd(read_kib, write_kib)
+    R, Wm = read_kib // g, write_kib // g
+    if R > 32 or Wm > 32:
+        return None
+    return (R, Wm, write_kib // Wm)
+
+
 # ------------------------------------------------------------------ workloads
 def setup_dispatch(ctx, wl, with_cpu, general=False):
     """general: gather and scatter through the entry points that take
@@ -265,6 +290,11 @@ def setup_dispatch(ctx, wl, with_cpu, general=False):
             ops.moe_scatter_add_by_token(out, y, rop, vr)
 
     name = wl.name + ("-general" if general else "")
+    # the row bytes of gather and scatter (indices and scores left out)
+    tok_kib = vtc * D * 2 / 1024
+    ceiling = {"gather": stream_mix(2 * V * D / 1024, V * D / 1024) if quant else
+               stream_mix(tok_kib, K * tok_kib),
+               "scatter": stream_mix((K + 1) * tok_kib, tok_kib)}
     stage_names = (("gather_scale_quant", "scatter_add_by_token") if quant else
                    ("gather_scale (token_indices, workspace)", "scatter_add (token_indices)")
                    if general else ("gather_scale_by_token", "scatter_add_by_token"))
@@ -276,7 +306,7 @@ def setup_dispatch(ctx, wl, with_cpu, general=False):
                 "tokens": T, "hidden": D, "experts": E, "top_k": K,
                 "valid_token_count": vtc, "routed_rows": V,
                 "stages": "shuffle -> " + " -> ".join(stage_names)},
-        traffic_key=name,
+        traffic_key=name, ceiling=ceiling,
         dtype="bf16" if not quant else "bf16->fp8e4m3",
         kernel_src={"shuffle": ["shuffle.hip"],
                     # the general gather builds its row lists with combine.hip's kernel
@@ -311,6 +341,8 @@ def setup_finalize(ctx, wl, with_cpu, variant=False, T=None):
 
     fin_bytes = finalize_bytes(T, D, K, sbytes if mx else None, bf16_weights=variant)
     name = wl.name + ("-swizzled" if variant else "")
+    row_kib = T * D * 2 / 1024  # expert and shared rows in, bf16 rows (and codes) out
+    ceiling = {"finalize": stream_mix((K + 1) * row_kib, row_kib * (1.5 if mx else 1))}
     return SimpleNamespace(
         stages={"finalize": finalize}, stage_bytes={"finalize": fin_bytes},
         units_per_step=T, unit="tokens/s",
@@ -320,7 +352,7 @@ def setup_finalize(ctx, wl, with_cpu, variant=False, T=None):
                 "tokens": T, "hidden": D, "top_k": K,
                 "stages": "finalize_rmsnorm" + (" + mxfp8" if mx else "")},
         dtype="bf16" if not mx else "bf16->mxfp8", kernel_src={"finalize": ["finalize.hip"]},
-        traffic_key=name,
+        traffic_key=name, ceiling=ceiling,
         cpu=cpu_baseline_finalize(ctx.orc, fi, wl, w, 2 if variant else 0, name)
         if with_cpu else None)
 
@@ -345,8 +377,10 @@ def setup_mhc(ctx, wl, with_cpu):
                              residual_out=res_out, out=outd, mxfp8=True,
                              scale_layout="swizzled", mx_codes=codes, mx_scales=scales)
 
+    row_kib = T * D * 2 / 1024  # rows in: K experts, shared, hc streams; out: hc, bf16, codes
+    ceiling = {"finalize_mhc": stream_mix((K + 1 + hc) * row_kib, (hc + 1.5) * row_kib)}
     return SimpleNamespace(
-        stages={"finalize_mhc": finalize_mhc},
+        stages={"finalize_mhc": finalize_mhc}, ceiling=ceiling,
         stage_bytes={"finalize_mhc": mhc_bytes(T, D, K, hc, sbytes)},
         units_per_step=T, unit="tokens/s",
         metric="mHC finalize+RMSNorm tokens/s and achieved HBM GB/s (% of peak), 1xMI355X",
@@ -387,8 +421,10 @@ def setup_padded(ctx, wl, with_cpu):
     def padded_scatter():
         ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
 
+    tok_kib = vtc * D * 2 / 1024
     return SimpleNamespace(
         stages={"padded_scatter": padded_scatter},
+        ceiling={"padded_scatter": stream_mix((K + 1) * tok_kib, tok_kib)},
         stage_bytes={"padded_scatter": padded_bytes(D, E, K, vtc)},
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
         config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} EP={EP} "
@@ -425,7 +461,9 @@ def setup_shuffling(ctx, wl, with_cpu):
         ops.moe_split_shuffling(em, counts, 0, EG, None, out=back, workspace=ws_s)
 
     nb = shuffling_bytes(rows, D, EP, EG)
+    mix = stream_mix(rows * D * 2 / 1024, rows * D * 2 / 1024)
     return SimpleNamespace(
+        ceiling={"combine_shuffling": mix, "split_shuffling": mix},
         stages={"combine_shuffling": combine_shuffling, "split_shuffling": split_shuffling},
         stage_bytes={"combine_shuffling": nb, "split_shuffling": nb},
         units_per_step=rows, unit="rows/s",
@@ -564,11 +602,42 @@ def main():
             fn()
         flush_stage()
         cold_stage[n] = (time_region(flush_stage) - t_flush) / steps
-    del flush_buf
     # ---- each stage alone, `steps` launches back to back: its average
     # duration per launch, the denominator of the roofline
     names = [n for n, _ in stages]
     st_ms = {n: stage_ms(torch, fn, steps) for n, fn in stages}
+    dom = max(names, key=lambda n: st_ms[n])
+    # ---- the same read and write bytes as the roofline kernel, streamed in
+    # the most favourable order (consecutive waves on consecutive memory): the
+    # rate that mix reaches on this GPU, timed the same two ways
+    ceiling = None
+    mix = getattr(s, "ceiling", {}).get(dom)
+    if mix and not args.no_ceiling:
+        R, Wm, units = mix
+        p_src = torch.zeros(units * R * 1024, dtype=torch.uint8, device=dev)
+        p_dst = torch.empty(units * Wm * 1024, dtype=torch.uint8, device=dev)
+        probe = ctx.ops.prepare(ctx.ops.moe_stream_probe, R, Wm, units, src=p_src, dst=p_dst)
+        p_bytes = units * (R + Wm) * 1024
+        p_ms = stage_ms(torch, probe, steps)
+        p_gbps = p_bytes / (p_ms * 1e-3) / 1e9
+        k_gbps = s.stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
+        ceiling = {"kernel": dom, "probe": "moe_stream_probe", "R_kib": R, "W_kib": Wm,
+                   "waves": units, "bytes": p_bytes, "us": round(p_ms * 1e3, 2),
+                   "gbps": round(p_gbps, 1), "frac_of_peak": p_gbps / HBM_PEAK_GBPS,
+                   "kernel_vs_probe": k_gbps / p_gbps}
+        if not args.no_cold:
+            def flush_probe():
+                flush_read()
+                probe()
+            flush_probe()
+            pc_ms = (time_region(flush_probe) - t_flush) / steps
+            pc_gbps = p_bytes / (pc_ms * 1e-3) / 1e9
+            kc_gbps = s.stage_bytes[dom] / (cold_stage[dom] * 1e-3) / 1e9
+            ceiling.update({"us_after_read": round(pc_ms * 1e3, 2),
+                            "gbps_after_read": round(pc_gbps, 1),
+                            "kernel_vs_probe_after_read": kc_gbps / pc_gbps})
+        del p_src, p_dst, probe
+    del flush_buf
     if args.copy_bytes > 0:
         n = args.copy_bytes // 2
         src = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -582,7 +651,6 @@ def main():
     # caches); the warm steps when the cold ones were skipped
     ms_step = cold["read"] if "read" in cold else warm_ms
     total_bytes = sum(s.stage_bytes.values())
-    dom = max(names, key=lambda n: st_ms[n])
     achieved = s.stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
     traffic = load_traffic(dom, s.kernel_src[dom], getattr(s, "traffic_key", name))
 
@@ -633,6 +701,7 @@ def main():
                      "duration": "the kernel's average launch duration, launches back to "
                                  "back (what the rocprofv3 kernel trace shows); after a "
                                  "read flush: cold.roofline_frac_after_read"},
+        "stream_ceiling": ceiling,
         "cpu_baseline": s.cpu,
     }
     if name == "decode" and not args.no_sweep:

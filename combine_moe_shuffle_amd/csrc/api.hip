@@ -8,6 +8,7 @@
 
 #include "moe_shuffle.h"
 #include "launch.hpp"
+#include "probe.hpp"
 
 // The workspace of moe_shuffle_noalloc: a static device array, one copy per
 // GPU. In host code `scratch` names a host-side stand-in, never a device
@@ -544,6 +545,27 @@ moe_status_t moe_launch_floor(int32_t kind, int32_t T, int32_t D, const void* sr
   }
   return hip_status(moe::launch_floor(kind, T, D, src, dst, static_cast<hipStream_t>(stream)),
                     "moe_launch_floor");
+}
+
+moe_status_t moe_stream_probe(int32_t R, int32_t W, int64_t units, const void* src, void* dst,
+                              void* stream) {
+  REQUIRE(R >= 1 && R <= moe::kStreamMaxR, MOE_ERR_INVALID_ARG, "R must be in [1, %d] (got %d)",
+          moe::kStreamMaxR, R);
+  REQUIRE(W >= 1 && W <= moe::kStreamMaxW, MOE_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)",
+          moe::kStreamMaxW, W);
+  REQUIRE(units >= 0 && units < (int64_t{1} << 31), MOE_ERR_INVALID_ARG,
+          "units must be in [0, 2^31)");
+  if (units == 0) return ok();
+  REQUIRE(src != nullptr && dst != nullptr, MOE_ERR_INVALID_ARG, "src and dst are required");
+  REQUIRE(aligned(src, 16) && aligned(dst, 16), MOE_ERR_INVALID_ARG,
+          "src and dst must be 16-byte aligned");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + static_cast<uintptr_t>(units) * R * 1024;
+  const uintptr_t d1 = d0 + static_cast<uintptr_t>(units) * W * 1024;
+  REQUIRE(s1 <= d0 || d1 <= s0, MOE_ERR_INVALID_ARG, "src and dst overlap");
+  return hip_status(moe::launch_stream_probe(R, W, units, src, dst,
+                                             static_cast<hipStream_t>(stream)),
+                    "moe_stream_probe");
 }
 
 }  // extern "C"

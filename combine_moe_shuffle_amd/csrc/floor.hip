@@ -1,11 +1,21 @@
+// Measurement aids, timed beside the path's kernels and used by none of them.
+//
 // Latency floors of the finalize's launch: kernels with the finalize's grid
 // and workgroup shape for (T, D) that do (0) nothing, or (1) two dependent
 // 16-byte loads per lane (an index, then the element it points at) and one
 // store. Timed beside the finalize they bound what a one-token-per-workgroup
 // kernel can reach at small T: the launch itself, and the two memory round
 // trips the finalize's slot rows and expert rows take.
+//
+// A contiguous stream with a chosen read:write mix: wave u reads R
+// consecutive KiB and writes W consecutive KiB, consecutive waves on
+// consecutive memory, every row access a nontemporal 16-byte one per lane as
+// in the streaming kernels. With the byte counts of a streaming kernel it
+// gives the rate the same mix reaches in the most favourable order: the
+// ceiling to hold that kernel's rate against, next to the HBM peak.
 #include "device.hpp"
 #include "launch.hpp"
+#include "probe.hpp"
 
 namespace moe {
 
@@ -20,6 +30,30 @@ __global__ __launch_bounds__(1024) void floor_loads_kernel(const u32x4* __restri
   const u32x4 a = src[i];
   const u32x4 b = src[a.x % static_cast<uint32_t>(n)];
   dst[i] = static_cast<int>(b.x + b.y + b.z + b.w);
+}
+
+constexpr int kProbeWaves = 4;
+
+// Each 16-byte word written is the wrapping uint32 sum, lane by lane, of the
+// R words at the same position of the wave's R KiB read, xor the index
+// (0..W-1) of the KiB it lands in.
+template <int R>
+__global__ __launch_bounds__(kProbeWaves* kWave) void stream_probe_kernel(
+    const u32x4* __restrict__ src, u32x4* __restrict__ dst, int W, int64_t units) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * kProbeWaves + (threadIdx.x >> 6);
+  if (u >= units) return;
+  const int lane = lane_id();
+  constexpr int kWordsPerKiB = 1024 / 16;
+  const u32x4* s = src + u * (R * kWordsPerKiB) + lane;
+  u32x4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = ld16_stream(s + r * kWordsPerKiB);
+  u32x4 acc = v[0];
+#pragma unroll
+  for (int r = 1; r < R; ++r) acc += v[r];
+  u32x4* d = dst + u * W * kWordsPerKiB + lane;
+  for (int w = 0; w < W; ++w)
+    st16_stream(d + static_cast<int64_t>(w) * kWordsPerKiB, acc ^ static_cast<uint32_t>(w));
 }
 
 }  // namespace
@@ -38,6 +72,31 @@ hipError_t launch_floor(int kind, int T, int D, const void* src, void* dst,
     hipLaunchKernelGGL(floor_loads_kernel, grid, block, 0, stream,
                        static_cast<const u32x4*>(src), static_cast<int*>(dst),
                        static_cast<int>(grid.x * block.x));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_probe(int R, int W, int64_t units, const void* src, void* dst,
+                               hipStream_t stream) {
+  if (units <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((units + kProbeWaves - 1) / kProbeWaves));
+  const dim3 block(kProbeWaves * kWave);
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  static_assert(kStreamMaxR == 32, "one case below for every R in [1, kStreamMaxR]");
+  switch (R) {
+#define MOE_PROBE_CASE(RV) \
+  case RV: hipLaunchKernelGGL(stream_probe_kernel<RV>, grid, block, 0, stream, s, d, W, units); break;
+    MOE_PROBE_CASE(1) MOE_PROBE_CASE(2) MOE_PROBE_CASE(3) MOE_PROBE_CASE(4)
+    MOE_PROBE_CASE(5) MOE_PROBE_CASE(6) MOE_PROBE_CASE(7) MOE_PROBE_CASE(8)
+    MOE_PROBE_CASE(9) MOE_PROBE_CASE(10) MOE_PROBE_CASE(11) MOE_PROBE_CASE(12)
+    MOE_PROBE_CASE(13) MOE_PROBE_CASE(14) MOE_PROBE_CASE(15) MOE_PROBE_CASE(16)
+    MOE_PROBE_CASE(17) MOE_PROBE_CASE(18) MOE_PROBE_CASE(19) MOE_PROBE_CASE(20)
+    MOE_PROBE_CASE(21) MOE_PROBE_CASE(22) MOE_PROBE_CASE(23) MOE_PROBE_CASE(24)
+    MOE_PROBE_CASE(25) MOE_PROBE_CASE(26) MOE_PROBE_CASE(27) MOE_PROBE_CASE(28)
+    MOE_PROBE_CASE(29) MOE_PROBE_CASE(30) MOE_PROBE_CASE(31) MOE_PROBE_CASE(32)
+#undef MOE_PROBE_CASE
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

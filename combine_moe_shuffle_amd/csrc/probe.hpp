@@ -1,0 +1,17 @@
+// Measurement aids that no kernel of the path uses: declared apart from
+// launch.hpp so that adding one leaves the path's headers as they are.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+// floor.hip: a contiguous stream of R KiB read and W KiB written per wave
+constexpr int kStreamMaxR = 32;
+constexpr int kStreamMaxW = 32;
+hipError_t launch_stream_probe(int R, int W, int64_t units, const void* src, void* dst,
+                               hipStream_t stream);
+
+}  // namespace moe

@@ -604,6 +604,28 @@ def moe_launch_floor(kind, T, D, src=None, dst=None, device=None):
     return dst
 
 
+def moe_stream_probe(R, W, units, src=None, dst=None, device=None):
+    """A plain contiguous stream: wave u of ``units`` reads R consecutive KiB
+    of ``src`` and writes W consecutive KiB of ``dst`` (each uint32 word the
+    wrapping sum of the R words at its position, xor the KiB's index). Timed
+    with a streaming kernel's read and write bytes it gives the rate that mix
+    reaches in the most favourable order. ``src`` is a uint8 tensor of at
+    least units * R KiB, ``dst`` of at least units * W KiB; each is made when
+    None. Returns dst."""
+    device = device or (src.device if src is not None else torch.device("cuda", 0))
+    if src is None:
+        src = torch.zeros(units * R * 1024, dtype=torch.uint8, device=device)
+    if dst is None:
+        dst = torch.empty(units * W * 1024, dtype=torch.uint8, device=device)
+    for t, nm, need in ((src, "src", units * R * 1024), (dst, "dst", units * W * 1024)):
+        _need(t, nm, torch.uint8, device=device)
+        _contig(t, nm)
+        if t.numel() < need:
+            raise ValueError(f"{nm} must hold at least {need} bytes (has {t.numel()})")
+    _call("moe_stream_probe", R, W, units, _ptr(src), _ptr(dst), _stream(device))
+    return dst
+
+
 # The pages' names for the same operations
 gather_scale_dense_tokens = moe_gather_scale
 gather_scale_quant_dense_tokens = moe_gather_scale_quant

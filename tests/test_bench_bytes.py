@@ -78,3 +78,23 @@ def test_mhc_padded_shuffling_bytes():
     assert bench.padded_bytes(7168, 256, 8, 6000) == dense - 8192 * 8 * 4 + 48000 * 4 + 256 * 4
     # a re-sort moves every row once each way
     assert bench.shuffling_bytes(1000, 256, 8, 32) == 2 * 1000 * 512 + 8 * 32 * 4 + 33 * 4
+
+
+def test_stream_mix():
+    """The contiguous-stream probe's R:W and wave count carry the roofline
+    kernel's row bytes: the zipf scatter reads 9 rows' KiB for each KiB it
+    writes, the zipf gather writes 8 for each it reads, the MXFP8 prefill
+    finalize reads 5 bf16 rows per token and writes 1.5 (bf16 row and codes)."""
+    tok_kib = 6000 * 7168 * 2 // 1024
+    assert bench.stream_mix(9 * tok_kib, tok_kib) == (9, 1, 84000)
+    assert bench.stream_mix(tok_kib, 8 * tok_kib) == (1, 8, 84000)
+    row_kib = 16384 * 5120 * 2 // 1024
+    assert bench.stream_mix(5 * row_kib, 1.5 * row_kib) == (10, 3, 81920)
+    # mhc: K + 1 + hc = 9 rows in, hc + 1.5 = 5.5 out
+    assert bench.stream_mix(9 * row_kib, 5.5 * row_kib) == (18, 11, 81920)
+    for R, Wm, u in ((9, 1, 84000), (10, 3, 81920), (18, 11, 81920)):
+        assert 1 <= R <= 32 and 1 <= Wm <= 32 and u > 0
+    # not whole KiB, or no ratio within 32:32
+    assert bench.stream_mix(1.5, 1) is None
+    assert bench.stream_mix(33, 1) is None
+    assert bench.stream_mix(0, 4) is None
