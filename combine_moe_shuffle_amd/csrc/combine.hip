@@ -14,7 +14,9 @@
 //
 // Where a token's rows come from:
 //  by_token  the inverse map row_of_pair[t, 0..K) written by the shuffle;
-//            invalid slots dropped and the rest sorted in-wave.
+//            invalid slots dropped and the rest sorted in-wave. For top-1
+//            and top-2 on more than 4096 (token, slice) waves a wave takes
+//            four consecutive tokens' slice, their slots in one load.
 //  general   only token_indices is known. Up to 1024 rows each wave finds
 //            its token's rows itself, in ascending order, with no other
 //            launch. Beyond that a CSR of rows per token is built first: up
@@ -39,6 +41,7 @@ namespace {
 
 constexpr int kRowWaves = 4;
 constexpr int kGroup = 4;  // rows in flight together in the general combine
+constexpr int kMultiTok = 4;  // tokens per wave of the top-1/top-2 by-token combine
 constexpr int kScanThreads = 1024;
 
 __device__ __forceinline__ int clamp_count(const int* p, int hi) {
@@ -223,6 +226,111 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_kernel(
     scatter_token<CPL, G, true>(out, in, rop, t, K, V, D, nch, slice0 + lane, lane);
   else
     scatter_token<CPL, G, false>(out, in, rop, t, K, V, D, nch, slice0 + lane, lane);
+}
+
+// M consecutive tokens' same slice in one wave, for top-k of at most KP (1 or
+// 2) slots: lanes m*KP .. m*KP+KP-1 load token m's slots in one coalesced
+// load, each token's lanes are put in ascending row order, and the M initial rows
+// and all the tokens' rows are in flight together before the first add. The
+// index round trip is paid once per M slices instead of once per slice. The
+// additions are those of scatter_token, in the same order.
+template <int CPL, int M, int KP, bool FULL>
+__device__ __forceinline__ void scatter_tokens_m(uint16_t* __restrict__ out,
+                                                 const uint16_t* __restrict__ in,
+                                                 const int* __restrict__ rop, int t0, int T,
+                                                 int K, int V, int D, int nch, int base,
+                                                 int lane) {
+  static_assert(M * KP <= kWave && (KP == 1 || KP == 2), "one slot per lane");
+  const int m_l = lane / KP;
+  const int s_l = lane % KP;
+  const int t_l = t0 + m_l;
+  const int r = (m_l < M && s_l < K && t_l < T) ? rop[static_cast<int64_t>(t_l) * K + s_l] : -1;
+  u32x4 o0[M][CPL];
+  bool early[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int tm = t0 + m;
+    early[m] = tm < T && static_cast<int64_t>(tm) * K < V;  // wave-uniform
+    if (early[m]) load_init<CPL, FULL>(o0[m], out + static_cast<int64_t>(tm) * D, nch, base);
+  }
+  const bool ok = r >= 0 && r < V;
+  const uint64_t okm = __ballot(ok);
+  // each token's KP lanes ascending, invalid slots (INT_MAX) last; for KP = 2
+  // one compare-exchange per lane pair (wave_sort_asc orders only its first
+  // block ascending: its last stage alternates direction from block to block)
+  int sorted = ok ? r : INT_MAX;
+  if constexpr (KP == 2) {
+    const int o = __shfl_xor(sorted, 1, kWave);
+    sorted = (lane & 1) ? max(sorted, o) : min(sorted, o);
+  }
+  int n[M];
+  u32x4 buf[M][KP][CPL];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    n[m] = __popcll((okm >> (m * KP)) & ((1ull << KP) - 1ull));
+    if (n[m] > 0) {
+#pragma unroll
+      for (int q = 0; q < KP; ++q) {
+        const int row = __builtin_amdgcn_readlane(sorted, m * KP + min(q, n[m] - 1));
+        const uint16_t* src = in + static_cast<int64_t>(row) * D;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = base + j * kWave;
+          if (FULL || c < nch) buf[m][q][j] = ld16_stream(src + c * kChunk);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (n[m] > 0 && !early[m])
+      load_init<CPL, FULL>(o0[m], out + static_cast<int64_t>(t0 + m) * D, nch, base);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (n[m] == 0) continue;
+    float acc[CPL][8];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) unpack8(o0[m][j], acc[j]);
+#pragma unroll
+    for (int q = 0; q < KP; ++q) {
+      if (q < n[m]) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int c = base + j * kWave;
+          if (FULL || c < nch) {
+            float f[8];
+            unpack8(buf[m][q][j], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] + f[i];
+          }
+        }
+      }
+    }
+    store_acc<CPL, FULL>(acc, out + static_cast<int64_t>(t0 + m) * D, nch, base);
+  }
+}
+
+template <int CPL, int M, int KP>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_tokens_multi_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in,
+    const int* __restrict__ rop, int K, int a, int D, const int* __restrict__ vrows,
+    int nsl) {
+  const int lane = lane_id();
+  const int64_t unit =
+      static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
+  const int g = static_cast<int>(unit / nsl);
+  const int sl = static_cast<int>(unit - static_cast<int64_t>(g) * nsl);
+  const int64_t t0 = static_cast<int64_t>(g) * M;
+  if (t0 >= T) return;
+  const int V = clamp_count(vrows, a);
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  if (slice0 + kWave * CPL <= nch)
+    scatter_tokens_m<CPL, M, KP, true>(out, in, rop, static_cast<int>(t0), T, K, V, D, nch,
+                                       slice0 + lane, lane);
+  else
+    scatter_tokens_m<CPL, M, KP, false>(out, in, rop, static_cast<int>(t0), T, K, V, D, nch,
+                                        slice0 + lane, lane);
 }
 
 // ---------------------------------------------------------------- general
@@ -974,8 +1082,32 @@ hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
   constexpr int64_t kFewUnits = 4096;
   const int G = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 || units > kFewUnits ? 4 : 8));
-  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
   const dim3 block(kRowWaves * kWave);
+  // top-1 and top-2 on a full grid: kMultiTok tokens per wave (measured at
+  // T=4096, D=5120, K=1: 2, 4 and 8 tokens against one; 4 the fastest, warm
+  // and after a cache flush)
+  if (K <= 2 && units > kFewUnits) {
+    const int64_t mu = (static_cast<int64_t>(T) + kMultiTok - 1) / kMultiTok * sh.nsl;
+    const dim3 mgrid(static_cast<unsigned>((mu + kRowWaves - 1) / kRowWaves));
+#define LM(C)                                                                                  \
+  do {                                                                                         \
+    if (K <= 1)                                                                                \
+      hipLaunchKernelGGL((scatter_tokens_multi_kernel<C, kMultiTok, 1>), mgrid, block, 0,      \
+                         stream, out, T, in, row_of_pair, K, a, D, valid_rows, sh.nsl);        \
+    else                                                                                       \
+      hipLaunchKernelGGL((scatter_tokens_multi_kernel<C, kMultiTok, 2>), mgrid, block, 0,      \
+                         stream, out, T, in, row_of_pair, K, a, D, valid_rows, sh.nsl);        \
+  } while (0)
+    switch (sh.cpl) {
+      case 1: LM(1); break;
+      case 2: LM(2); break;
+      case 3: LM(3); break;
+      default: LM(4); break;
+    }
+#undef LM
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
 #define L2(C, GV)                                                                          \
   hipLaunchKernelGGL((scatter_tokens_kernel<C, GV>), grid, block, 0, stream, out, T, in,  \
                      row_of_pair, K, a, D, valid_rows, sh.nsl)

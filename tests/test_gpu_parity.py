@@ -116,6 +116,28 @@ def test_launch_floor_kernels(dev):
         assert np.array_equal(dst.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("R,W,units", [(1, 1, 1), (9, 1, 1001), (1, 8, 999), (32, 32, 6),
+                                       (10, 3, 257)])
+def test_stream_probe(dev, R, W, units):
+    """The contiguous-stream aid writes, for each wave and each of its W KiB,
+    the wrapping uint32 sum of its R KiB read (word by word) xor the KiB's
+    index, and nothing past units * W KiB."""
+    g = np.random.default_rng(R * 100 + W)
+    src = g.integers(0, 1 << 32, size=units * R * 256, dtype=np.uint32)
+    extra = 4096
+    dst = torch.full((units * W * 1024 + extra,), 0xA5, dtype=torch.uint8, device=dev)
+    say("stream probe", R, W, units)
+    ops.moe_stream_probe(R, W, units, src=torch.from_numpy(src.view(np.uint8)).to(dev),
+                         dst=dst)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    body = got[:units * W * 1024].view(np.uint32).reshape(units, W, 256)
+    acc = np.add.reduce(src.reshape(units, R, 256), axis=1, dtype=np.uint32)
+    want = acc[:, None, :] ^ np.arange(W, dtype=np.uint32)[None, :, None]
+    assert np.array_equal(body, want)
+    assert np.all(got[units * W * 1024:] == 0xA5)
+
+
 # ---------------------------------------------------------------- shuffle
 SHUFFLE_CASES = [
     # (name, T, E, K, vtc, score kind)
@@ -383,6 +405,53 @@ def test_scatter_add_by_token_any_inverse_map(dev):
     y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
     out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
     say("scatter by token, any inverse map", T, K, D, V)
+    want = orc.scatter_add(out0.copy(), y, ti, V)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_by_token(out, bf_dev(y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+    out2 = bf_dev(out0, dev)
+    ops.moe_scatter_add(out2, bf_dev(y, dev), i32_dev(ti, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out2), want)
+
+
+MANY_SMALL_K_CASES = [
+    # (name, T, D, E, K, vtc): top-1 and top-2 on grids of more than 4096
+    # (token, slice) waves, where a wave takes several consecutive tokens
+    ("K1-ragged-D", 4099, 8 * (64 * 4 + 5), 16, 1, 4000),  # partial last slice
+    ("K2", 5003, 512, 16, 2, 4990),                        # T not a multiple of the tokens
+    ("K1-quant-D", 4110, 5120, 16, 1, None),               # per wave
+    ("K2-vtc0", 5000, 1024, 8, 2, 0),                      # no routed token: out unchanged
+]
+
+
+@pytest.mark.parametrize("case", MANY_SMALL_K_CASES, ids=[c[0] for c in MANY_SMALL_K_CASES])
+def test_scatter_add_by_token_many_tokens_small_k(dev, case):
+    name, T, D, E, K, vtc = case
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=4)
+    V = int(counts[E])
+    say("scatter by token, small K", name, T, D, K, V)
+    want = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+    out = bf_dev(inp.out0, dev)
+    ops.moe_scatter_add_by_token(out, bf_dev(inp.y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
+    assert np.array_equal(bits_host(out), want)
+
+
+def test_scatter_add_by_token_small_k_any_inverse_map(dev):
+    """Top-2 on a large grid with an inverse map no shuffle makes: rows dealt
+    to tokens by a random permutation, 60 % of them valid, so a token may own
+    0, 1 or 2 valid rows in either slot order, and tokens past V/K still own
+    some. Equal to the oracle and to the general path."""
+    g = np.random.default_rng(41)
+    T, K, D = 4600, 2, 8 * 100
+    a = T * K
+    perm = g.permutation(a).astype(np.int32)
+    rop = perm.reshape(T, K)
+    ti = np.empty(a, np.int32)
+    ti[perm] = np.repeat(np.arange(T, dtype=np.int32), K)
+    V = a * 3 // 5
+    y = W.to_bf16_bits(g.standard_normal((a, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("scatter by token, small K, any inverse map", T, K, D, V)
     want = orc.scatter_add(out0.copy(), y, ti, V)
     out = bf_dev(out0, dev)
     ops.moe_scatter_add_by_token(out, bf_dev(y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
