@@ -61,7 +61,7 @@ SIGNATURES = {
     "moe_convert_check": (_status, [_p, _i64, _p, _p, _p]),
     "moe_launch_floor_threads": (_i32, [_i32, _i32]),
     "moe_launch_floor": (_status, [_i32, _i32, _i32, _p, _p, _p]),
-    "moe_stream_probe": (_status, [_i32, _i32, _i64, _p, _p, _p]),
+    "moe_stream_probe": (_status, [_i32, _i32, _i32, _i64, _p, _p, _p]),
 }
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",

@@ -547,8 +547,10 @@ moe_status_t moe_launch_floor(int32_t kind, int32_t T, int32_t D, const void* sr
                     "moe_launch_floor");
 }
 
-moe_status_t moe_stream_probe(int32_t R, int32_t W, int64_t units, const void* src, void* dst,
-                              void* stream) {
+moe_status_t moe_stream_probe(int32_t layout, int32_t R, int32_t W, int64_t units,
+                              const void* src, void* dst, void* stream) {
+  REQUIRE(layout == 0 || layout == 1, MOE_ERR_INVALID_ARG, "layout must be 0 or 1 (got %d)",
+          layout);
   REQUIRE(R >= 1 && R <= moe::kStreamMaxR, MOE_ERR_INVALID_ARG, "R must be in [1, %d] (got %d)",
           moe::kStreamMaxR, R);
   REQUIRE(W >= 1 && W <= moe::kStreamMaxW, MOE_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)",
@@ -563,7 +565,7 @@ moe_status_t moe_stream_probe(int32_t R, int32_t W, int64_t units, const void* s
   const uintptr_t s1 = s0 + static_cast<uintptr_t>(units) * R * 1024;
   const uintptr_t d1 = d0 + static_cast<uintptr_t>(units) * W * 1024;
   REQUIRE(s1 <= d0 || d1 <= s0, MOE_ERR_INVALID_ARG, "src and dst overlap");
-  return hip_status(moe::launch_stream_probe(R, W, units, src, dst,
+  return hip_status(moe::launch_stream_probe(layout, R, W, units, src, dst,
                                              static_cast<hipStream_t>(stream)),
                     "moe_stream_probe");
 }

@@ -7,12 +7,16 @@
 // kernel can reach at small T: the launch itself, and the two memory round
 // trips the finalize's slot rows and expert rows take.
 //
-// A contiguous stream with a chosen read:write mix: wave u reads R
-// consecutive KiB and writes W consecutive KiB, consecutive waves on
-// consecutive memory, every row access a nontemporal 16-byte one per lane as
-// in the streaming kernels. With the byte counts of a streaming kernel it
-// gives the rate the same mix reaches in the most favourable order: the
-// ceiling to hold that kernel's rate against, next to the HBM peak.
+// A contiguous stream with a chosen read:write mix, in one of two layouts:
+// blocked (wave u reads R consecutive KiB of src and writes W consecutive KiB
+// of dst, consecutive waves on consecutive memory) or interleaved (src is R
+// streams and dst W streams of `units` KiB each; wave u reads and writes KiB
+// u of every stream, consecutive waves on consecutive memory in each). Every
+// access is a nontemporal 16-byte one per lane, as in the streaming kernels.
+// Few streams favour the interleaved layout, many streams the blocked one.
+// Timed with a streaming kernel's byte counts it gives a reference rate for
+// that mix: what a plain stream of the same bytes reaches, next to the HBM
+// peak.
 #include "device.hpp"
 #include "launch.hpp"
 #include "probe.hpp"
@@ -35,25 +39,28 @@ __global__ __launch_bounds__(1024) void floor_loads_kernel(const u32x4* __restri
 constexpr int kProbeWaves = 4;
 
 // Each 16-byte word written is the wrapping uint32 sum, lane by lane, of the
-// R words at the same position of the wave's R KiB read, xor the index
-// (0..W-1) of the KiB it lands in.
-template <int R>
+// R words at the same position of the wave's R source KiB, xor the index
+// (0..W-1) of the destination KiB it lands in (blocked: the wave's w-th KiB;
+// interleaved: stream w).
+template <int R, bool INTERLEAVED>
 __global__ __launch_bounds__(kProbeWaves* kWave) void stream_probe_kernel(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, int W, int64_t units) {
   const int64_t u = static_cast<int64_t>(blockIdx.x) * kProbeWaves + (threadIdx.x >> 6);
   if (u >= units) return;
   const int lane = lane_id();
   constexpr int kWordsPerKiB = 1024 / 16;
-  const u32x4* s = src + u * (R * kWordsPerKiB) + lane;
+  // distance between a wave's consecutive KiB, and the wave's first KiB
+  const int64_t rstep = INTERLEAVED ? units * kWordsPerKiB : kWordsPerKiB;
+  const int64_t wstep = rstep;
+  const u32x4* s = src + (INTERLEAVED ? u : u * R) * kWordsPerKiB + lane;
+  u32x4* d = dst + (INTERLEAVED ? u : u * W) * kWordsPerKiB + lane;
   u32x4 v[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = ld16_stream(s + r * kWordsPerKiB);
+  for (int r = 0; r < R; ++r) v[r] = ld16_stream(s + r * rstep);
   u32x4 acc = v[0];
 #pragma unroll
   for (int r = 1; r < R; ++r) acc += v[r];
-  u32x4* d = dst + u * W * kWordsPerKiB + lane;
-  for (int w = 0; w < W; ++w)
-    st16_stream(d + static_cast<int64_t>(w) * kWordsPerKiB, acc ^ static_cast<uint32_t>(w));
+  for (int w = 0; w < W; ++w) st16_stream(d + w * wstep, acc ^ static_cast<uint32_t>(w));
 }
 
 }  // namespace
@@ -76,8 +83,8 @@ hipError_t launch_floor(int kind, int T, int D, const void* src, void* dst,
   return hipGetLastError();
 }
 
-hipError_t launch_stream_probe(int R, int W, int64_t units, const void* src, void* dst,
-                               hipStream_t stream) {
+hipError_t launch_stream_probe(int layout, int R, int W, int64_t units, const void* src,
+                               void* dst, hipStream_t stream) {
   if (units <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((units + kProbeWaves - 1) / kProbeWaves));
   const dim3 block(kProbeWaves * kWave);
@@ -85,8 +92,15 @@ hipError_t launch_stream_probe(int R, int W, int64_t units, const void* src, voi
   u32x4* d = static_cast<u32x4*>(dst);
   static_assert(kStreamMaxR == 32, "one case below for every R in [1, kStreamMaxR]");
   switch (R) {
-#define MOE_PROBE_CASE(RV) \
-  case RV: hipLaunchKernelGGL(stream_probe_kernel<RV>, grid, block, 0, stream, s, d, W, units); break;
+#define MOE_PROBE_CASE(RV)                                                                     \
+  case RV:                                                                                     \
+    if (layout == 1)                                                                           \
+      hipLaunchKernelGGL((stream_probe_kernel<RV, true>), grid, block, 0, stream, s, d, W,     \
+                         units);                                                               \
+    else                                                                                       \
+      hipLaunchKernelGGL((stream_probe_kernel<RV, false>), grid, block, 0, stream, s, d, W,    \
+                         units);                                                               \
+    break;
     MOE_PROBE_CASE(1) MOE_PROBE_CASE(2) MOE_PROBE_CASE(3) MOE_PROBE_CASE(4)
     MOE_PROBE_CASE(5) MOE_PROBE_CASE(6) MOE_PROBE_CASE(7) MOE_PROBE_CASE(8)
     MOE_PROBE_CASE(9) MOE_PROBE_CASE(10) MOE_PROBE_CASE(11) MOE_PROBE_CASE(12)

@@ -604,14 +604,16 @@ def moe_launch_floor(kind, T, D, src=None, dst=None, device=None):
     return dst
 
 
-def moe_stream_probe(R, W, units, src=None, dst=None, device=None):
-    """A plain contiguous stream: wave u of ``units`` reads R consecutive KiB
-    of ``src`` and writes W consecutive KiB of ``dst`` (each uint32 word the
-    wrapping sum of the R words at its position, xor the KiB's index). Timed
-    with a streaming kernel's read and write bytes it gives the rate that mix
-    reaches in the most favourable order. ``src`` is a uint8 tensor of at
-    least units * R KiB, ``dst`` of at least units * W KiB; each is made when
-    None. Returns dst."""
+def moe_stream_probe(R, W, units, src=None, dst=None, device=None, layout=0):
+    """A plain contiguous stream of ``units`` waves, each reading R KiB and
+    writing W KiB (each uint32 word written the wrapping sum of the R words
+    at its position, xor the index of the destination KiB). layout 0: wave u
+    reads R consecutive KiB of ``src`` and writes W consecutive KiB of
+    ``dst``; layout 1: ``src`` holds R streams and ``dst`` W streams of
+    ``units`` KiB, wave u reads and writes KiB u of each. Timed with a
+    streaming kernel's read and write bytes it gives a reference rate for
+    that mix. ``src`` is a uint8 tensor of at least units * R KiB, ``dst`` of
+    at least units * W KiB; each is made when None. Returns dst."""
     device = device or (src.device if src is not None else torch.device("cuda", 0))
     if src is None:
         src = torch.zeros(units * R * 1024, dtype=torch.uint8, device=device)
@@ -622,7 +624,7 @@ def moe_stream_probe(R, W, units, src=None, dst=None, device=None):
         _contig(t, nm)
         if t.numel() < need:
             raise ValueError(f"{nm} must hold at least {need} bytes (has {t.numel()})")
-    _call("moe_stream_probe", R, W, units, _ptr(src), _ptr(dst), _stream(device))
+    _call("moe_stream_probe", layout, R, W, units, _ptr(src), _ptr(dst), _stream(device))
     return dst
 
 

@@ -462,21 +462,26 @@ MOE_API moe_status_t moe_launch_floor(int32_t kind, int32_t T, int32_t D, const 
 
 /* ------------------------------------------------------------------------
  * moe_stream_probe -- measurement aid: a plain contiguous stream with a
- * chosen read:write mix. units waves; wave u reads the R KiB of src from
- * byte u * R * 1024 and writes the W KiB of dst from byte u * W * 1024
- * (consecutive waves on consecutive memory, nontemporal 16-byte accesses).
- * Word j (uint32) of KiB w of wave u's writes is the wrapping sum over r < R
- * of word j of KiB r of its reads, xor w. Timed with a streaming kernel's
- * read and write bytes, it gives the rate that mix reaches in the most
- * favourable order on this GPU: the ceiling to hold that kernel against,
- * beside the HBM peak.
- * R and W in [1, 32]; units in [0, 2^31) (0: nothing is launched). src holds
- * at least units * R KiB, dst at least units * W KiB (the caller's to
- * guarantee: the call sees no sizes); both 16-byte aligned, and the two
- * ranges must not overlap (MOE_ERR_INVALID_ARG). Only dst is written.
+ * chosen read:write mix, units waves of R KiB read and W KiB written, every
+ * access a nontemporal 16-byte one per lane. Layout 0 (blocked): wave u
+ * reads the R KiB of src from byte u * R * 1024 and writes the W KiB of dst
+ * from byte u * W * 1024. Layout 1 (interleaved): src is R streams and dst W
+ * streams of units KiB each (stream r from byte r * units * 1024); wave u
+ * reads KiB u of every source stream and writes KiB u of every destination
+ * stream. Either way consecutive waves touch consecutive memory. Word j
+ * (uint32) of the wave's w-th destination KiB is the wrapping sum over
+ * r < R of word j of its r-th source KiB, xor w. Timed with a streaming
+ * kernel's read and write bytes, it gives a reference rate for that mix on
+ * this GPU (what a plain stream of the same bytes reaches), beside the HBM
+ * peak.
+ * layout 0 or 1; R and W in [1, 32]; units in [0, 2^31) (0: nothing is
+ * launched). src holds at least units * R KiB, dst at least units * W KiB
+ * (the caller's to guarantee: the call sees no sizes); both 16-byte
+ * aligned, and the two ranges must not overlap (MOE_ERR_INVALID_ARG). Only
+ * dst is written.
  * ---------------------------------------------------------------------- */
-MOE_API moe_status_t moe_stream_probe(int32_t R, int32_t W, int64_t units, const void *src,
-                                      void *dst, void *stream);
+MOE_API moe_status_t moe_stream_probe(int32_t layout, int32_t R, int32_t W, int64_t units,
+                                      const void *src, void *dst, void *stream);
 
 #ifdef __cplusplus
 }

@@ -94,23 +94,25 @@ def _err(lib):
 @host_only
 def test_stream_probe_rejects(lib):
     f = lib.moe_stream_probe
-    assert f(0, 1, 4, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(2, 1, 1, 4, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert "layout" in _err(lib)
+    assert f(0, 0, 1, 4, FAKE, FAKE + (1 << 20), None) == INVALID
     assert "R must be" in _err(lib)
-    assert f(33, 1, 4, FAKE, FAKE + (1 << 20), None) == INVALID
-    assert f(1, 0, 4, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(1, 33, 1, 4, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(0, 1, 0, 4, FAKE, FAKE + (1 << 20), None) == INVALID
     assert "W must be" in _err(lib)
-    assert f(1, 33, 4, FAKE, FAKE + (1 << 20), None) == INVALID
-    assert f(1, 1, -1, FAKE, FAKE + (1 << 20), None) == INVALID
-    assert f(1, 1, 1 << 31, FAKE, FAKE + (1 << 20), None) == INVALID
-    assert f(1, 1, 4, None, FAKE, None) == INVALID
-    assert f(1, 1, 4, FAKE + 8, FAKE + (1 << 20), None) == INVALID
+    assert f(1, 1, 33, 4, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(0, 1, 1, -1, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(0, 1, 1, 1 << 31, FAKE, FAKE + (1 << 20), None) == INVALID
+    assert f(0, 1, 1, 4, None, FAKE, None) == INVALID
+    assert f(1, 1, 1, 4, FAKE + 8, FAKE + (1 << 20), None) == INVALID
     assert "aligned" in _err(lib)
     # 4 waves of 2 KiB read from FAKE reach FAKE + 8 KiB: a dst inside overlaps
-    assert f(2, 1, 4, FAKE, FAKE + 8192 - 1024, None) == INVALID
+    assert f(0, 2, 1, 4, FAKE, FAKE + 8192 - 1024, None) == INVALID
     assert "overlap" in _err(lib)
-    assert f(1, 2, 4, FAKE + 8192 - 1024, FAKE, None) == INVALID
+    assert f(1, 1, 2, 4, FAKE + 8192 - 1024, FAKE, None) == INVALID
     # nothing to do: OK without touching anything
-    assert f(1, 1, 0, None, None, None) == OK
+    assert f(0, 1, 1, 0, None, None, None) == OK
 
 
 @host_only

@@ -116,24 +116,31 @@ def test_launch_floor_kernels(dev):
         assert np.array_equal(dst.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("R,W,units", [(1, 1, 1), (9, 1, 1001), (1, 8, 999), (32, 32, 6),
                                        (10, 3, 257)])
-def test_stream_probe(dev, R, W, units):
-    """The contiguous-stream aid writes, for each wave and each of its W KiB,
-    the wrapping uint32 sum of its R KiB read (word by word) xor the KiB's
-    index, and nothing past units * W KiB."""
+def test_stream_probe(dev, R, W, units, layout):
+    """The contiguous-stream aid writes the wave's w-th destination KiB as
+    the wrapping uint32 sum (word by word) of its R source KiB, xor w, with
+    the KiB of wave u at u*R + r / u*W + w (blocked) or r*units + u /
+    w*units + u (interleaved), and nothing past units * W KiB."""
     g = np.random.default_rng(R * 100 + W)
     src = g.integers(0, 1 << 32, size=units * R * 256, dtype=np.uint32)
     extra = 4096
     dst = torch.full((units * W * 1024 + extra,), 0xA5, dtype=torch.uint8, device=dev)
-    say("stream probe", R, W, units)
+    say("stream probe", layout, R, W, units)
     ops.moe_stream_probe(R, W, units, src=torch.from_numpy(src.view(np.uint8)).to(dev),
-                         dst=dst)
+                         dst=dst, layout=layout)
     torch.cuda.synchronize()
     got = dst.cpu().numpy()
-    body = got[:units * W * 1024].view(np.uint32).reshape(units, W, 256)
-    acc = np.add.reduce(src.reshape(units, R, 256), axis=1, dtype=np.uint32)
-    want = acc[:, None, :] ^ np.arange(W, dtype=np.uint32)[None, :, None]
+    body = got[:units * W * 1024].view(np.uint32)
+    if layout == 0:
+        acc = np.add.reduce(src.reshape(units, R, 256), axis=1, dtype=np.uint32)
+        body = body.reshape(units, W, 256).transpose(1, 0, 2)
+    else:
+        acc = np.add.reduce(src.reshape(R, units, 256), axis=0, dtype=np.uint32)
+        body = body.reshape(W, units, 256)
+    want = acc[None, :, :] ^ np.arange(W, dtype=np.uint32)[:, None, None]
     assert np.array_equal(body, want)
     assert np.all(got[units * W * 1024:] == 0xA5)
 
