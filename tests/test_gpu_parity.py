@@ -1014,6 +1014,40 @@ def test_graph_replay_matches_eager(dev):
             assert torch.equal(got[k], v), (rep, k)
 
 
+@pytest.mark.parametrize("K", [1, 2])
+def test_graph_replay_small_k_combine(dev, K):
+    """The top-1/top-2 combine on a grid of more than 4096 waves (several
+    tokens per wave), captured in a HIP graph: every replay, with the output
+    reset eagerly between replays, equals the eager run and the oracle."""
+    T, D, E, vtc = 4200, 1024, 8, 4100
+    inp, counts, ei, ti, rop = _dispatch_case(T, D, E, K, vtc, seed=6)
+    V = int(counts[E])
+    want = orc.scatter_add(inp.out0.copy(), inp.y, ti, V)
+    out0, y = bf_dev(inp.out0, dev), bf_dev(inp.y, dev)
+    rop_d, v_d = i32_dev(rop, dev), scalar_dev(V, dev)
+    say("graph replay, small-K combine", T, D, K, V)
+    out = out0.clone()
+    ops.moe_scatter_add_by_token(out, y, rop_d, v_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_host(out), want)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out.copy_(out0)
+        ops.moe_scatter_add_by_token(out, y, rop_d, v_d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.moe_scatter_add_by_token(out, y, rop_d, v_d)
+    for rep in range(3):
+        out.copy_(out0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_host(out), want), rep
+
+
 @pytest.mark.parametrize("T", [300, 100])
 def test_graph_replay_general_paths(dev, T):
     """The entry points the first graph test leaves out, captured in one HIP
