@@ -12,8 +12,11 @@
 //
 // Three launches: one workgroup builds the segment table (per-rank column
 // scans, rank bases, and the expert-major scan, in LDS); one wave per segment
-// marks the segment of every expert-major row; then one wave per (row, slice)
-// copies the row with 16-byte loads and stores.
+// writes every expert-major row's rank-major row; then one wave per (row,
+// slice) copies the row with 16-byte loads and stores, one table load ahead
+// of its row.
+#include <limits.h>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -121,17 +124,25 @@ __global__ __launch_bounds__(kTableThreads) void shuffling_table_kernel(
   }
 }
 
-// seg_of_row[o] = q for every expert-major row o of segment q (one wave per
-// segment). Rows at or beyond em_rows (counts larger than the buffer) are not
+// src_of_row[o] = the rank-major row of expert-major row o: segment q's
+// rank-major start plus o's offset in the segment (one wave per segment).
+// Rows are taken in 64 bits and only rows in [0, em_rows) are written, so
+// counts whose sums pass 2^31 - 1 (wrapped table entries) write nothing out
+// of range; an entry past INT_MAX is stored as INT_MAX, which the copy drops. Rows at or beyond em_rows (counts larger than the buffer) are not
 // marked; the copy kernel never reaches them.
 __global__ __launch_bounds__(kRowWaves* kWave) void shuffling_mark_kernel(
-    const int* __restrict__ seg_dst, int nseg, int64_t em_rows, int* __restrict__ seg_of_row) {
+    const int* __restrict__ seg_src, const int* __restrict__ seg_dst, int nseg,
+    int64_t em_rows, int* __restrict__ src_of_row) {
   const int q = blockIdx.x * kRowWaves + uniform(threadIdx.x >> 6);
   if (q >= nseg) return;
   const int s0 = seg_dst[q];
   const int len = seg_dst[q + 1] - s0;
-  for (int j = lane_id(); j < len; j += kWave)
-    if (s0 + j < em_rows) seg_of_row[s0 + j] = q;
+  const int r0 = seg_src[q];
+  for (int j = lane_id(); j < len; j += kWave) {
+    const int64_t o = static_cast<int64_t>(s0) + j;
+    const int64_t r = static_cast<int64_t>(r0) + j;
+    if (o >= 0 && o < em_rows) src_of_row[o] = r > INT_MAX ? INT_MAX : static_cast<int>(r);
+  }
 }
 
 // Copies expert-major row o from / to its rank-major position.
@@ -139,21 +150,23 @@ __global__ __launch_bounds__(kRowWaves* kWave) void shuffling_mark_kernel(
 template <int CPL, bool INVERSE>
 __global__ __launch_bounds__(kRowWaves* kWave) void shuffling_copy_kernel(
     const uint16_t* __restrict__ in, int64_t in_rows, uint16_t* __restrict__ out,
-    int64_t out_rows, int D, const int* __restrict__ seg_src, const int* __restrict__ seg_dst,
-    int nseg, const int* __restrict__ seg_of_row, int64_t em_rows, int nsl) {
+    int64_t out_rows, int D, const int* __restrict__ seg_dst, int nseg,
+    const int* __restrict__ src_of_row, int64_t em_rows, int nsl) {
   const int lane = lane_id();
   const int64_t unit =
       static_cast<int64_t>(blockIdx.x) * kRowWaves + uniform(threadIdx.x >> 6);
   const int64_t o = unit / nsl;
   const int sl = static_cast<int>(unit - o * nsl);
   if (o >= em_rows) return;
+  // both loads at once; rows at or past the total were not written by the
+  // mark kernel and are dropped before their entry is used
   const int total = seg_dst[nseg];
-  if (o >= total) return;  // o < em_rows too, so seg_of_row[o] was marked
-  const int q = seg_of_row[o];
-  const int64_t rm = static_cast<int64_t>(seg_src[q]) + (o - seg_dst[q]);
+  const int64_t rm = src_of_row[o];
+  if (o >= total) return;
   const int64_t from = INVERSE ? o : rm;
   const int64_t to = INVERSE ? rm : o;
-  if (from >= in_rows || to >= out_rows) return;  // out-of-range layout: skipped
+  // out-of-range layout (a negative row only from wrapped counts): skipped
+  if (rm < 0 || from >= in_rows || to >= out_rows) return;
   const uint16_t* src = in + from * D;
   uint16_t* dst = out + to * D;
   const int nch = D >> 3;
@@ -197,13 +210,14 @@ hipError_t launch_shuffling(bool inverse, const uint16_t* in, int64_t in_rows, u
   char* ws = static_cast<char*>(workspace);
   int* seg_src = reinterpret_cast<int*>(ws);
   int* seg_dst = reinterpret_cast<int*>(ws + align256((static_cast<size_t>(nseg) + 1) * 4));
-  int* seg_of_row =
+  int* src_of_row =
       reinterpret_cast<int*>(ws + 2 * align256((static_cast<size_t>(nseg) + 1) * 4));
   hipLaunchKernelGGL(shuffling_table_kernel, dim3(1), dim3(kTableThreads), 0, stream, counts,
                      EP, C, c_lo, c_hi, rank_stride, seg_src, seg_dst, out_counts);
   if (nseg > 0)
     hipLaunchKernelGGL(shuffling_mark_kernel, dim3((nseg + kRowWaves - 1) / kRowWaves),
-                       dim3(kRowWaves * kWave), 0, stream, seg_dst, nseg, em_rows, seg_of_row);
+                       dim3(kRowWaves * kWave), 0, stream, seg_src, seg_dst, nseg, em_rows,
+                       src_of_row);
   if (em_rows == 0 || D == 0 || nseg == 0) return hipGetLastError();
   static const int allowed[] = {1, 2, 3, 4, 5, 6, 7, 8};
   const SliceShape sh = pick_slices(D / kChunk, allowed, 8, 1 << 20);
@@ -214,12 +228,12 @@ hipError_t launch_shuffling(bool inverse, const uint16_t* in, int64_t in_rows, u
   do {                                                                                      \
     if (inverse)                                                                            \
       hipLaunchKernelGGL((shuffling_copy_kernel<C, true>), grid, block, 0, stream, in,      \
-                         in_rows, out, out_rows, D, seg_src, seg_dst, nseg, seg_of_row,     \
-                         em_rows, sh.nsl);                                                  \
+                         in_rows, out, out_rows, D, seg_dst, nseg, src_of_row, em_rows,     \
+                         sh.nsl);                                                           \
     else                                                                                    \
       hipLaunchKernelGGL((shuffling_copy_kernel<C, false>), grid, block, 0, stream, in,     \
-                         in_rows, out, out_rows, D, seg_src, seg_dst, nseg, seg_of_row,     \
-                         em_rows, sh.nsl);                                                  \
+                         in_rows, out, out_rows, D, seg_dst, nseg, src_of_row, em_rows,     \
+                         sh.nsl);                                                           \
   } while (0)
   MOE_DISPATCH_CPL(sh.cpl, L)
 #undef L
