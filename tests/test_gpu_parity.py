@@ -1410,7 +1410,7 @@ def test_randomized_shapes_against_oracle(dev, random_seed):
     count, score strides and EP drawn per seed; every output checked. The
     large seeds draw thousands of tokens and up to 1024 experts (narrow rows),
     so the shuffle takes its three-launch form there. `--random-shape-seeds N`
-    runs seeds 0 .. N-1 (default 32)."""
+    runs seeds F .. F+N-1 (`--random-shape-first F`, default 0; N default 32)."""
     seed = random_seed
     g = np.random.default_rng(1000 + seed)
     if not _large_seed(seed):
