@@ -428,6 +428,8 @@ MANY_SMALL_K_CASES = [
     ("K2", 5003, 512, 16, 2, 4990),                        # T not a multiple of the tokens
     ("K1-quant-D", 4110, 5120, 16, 1, None),               # per wave
     ("K2-vtc0", 5000, 1024, 8, 2, 0),                      # no routed token: out unchanged
+    ("K1-D8-4097", 4097, 8, 4, 1, None),                   # one chunk per row, 4097 waves
+    ("K2-D8-4097", 4097, 8, 4, 2, 3001),                   # the first grid past 4096 waves
 ]
 
 
