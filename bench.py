@@ -22,6 +22,8 @@ resident in HBM:
   mhc       (T=16384, D=5120, K=4, hc=4) moe_finalize_mhc with MXFP8
             (128x4-tiled scales)
   padded    the zipf routing combined from a static (EP=8, T*K, D) buffer:
+            moe_scatter_add_padded_by_token (the shuffle's inverse map)
+  padded-general  the same through token_indices (the pages' arguments):
             moe_scatter_add_padded
   shuffling rows from EP=8 source ranks for one rank's 32 local experts:
             moe_combine_shuffling -> moe_split_shuffling
@@ -85,7 +87,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 WORKLOAD_CHOICES = ["zipf", "zipf-general", "quant", "tiny", "prefill", "decode",
-                    "prefill-swizzled", "mhc", "padded", "shuffling"]
+                    "prefill-swizzled", "mhc", "padded", "padded-general", "shuffling"]
 DISPATCH_METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of peak), 1xMI355X"
 
 
@@ -207,11 +209,13 @@ def mhc_bytes(T, D, K, hc, scale_bytes):
             T * hc * 8 + T * hc * hc * 4 + T * D + scale_bytes)
 
 
-def padded_bytes(D, E, K, vtc):
+def padded_bytes(D, E, K, vtc, T=None):
     """The routed rows from the slabs, each routed token's row read and
-    written, the rows' token indices and the expert counts."""
+    written, the expert counts, and the rows' token indices (V words) or,
+    given T, the inverse map the by-token form reads (T*K words)."""
     V, row_b = vtc * K, D * 2
-    return V * row_b + 2 * vtc * row_b + V * 4 + E * 4
+    idx = V * 4 if T is None else T * K * 4
+    return V * row_b + 2 * vtc * row_b + idx + E * 4
 
 
 def shuffling_bytes(rows, D, EP, EG):
@@ -405,7 +409,10 @@ def _device_normal_bf16(torch, shape, seed, dev):
     return out
 
 
-def setup_padded(ctx, wl, with_cpu):
+def setup_padded(ctx, wl, with_cpu, general=False):
+    """general: through token_indices (moe_scatter_add_padded, which builds
+    per-token row lists in its workspace) instead of the shuffle's inverse map
+    (moe_scatter_add_padded_by_token)."""
     torch, ops, W, dev = ctx.torch, ctx.ops, ctx.W, ctx.dev
     T, D, E, K, EP = wl.T, wl.D, wl.E, wl.K, wl.ep
     inp = W.dispatch_inputs(wl, with_y=False)
@@ -422,19 +429,25 @@ def setup_padded(ctx, wl, with_cpu):
                      dtype=torch.uint8, device=dev)
 
     def padded_scatter():
-        ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
+        if general:
+            ops.moe_scatter_add_padded(slabs, counts_e, ti, out, workspace=ws)
+        else:
+            ops.moe_scatter_add_padded_by_token(slabs, counts_e, rop, out)
 
     tok_kib = vtc * D * 2 / 1024
+    name = wl.name + ("-general" if general else "")
     return SimpleNamespace(
         stages={"padded_scatter": padded_scatter},
         ceiling={"padded_scatter": stream_mix((K + 1) * tok_kib, tok_kib)},
-        stage_bytes={"padded_scatter": padded_bytes(D, E, K, vtc)},
+        stage_bytes={"padded_scatter": padded_bytes(D, E, K, vtc, None if general else T)},
         units_per_step=vtc, unit="tokens/s", metric=DISPATCH_METRIC,
-        config={"workload": f"{wl.name}: T={T} D={D} E={E} K={K} EP={EP} "
+        config={"workload": f"{name}: T={T} D={D} E={E} K={K} EP={EP} "
                             f"valid_token_count={vtc} static (EP, T*K, D) buffer",
                 "tokens": T, "hidden": D, "experts": E, "top_k": K, "ep": EP,
                 "valid_token_count": vtc, "routed_rows": V,
-                "stages": "scatter_add_padded"},
+                "stages": "scatter_add_padded (token_indices)" if general else
+                          "scatter_add_padded_by_token (row_of_pair)"},
+        traffic_key=name,
         dtype="bf16", kernel_src={"padded_scatter": ["combine.hip"]},
         cpu=cpu_baseline_padded(ctx.orc, ctx.W, wl) if with_cpu else None)
 
@@ -517,8 +530,8 @@ def main():
         s = setup_finalize(ctx, W.WORKLOADS["prefill"], with_cpu, variant=True)
     elif name == "mhc":
         s = setup_mhc(ctx, W.WORKLOADS["mhc"], with_cpu)
-    elif name == "padded":
-        s = setup_padded(ctx, W.WORKLOADS["padded"], with_cpu)
+    elif name in ("padded", "padded-general"):
+        s = setup_padded(ctx, W.WORKLOADS["padded"], with_cpu, general=name == "padded-general")
     else:
         s = setup_shuffling(ctx, W.WORKLOADS["shuffling"], with_cpu)
     if s.cpu:

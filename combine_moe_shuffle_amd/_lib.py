@@ -48,6 +48,8 @@ SIGNATURES = {
     "moe_scatter_add_padded_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_scatter_add_padded": (_status, [_p, _i32, _i32, _p, _i32, _p, _p, _i32, _i32, _p, _sz,
                                          _p]),
+    "moe_scatter_add_padded_by_token": (_status, [_p, _i32, _i32, _p, _i32, _p, _i32, _p, _i32,
+                                                  _i32, _p]),
     "moe_shuffling_workspace_bytes": (_sz, [_i32, _i32, _i64]),
     "moe_combine_shuffling": (_status, [_p, _i64, _p, _i64, _i32, _p, _i32, _i32, _i32, _i32,
                                         _i64, _p, _p, _sz, _p]),

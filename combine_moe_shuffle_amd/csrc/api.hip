@@ -365,6 +365,28 @@ moe_status_t moe_scatter_add_padded(const moe_bf16_t* in_tokens, int32_t EP, int
                     "moe_scatter_add_padded");
 }
 
+moe_status_t moe_scatter_add_padded_by_token(const moe_bf16_t* in_tokens, int32_t EP,
+                                             int32_t T_K, const int32_t* token_counts,
+                                             int32_t E, const int32_t* row_of_pair, int32_t K,
+                                             moe_bf16_t* out_tokens, int32_t T, int32_t D,
+                                             void* stream) {
+  REQUIRE(EP >= 1 && E >= 1 && T_K >= 0 && T >= 0, MOE_ERR_INVALID_ARG,
+          "EP, E >= 1 and T_K, T >= 0 required (EP=%d E=%d T_K=%d T=%d)", EP, E, T_K, T);
+  REQUIRE(E % EP == 0, MOE_ERR_INVALID_ARG, "E must be a multiple of EP (E=%d, EP=%d)", E, EP);
+  REQUIRE(E <= kMaxE, MOE_ERR_UNSUPPORTED, "E > %d is not supported (got %d)", kMaxE, E);
+  REQUIRE(static_cast<int64_t>(EP) * T_K < (int64_t{1} << 31), MOE_ERR_INVALID_ARG,
+          "EP*T_K must be < 2^31");
+  REQUIRE(K >= 1 && K <= kMaxK, MOE_ERR_INVALID_ARG, "K must be in [1, %d] (got %d)", kMaxK, K);
+  moe_status_t s = check_scatter(out_tokens, T, in_tokens, T_K, D);
+  if (s != MOE_OK) return s;
+  if (T_K == 0 || D == 0 || T == 0) return ok();
+  REQUIRE(token_counts && row_of_pair, MOE_ERR_INVALID_ARG, "index inputs are NULL");
+  return hip_status(moe::launch_scatter_add_padded_by_token(in_tokens, EP, T_K, token_counts,
+                                                            E, row_of_pair, K, out_tokens, T, D,
+                                                            static_cast<hipStream_t>(stream)),
+                    "moe_scatter_add_padded_by_token");
+}
+
 size_t moe_shuffling_workspace_bytes(int32_t EP, int32_t n_local, int64_t em_rows) {
   if (EP < 1 || n_local < 0 || em_rows < 0) return 0;
   return moe::shuffling_workspace_bytes(EP * n_local, em_rows);

@@ -887,20 +887,16 @@ __device__ __forceinline__ void padded_scan_reduce(uint16_t* __restrict__ orow,
   if (n) store_acc<CPL, FULL>(acc, orow, nch, base);
 }
 
-template <int CPL>
-__global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_scan_kernel(
-    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in, int T_K,
-    const int* __restrict__ counts, int E, int EP, const int* __restrict__ ti, int D,
-    int nsl) {
-  constexpr int NT = kRowWaves * kWave;
+// The expert prefix of the padded layout in LDS, for workgroups that need
+// each row's owner rank: pre[e] = the rows of the experts below e (counts
+// taken as >= 0) and pre[E] = the valid row bound, each clamped to T_K.
+// Thread i owns experts [i*kPer, i*kPer + kPer). Every thread of the
+// workgroup calls it; it ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void padded_prefix(const int* __restrict__ counts, int E, int T_K,
+                                              int* pre, int* wave_tot, int tid, int lane,
+                                              int wv) {
   constexpr int kPer = (kMaxPaddedE + NT - 1) / NT;
-  __shared__ int pre[kMaxPaddedE + 1];
-  __shared__ int wave_tot[kRowWaves];
-  __shared__ int stage[kRowWaves][kWave];
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wv = uniform(tid >> 6);
-  // prefix of the counts: thread i owns experts [i*kPer, i*kPer + kPer)
   int c[kPer];
   int mine = 0;
 #pragma unroll
@@ -919,6 +915,21 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_scan_kernel(
   }
   if (tid == 0) pre[E] = min(total, T_K);
   __syncthreads();
+}
+
+template <int CPL>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_scan_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in, int T_K,
+    const int* __restrict__ counts, int E, int EP, const int* __restrict__ ti, int D,
+    int nsl) {
+  constexpr int NT = kRowWaves * kWave;
+  __shared__ int pre[kMaxPaddedE + 1];
+  __shared__ int wave_tot[kRowWaves];
+  __shared__ int stage[kRowWaves][kWave];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = uniform(tid >> 6);
+  padded_prefix<NT>(counts, E, T_K, pre, wave_tot, tid, lane, wv);
 
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRowWaves + wv;
   const int t = static_cast<int>(unit / nsl);
@@ -942,7 +953,73 @@ __global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_scan_kernel(
                                    slice0 + lane, lane, stage[wv]);
 }
 
+// One (token, slice) of the by-token padded combine: the token's slots from
+// the shuffle's inverse map, the valid rows sorted ascending, each then read
+// from the slab of the rank that owns its expert; the additions and the
+// early initial row are scatter_token's.
+template <int CPL, int G, bool FULL>
+__device__ __forceinline__ void scatter_padded_token(uint16_t* __restrict__ out,
+                                                     const uint16_t* __restrict__ in, int T_K,
+                                                     const int* pre, int E, int epr, int r,
+                                                     int t, int K, int V, int D, int nch,
+                                                     int base, int lane) {
+  uint16_t* orow = out + static_cast<int64_t>(t) * D;
+  const bool early = static_cast<int64_t>(t) * K < V;  // wave-uniform
+  u32x4 o0[CPL];
+  if (early) load_init<CPL, FULL>(o0, orow, nch, base);
+  const bool ok = r >= 0 && r < V;
+  const int n = __popcll(__ballot(ok));
+  if (n == 0) return;
+  const int sorted = wave_sort_asc(ok ? r : INT_MAX, lane, sort_width(uniform(K)));
+  const int src = lane < n ? rank_of_row(pre, E, epr, sorted) * T_K + sorted : 0;
+  if (!early) load_init<CPL, FULL>(o0, orow, nch, base);
+  reduce_slice_from<CPL, G, FULL>(o0, orow, in, D, nch, base, src, n);
+}
+
+// The padded combine through row_of_pair: no row lists. Every workgroup
+// first scans the expert counts into its LDS prefix (each row's owner rank,
+// the valid bound V); the token's slots load meanwhile.
+template <int CPL, int G>
+__global__ __launch_bounds__(kRowWaves* kWave) void scatter_padded_tokens_kernel(
+    uint16_t* __restrict__ out, int T, const uint16_t* __restrict__ in, int T_K,
+    const int* __restrict__ counts, int E, int EP, const int* __restrict__ rop, int K, int D,
+    int nsl) {
+  constexpr int NT = kRowWaves * kWave;
+  __shared__ int pre[kMaxPaddedE + 1];
+  __shared__ int wave_tot[kRowWaves];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wv = uniform(tid >> 6);
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kRowWaves + wv;
+  const int64_t t64 = unit / nsl;
+  const int sl = static_cast<int>(unit - t64 * nsl);
+  const bool live = t64 < T;  // wave-uniform; every wave joins the prefix scan
+  const int t = live ? static_cast<int>(t64) : 0;
+  const int r = (live && lane < K) ? rop[static_cast<int64_t>(t) * K + lane] : -1;
+  padded_prefix<NT>(counts, E, T_K, pre, wave_tot, tid, lane, wv);
+  if (!live) return;
+  const int V = pre[E];
+  const int nch = D >> 3;
+  const int slice0 = sl * kWave * CPL;
+  if (slice0 + kWave * CPL <= nch)
+    scatter_padded_token<CPL, G, true>(out, in, T_K, pre, E, E / EP, r, t, K, V, D, nch,
+                                       slice0 + lane, lane);
+  else
+    scatter_padded_token<CPL, G, false>(out, in, T_K, pre, E, E / EP, r, t, K, V, D, nch,
+                                        slice0 + lane, lane);
+}
+
 size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Rows in flight per group of the by-token combines: the next power of two
+// >= K, at most 4 on a full grid (for K = 8 two groups of 4 measured 1.5 %
+// faster than one of 8: fewer registers, more waves resident), 8 on a grid of
+// at most kFewUnits waves, which is latency-bound and saves the second
+// group's round trip.
+constexpr int64_t kFewUnits = 4096;
+int by_token_group(int K, int64_t units) {
+  return K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 || units > kFewUnits ? 4 : 8));
+}
 
 SliceShape combine_shape(int nch) {
   // kGroup rows * cpl chunks of loads are in flight per lane
@@ -1070,18 +1147,42 @@ hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const 
   return hipGetLastError();
 }
 
+hipError_t launch_scatter_add_padded_by_token(const uint16_t* in, int EP, int T_K,
+                                              const int* counts, int E, const int* row_of_pair,
+                                              int K, uint16_t* out, int T, int D,
+                                              hipStream_t stream) {
+  const SliceShape sh = combine_shape(D / kChunk);
+  const int64_t units = static_cast<int64_t>(T) * sh.nsl;
+  const int G = by_token_group(K, units);
+  const dim3 grid(static_cast<unsigned>((units + kRowWaves - 1) / kRowWaves));
+  const dim3 block(kRowWaves * kWave);
+#define L2(C, GV)                                                                             \
+  hipLaunchKernelGGL((scatter_padded_tokens_kernel<C, GV>), grid, block, 0, stream, out, T, in, \
+                     T_K, counts, E, EP, row_of_pair, K, D, sh.nsl)
+#define LG(C)                         \
+  do {                                \
+    if (G == 1) L2(C, 1);             \
+    else if (G == 2) L2(C, 2);        \
+    else if (G == 4) L2(C, 4);        \
+    else L2(C, 8);                    \
+  } while (0)
+  switch (sh.cpl) {
+    case 1: LG(1); break;
+    case 2: LG(2); break;
+    case 3: LG(3); break;
+    default: LG(4); break;
+  }
+#undef LG
+#undef L2
+  return hipGetLastError();
+}
+
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream) {
-  // G rows in flight: the next power of two >= K, at most 4 on a full grid
-  // (for K = 8 two groups of 4 measured 1.5 % faster than one of 8: fewer
-  // registers, more waves resident), 8 on a grid of at most kFewUnits waves,
-  // which is latency-bound and saves the second group's round trip
-  static const int allowed[] = {2, 4, 3, 1};
-  const SliceShape sh = pick_slices(D / kChunk, allowed, 4, 1 << 20);
+  const SliceShape sh = combine_shape(D / kChunk);
   const int64_t units = static_cast<int64_t>(T) * sh.nsl;
-  constexpr int64_t kFewUnits = 4096;
-  const int G = K <= 1 ? 1 : (K <= 2 ? 2 : (K <= 4 || units > kFewUnits ? 4 : 8));
+  const int G = by_token_group(K, units);
   const dim3 block(kRowWaves * kWave);
   // top-1 and top-2 on a full grid: kMultiTok tokens per wave (measured at
   // T=4096, D=5120, K=1: 2, 4 and 8 tokens against one; 4 the fastest, warm

@@ -48,6 +48,10 @@ size_t scatter_add_padded_workspace_bytes(int T, int T_K, int E);
 hipError_t launch_scatter_add_padded(const uint16_t* in, int EP, int T_K, const int* counts,
                                      int E, const int* ti, uint16_t* out, int T, int D,
                                      void* workspace, hipStream_t stream);
+hipError_t launch_scatter_add_padded_by_token(const uint16_t* in, int EP, int T_K,
+                                              const int* counts, int E, const int* row_of_pair,
+                                              int K, uint16_t* out, int T, int D,
+                                              hipStream_t stream);
 hipError_t launch_scatter_add_by_token(uint16_t* out, int T, const uint16_t* in,
                                        const int* row_of_pair, int K, int a, int D,
                                        const int* valid_rows, hipStream_t stream);

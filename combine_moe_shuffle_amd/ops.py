@@ -384,6 +384,28 @@ def moe_scatter_add_padded(in_tokens, token_counts, token_indices, out_tokens, w
     return out_tokens
 
 
+def moe_scatter_add_padded_by_token(in_tokens, token_counts, row_of_pair, out_tokens):
+    """moe_scatter_add_padded's result, reading each token's rows from the
+    inverse map row_of_pair (T, K) instead of building row lists: no
+    workspace. In place on out_tokens (T, D)."""
+    device = out_tokens.device
+    _need(in_tokens, "in_tokens", torch.bfloat16, 3, device)
+    _need(out_tokens, "out_tokens", torch.bfloat16, 2, device)
+    _need(token_counts, "token_counts", torch.int32, 1, device)
+    _need(row_of_pair, "row_of_pair", torch.int32, 2, device)
+    for t, n in ((in_tokens, "in_tokens"), (out_tokens, "out_tokens"),
+                 (token_counts, "token_counts"), (row_of_pair, "row_of_pair")):
+        _contig(t, n)
+    EP, T_K, D = in_tokens.shape
+    T = out_tokens.shape[0]
+    if out_tokens.shape[1] != D or row_of_pair.shape[0] != T:
+        raise ValueError("shapes must be in (EP, T_K, D), row_of_pair (T, K), out (T, D)")
+    _call("moe_scatter_add_padded_by_token", _ptr(in_tokens), EP, T_K, _ptr(token_counts),
+          token_counts.numel(), _ptr(row_of_pair), row_of_pair.shape[1], _ptr(out_tokens), T, D,
+          _stream(device))
+    return out_tokens
+
+
 def _shuffling(name, tokens, counts, c_lo, c_hi, rank_stride, out, out_rows, with_counts,
                workspace):
     device = tokens.device

@@ -298,6 +298,22 @@ MOE_API moe_status_t moe_scatter_add_padded(const moe_bf16_t *in_tokens, int32_t
                                             void *workspace, size_t workspace_bytes,
                                             void *stream);
 
+/* moe_scatter_add_padded_by_token -- the same result as moe_scatter_add_padded,
+ * reading each token's rows from the inverse map row_of_pair ([T, K] int32,
+ * as moe_shuffle writes it) instead of building it from token_indices: no
+ * workspace, one launch. Rows < 0 or >= V (V = the count total, clamped to
+ * T_K) are skipped; the remaining rows of a token are added in ascending row
+ * order, each read from the slab of the rank that owns its expert.
+ * Precondition: row_of_pair is the inverse of token_indices on rows [0, V);
+ * then the output equals moe_scatter_add_padded's bit for bit. K <= 64; the
+ * other arguments and limits are moe_scatter_add_padded's. */
+MOE_API moe_status_t moe_scatter_add_padded_by_token(const moe_bf16_t *in_tokens, int32_t EP,
+                                                     int32_t T_K,
+                                                     const int32_t *token_counts, int32_t E,
+                                                     const int32_t *row_of_pair, int32_t K,
+                                                     moe_bf16_t *out_tokens, int32_t T,
+                                                     int32_t D, void *stream);
+
 /* ------------------------------------------------------------------------
  * moe_combine_shuffling / moe_split_shuffling -- the expert-parallel
  * receive-side re-sort and its inverse.

@@ -218,6 +218,23 @@ def test_scatter_padded_rejects(lib):
 
 
 @host_only
+def test_scatter_padded_by_token_rejects(lib):
+    p = lib.moe_scatter_add_padded_by_token
+    # (in, EP, T_K, counts, E, row_of_pair, K, out, T, D, stream)
+    assert p(FAKE, 3, 64, FAKE, 8, FAKE, 2, FAKE, 16, 64, None) == INVALID        # E % EP
+    assert p(FAKE, 2, 64, FAKE, 2048, FAKE, 2, FAKE, 16, 64, None) == UNSUPPORTED
+    assert p(FAKE, 2, 64, FAKE, 8, FAKE, 0, FAKE, 16, 64, None) == INVALID        # K
+    assert "K must be" in _err(lib)
+    assert p(FAKE, 2, 64, FAKE, 8, FAKE, 65, FAKE, 16, 64, None) == INVALID
+    assert p(FAKE, 2, 64, FAKE, 8, FAKE, 2, FAKE, 16, 60, None) == INVALID        # D % 8
+    assert p(FAKE, 2, 64, None, 8, FAKE, 2, FAKE, 16, 64, None) == INVALID
+    assert p(FAKE, 2, 64, FAKE, 8, None, 2, FAKE, 16, 64, None) == INVALID
+    assert p(FAKE, 1 << 10, 1 << 22, FAKE, 1 << 10, FAKE, 2, FAKE, 16, 64,
+             None) == INVALID                                                     # EP*T_K
+    assert p(None, 2, 0, None, 8, None, 2, None, 16, 64, None) == OK              # T_K == 0
+
+
+@host_only
 def test_shuffling_rejects(lib):
     c, sp = lib.moe_combine_shuffling, lib.moe_split_shuffling
     ws = 1 << 22

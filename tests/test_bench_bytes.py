@@ -76,6 +76,8 @@ def test_mhc_padded_shuffling_bytes():
     # and the rows' token indices instead of row_of_pair
     dense = bench.dispatch_bytes(8192, 7168, 256, 8, 6000, False)["scatter"]
     assert bench.padded_bytes(7168, 256, 8, 6000) == dense - 8192 * 8 * 4 + 48000 * 4 + 256 * 4
+    # the by-token form reads the inverse map (T*K words) as the dense by-token combine does
+    assert bench.padded_bytes(7168, 256, 8, 6000, T=8192) == dense + 256 * 4
     # a re-sort moves every row once each way
     assert bench.shuffling_bytes(1000, 256, 8, 32) == 2 * 1000 * 512 + 8 * 32 * 4 + 33 * 4
 

@@ -493,6 +493,35 @@ def test_scatter_add_padded_bit_exact(dev, case):
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), i32_dev(counts[:E], dev), i32_dev(ti, dev),
                                out)
     assert np.array_equal(bits_host(out), want)
+    out = bf_dev(inp.out0, dev)
+    ops.moe_scatter_add_padded_by_token(bf_dev(slabs, dev), i32_dev(counts[:E], dev),
+                                        i32_dev(rop, dev), out)
+    assert np.array_equal(bits_host(out), want)
+
+
+def test_scatter_add_padded_by_token_any_inverse_map(dev):
+    """The by-token padded combine with an inverse map no shuffle makes: rows
+    dealt to tokens by a random permutation and counts whose total (V) is
+    60 % of the rows, so a token may own none, some or all of its K slots,
+    in any order, and tokens past V/K still own rows. Equal to the oracle,
+    which takes the same map's token_indices."""
+    g = np.random.default_rng(43)
+    T, K, D, E, EP = 700, 6, 8 * 70, 24, 4
+    T_K = T * K
+    perm = g.permutation(T_K).astype(np.int32)
+    rop = perm.reshape(T, K)
+    ti = np.empty(T_K, np.int32)
+    ti[perm] = np.repeat(np.arange(T, dtype=np.int32), K)
+    V = T_K * 3 // 5
+    counts = np.bincount(np.sort(g.integers(0, E, size=V)), minlength=E).astype(np.int32)
+    slabs = W.to_bf16_bits(g.standard_normal((EP, T_K, D)).astype(np.float32))
+    out0 = W.to_bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    say("padded by token, any inverse map", T, K, D, E, EP, V)
+    want = orc.scatter_add_padded(out0.copy(), slabs, counts, ti)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded_by_token(bf_dev(slabs, dev), i32_dev(counts, dev),
+                                        i32_dev(rop, dev), out)
+    assert np.array_equal(bits_host(out), want)
 
 
 def test_scatter_add_padded_long_lists(dev):
@@ -1281,7 +1310,8 @@ def test_padded_combine_full_routing(dev):
     """The padded workload's routing at full size (zipf scores, T=8192, E=256,
     K=8, valid_token_count=6000, EP=8 static buffer), shuffled on the device
     as the benchmark does; rows of D=256 keep the host copy of the eight
-    slabs small. Every element checked."""
+    slabs small. Every element checked, through token_indices and through
+    row_of_pair."""
     wl = W.WORKLOADS["padded"]
     D = 256
     inp = W.dispatch_inputs(wl, D=D, with_y=False)
@@ -1296,6 +1326,9 @@ def test_padded_combine_full_routing(dev):
     out = torch.zeros((wl.T, D), dtype=torch.bfloat16, device=dev)
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:wl.E].contiguous(), gti, out)
     assert np.array_equal(bits_host(out), want)
+    out = torch.zeros((wl.T, D), dtype=torch.bfloat16, device=dev)
+    ops.moe_scatter_add_padded_by_token(bf_dev(slabs, dev), gc[:wl.E].contiguous(), grop, out)
+    assert np.array_equal(bits_host(out), want)
 
 
 def test_padded_combine_full_size(dev):
@@ -1303,7 +1336,8 @@ def test_padded_combine_full_size(dev):
     D=7168, E=256, K=8, valid_token_count=6000, eight (T*K, D) slabs drawn
     on the device. Every 7th 16-byte chunk of each output row -- every slice
     of the launch, lanes at every offset -- is checked against the oracle run
-    on those columns (the combine is independent per column)."""
+    on those columns (the combine is independent per column); the by-token
+    form (row_of_pair) equals it bit for bit on every element."""
     wl = W.WORKLOADS["padded"]
     T, D, E, K, EP = wl.T, wl.D, wl.E, wl.K, wl.ep
     inp = W.dispatch_inputs(wl, with_y=False)
@@ -1319,6 +1353,10 @@ def test_padded_combine_full_size(dev):
         slabs[r] = torch.randn((T * K, D), generator=gen, device=dev).to(torch.bfloat16)
     out = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
     ops.moe_scatter_add_padded(slabs, gc[:E].contiguous(), gti, out)
+    out_t = torch.zeros((T, D), dtype=torch.bfloat16, device=dev)
+    ops.moe_scatter_add_padded_by_token(slabs, gc[:E].contiguous(), grop, out_t)
+    assert torch.equal(out_t.view(torch.int16), out.view(torch.int16))
+    del out_t
     chunks = torch.arange(0, D // 8, 7, device=dev)
     cols = (chunks[:, None] * 8 + torch.arange(8, device=dev)).reshape(-1)
     sub = bits_host(slabs.index_select(2, cols))
