@@ -659,6 +659,23 @@ def test_out_of_range_indices_are_skipped(dev, a):
     out = bf_dev(out0, dev)
     ops.moe_scatter_add_by_token(out, bf_dev(y, dev), i32_dev(rop, dev), scalar_dev(V, dev))
     assert np.array_equal(bits_host(out), want)
+    # padded by-token combine: the same slots (counts summing to V), each row
+    # read from the slab of the rank that owns its expert
+    EPp = 2
+    cnt = np.bincount(g.integers(0, E, size=V), minlength=E).astype(np.int32)
+    owner = np.searchsorted(np.concatenate([[0], np.cumsum(cnt)]), np.arange(a), "right") - 1
+    slabs = W.to_bf16_bits(g.standard_normal((EPp, a, D)).astype(np.float32))
+    want = out0.copy()
+    for t_ in range(T):
+        rr = np.sort(rop[t_][okp[t_]])
+        if rr.size:
+            src = np.ascontiguousarray(slabs[owner[rr] // (E // EPp), rr])
+            want[t_] = orc.scatter_add(out0[t_:t_ + 1].copy(), src,
+                                       np.zeros(rr.size, np.int32))[0]
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded_by_token(bf_dev(slabs, dev), i32_dev(cnt, dev),
+                                        i32_dev(rop, dev), out)
+    assert np.array_equal(bits_host(out), want)
     # finalize: a slot past the permuted rows is not held
     rop_f = rop.copy()
     rop_f[rop_f >= a] = a + 5
@@ -1510,6 +1527,9 @@ def test_randomized_shapes_against_oracle(dev, random_seed):
     out = bf_dev(out0, dev)
     ops.moe_scatter_add_padded(bf_dev(slabs, dev), gc[:E].contiguous(), gti, out)
     assert np.array_equal(bits_host(out), want)
+    out = bf_dev(out0, dev)
+    ops.moe_scatter_add_padded_by_token(bf_dev(slabs, dev), gc[:E].contiguous(), grop, out)
+    assert np.array_equal(bits_host(out), want)
     # finalize and mHC on the shuffle's rows (D a multiple of 32 for MXFP8);
     # the finalize's flags drawn per seed: bf16 squares, bf16 weights, and the
     # 128x4-tiled scales where D allows them
@@ -1695,6 +1715,8 @@ def test_prepared_calls_cover_every_op(dev):
         "scatter": lambda o: ops.moe_scatter_add(o, y, ti, vr),
         "scatter by token": lambda o: ops.moe_scatter_add_by_token(o, y, rop, vr),
         "padded": lambda o: ops.moe_scatter_add_padded(slabs, counts[:E].contiguous(), ti, o),
+        "padded by token": lambda o: ops.moe_scatter_add_padded_by_token(
+            slabs, counts[:E].contiguous(), rop, o),
         "combine_shuffling": lambda o: ops.moe_combine_shuffling(tok, i32_dev(cnt, dev), 2, 6,
                                                                  out=o),
         "mhc": lambda o: ops.moe_finalize_mhc(
@@ -1710,7 +1732,7 @@ def test_prepared_calls_cover_every_op(dev):
         if name == "quant":
             return (torch.zeros((T * K, D), dtype=torch.uint8, device=dev),
                     torch.zeros(T * K, dtype=torch.float32, device=dev))
-        if name.startswith("scatter") or name == "padded":
+        if name.startswith("scatter") or name.startswith("padded"):
             return bf_dev(out0, dev)
         if name == "combine_shuffling":
             return torch.zeros_like(tok)
