@@ -40,8 +40,9 @@ of the step instead; a graph launch costs more than a few kernel launches here.
    step's latency, launch included ("step_us_isolated").
 2. K cold steps, each after a flush of L2 and the Infinity Cache -- a 1 GiB
    read (clean eviction) or a 1 GiB write (whose dirty lines the step then
-   writes back) -- between two device synchronisations, device time with the
-   flushes' own time (K flushes alone, timed the same way) subtracted; each
+   writes back) -- in 5 blocks of K/5, each block between two device
+   synchronisations and followed by a block of the flushes alone timed the
+   same way: the median over the blocks of the per-step difference; each
    stage alone after a read flush too. The steps after a read flush are the
    headline: `value`, `ms_per_step` and `hbm_frac` (--no-cold skips the cold
    steps, for profiling runs; the headline is then the warm steps).
@@ -85,6 +86,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COLD_BLOCKS = 5  # blocks of steps after a flush, alternated with the flush alone
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 WORKLOAD_CHOICES = ["zipf", "zipf-general", "quant", "tiny", "prefill", "decode",
                     "prefill-swizzled", "mhc", "padded", "padded-general", "shuffling"]
@@ -591,33 +593,37 @@ def main():
     def flush_write():
         flush_buf.fill_(1.0)
 
-    def time_region(fn):
+    def time_region(fn, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        for _ in range(steps):
+        for _ in range(n):
             fn()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    def after_flush(fl, fn):
+        """Device time per call of fn after flush fl: COLD_BLOCKS blocks of
+        flush + fn and of the flush alone, alternated; the median over the
+        blocks of the per-call difference (a flush takes ~150 us, so a drift
+        of a few per cent in its own time would swamp a step of a few us)."""
+        def both():
+            fl()
+            fn()
+        both()
+        n = max(1, steps // COLD_BLOCKS)
+        diffs = [(time_region(both, n) - time_region(fl, n)) / n for _ in range(COLD_BLOCKS)]
+        return float(np.median(diffs))
+
     cold = {}
     cold_stage = {}
     kinds = () if args.no_cold else (("read", flush_read), ("write", flush_write))
     for kind, fl in kinds:
-        def flush_step():
-            fl()
-            run_step()
-        flush_step()
-        cold[kind] = (time_region(flush_step) - time_region(fl)) / steps
+        cold[kind] = after_flush(fl, run_step)
     # each stage alone after a read flush
-    t_flush = 0.0 if args.no_cold else time_region(flush_read)
     for n, fn in ([] if args.no_cold else stages):
-        def flush_stage():
-            flush_read()
-            fn()
-        flush_stage()
-        cold_stage[n] = (time_region(flush_stage) - t_flush) / steps
+        cold_stage[n] = after_flush(flush_read, fn)
     # ---- each stage alone, `steps` launches back to back: its average
     # duration per launch, the denominator of the roofline
     names = [n for n, _ in stages]
@@ -640,12 +646,7 @@ def main():
                                         dst=p_dst, layout=layout)
                 lrec = {"us": round(stage_ms(torch, probe, steps) * 1e3, 2)}
                 if not args.no_cold:
-                    def flush_probe():
-                        flush_read()
-                        probe()
-                    flush_probe()
-                    lrec["us_after_read"] = round(
-                        (time_region(flush_probe) - t_flush) / steps * 1e3, 2)
+                    lrec["us_after_read"] = round(after_flush(flush_read, probe) * 1e3, 2)
                 rec[lname] = lrec
                 del probe
             # the faster layout is the reference, each way of timing on its own
@@ -693,7 +694,9 @@ def main():
         "warmup": warm,
         "ms_per_step": ms_step,
         "headline": ("cold: K steps, each after a 1 GiB read that evicts L2 and the "
-                     "Infinity Cache, device time with the K reads' own time subtracted"
+                     "Infinity Cache, device time with the reads' own time subtracted "
+                     "(median over 5 blocks of K/5 steps, each against a block of reads "
+                     "alone)"
                      if "read" in cold else
                      "warm: K steps back to back (cold steps skipped)"),
         "warm": {**rates(warm_ms), "ms_per_step_device": region_ms / steps,
