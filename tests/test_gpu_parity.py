@@ -979,10 +979,11 @@ def test_empty_inputs_leave_outputs_alone(dev):
 
 # ---------------------------------------------------------------- HIP graphs
 def test_graph_replay_matches_eager(dev):
-    """shuffle -> gather (by token) -> scatter (by token) -> finalize + MXFP8
-    (128x4-tiled scales) -> mHC finalize, captured in one HIP graph. Every
-    replay, with eager work (buffers overwritten) and synchronisations between
-    replays, equals the eager run bit for bit."""
+    """shuffle -> gather (by token) -> scatter (by token) -> padded scatter (by
+    token, two ranks' slabs) -> finalize + MXFP8 (128x4-tiled scales) -> mHC
+    finalize, captured in one HIP graph. Every replay, with eager work
+    (buffers overwritten) and synchronisations between replays, equals the
+    eager run bit for bit."""
     wl = W.WORKLOADS["zipf"]
     T, D, E, K, vtc, hc = 200, 1024, 16, 4, 150, 4
     inp = W.dispatch_inputs(wl, T=T, D=D, E=E, K=K, vtc=vtc, out0="normal")
@@ -994,6 +995,8 @@ def test_graph_replay_matches_eager(dev):
     yf, wf, ropf = bf_dev(fi.y, dev), f32(fi.w), i32_dev(fi.row_of_pair, dev)
     shf, gf = bf_dev(fi.shared, dev), bf_dev(fi.gamma, dev)
     res, post, comb, pre = bf_dev(m.residual, dev), f32(m.post), f32(m.comb), f32(m.pre)
+    slabs = bf_dev(W.to_bf16_bits(np.random.default_rng(9).standard_normal(
+        (2, T * K, D)).astype(np.float32)), dev)
 
     def buffers():
         i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device=dev)  # noqa: E731
@@ -1003,7 +1006,8 @@ def test_graph_replay_matches_eager(dev):
             ws=u8(ops._lib.load().moe_shuffle_workspace_bytes(T, E, K)),
             shuf=(i32(E + 1), i32(T * K), i32(T * K), i32(T, K)),
             rows=torch.empty((T * K, D), dtype=torch.bfloat16, device=dev),
-            out=out0.clone(), fin=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+            out=out0.clone(), pout=out0.clone(),
+            fin=torch.empty((T, D), dtype=torch.bfloat16, device=dev),
             codes=u8(T, D), scales=u8(nsc), res_out=torch.empty_like(res),
             mout=torch.empty((T, D), dtype=torch.bfloat16, device=dev), mcodes=u8(T, D),
             mscales=u8(nsc))
@@ -1012,6 +1016,7 @@ def test_graph_replay_matches_eager(dev):
         counts, ei, ti, rop = ops.moe_shuffle(s, K, vtc_d, workspace=b["ws"], out=b["shuf"])
         ops.moe_gather_scale_by_token(x, rop, ei, s, counts[E:], b["rows"])
         ops.moe_scatter_add_by_token(b["out"], y, rop, counts[E:])
+        ops.moe_scatter_add_padded_by_token(slabs, counts[:E], rop, b["pout"])
         ops.moe_finalize_rmsnorm(yf, wf, ropf, shf, gf, fi.eps, out=b["fin"], mxfp8=True,
                                  scale_layout="swizzled", mx_codes=b["codes"],
                                  mx_scales=b["scales"])
@@ -1022,8 +1027,8 @@ def test_graph_replay_matches_eager(dev):
 
     def snapshot(b):
         V = int(b["shuf"][0][E].item())
-        snap = {k: b[k].cpu().clone() for k in ("out", "fin", "codes", "scales", "res_out",
-                                                 "mout", "mcodes", "mscales")}
+        snap = {k: b[k].cpu().clone() for k in ("out", "pout", "fin", "codes", "scales",
+                                                 "res_out", "mout", "mcodes", "mscales")}
         snap["rows"] = b["rows"][:V].cpu().clone()
         for i, t in enumerate(b["shuf"]):
             snap[f"shuf{i}"] = t.cpu().clone()
@@ -1048,6 +1053,7 @@ def test_graph_replay_matches_eager(dev):
     for rep in range(3):
         # eager work between replays: reset the accumulated output, spoil the rest
         b["out"].copy_(out0)
+        b["pout"].copy_(out0)
         for k in ("fin", "res_out", "mout", "rows"):
             b[k].view(torch.int16).fill_(0x7E00 + rep)
         for k in ("codes", "scales", "mcodes", "mscales"):
