@@ -100,3 +100,16 @@ def test_stream_mix():
     assert bench.stream_mix(1.5, 1) is None
     assert bench.stream_mix(33, 1) is None
     assert bench.stream_mix(0, 4) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a
+    message, before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
